@@ -1,0 +1,130 @@
+"""Seeded synthetic workloads for causal attention (shared by tests and bench).
+
+This module only draws random inputs and names the workload shapes. It holds
+none of the attention arithmetic, so both the CPU oracle and the GPU path can
+take their inputs from here without sharing any of the method's code.
+
+Shapes follow the pages' workloads:
+  * tiny        - a single tile, two heads (a sanity case the oracle runs in ms)
+  * gqa124m     - "AxiomLM" (PyPI page), the 124M-class GQA model config in
+                  "Quick Start" (12 query heads, 4 kv heads, block 1024) and the
+                  q/k shapes (2,1024,12,64)/(2,1024,4,64) in "8. Standalone
+                  Modern Architectural Modules"
+  * llama1b     - "Axis" (Zyora Labs page): compile_model(batch=4, seq=2048,
+                  dtype="bf16"), 1B-class Llama with grouped kv heads (32/8)
+  * padded      - a right-padded batch, valid length uniform in [S/2, S]
+  * longseq     - one long 16K sequence; Axis (Zyora Labs) states that memory
+                  stays flat as sequence length grows
+
+Recipe (also stated in the design doc): generator = torch.Generator('cpu') seeded
+with 20260000 + index (index 1..5 in the order above); draw Q, K, V, dO as
+fp32 standard normals in [B, S, H, d] order, scale dO by its stated sigma,
+round to bf16 (round-to-nearest-even), and for the padded workload draw the
+per-sequence valid lengths last with randint(S//2, S+1).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int          # seed index (1-based)
+    B: int
+    S: int
+    Hq: int
+    Hkv: int
+    d: int
+    do_sigma: float = 1.0
+    padded: bool = False
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def seed(self) -> int:
+        return 20260000 + self.index
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "B": self.B, "S": self.S, "Hq": self.Hq,
+                "Hkv": self.Hkv, "d": self.d, "causal": True,
+                "padded": self.padded, "dO_sigma": self.do_sigma}
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, B=1, S=128, Hq=2, Hkv=2, d=64),
+    "gqa124m": Workload("gqa124m", 2, B=2, S=1024, Hq=12, Hkv=4, d=64),
+    "llama1b": Workload("llama1b", 3, B=4, S=2048, Hq=32, Hkv=8, d=64, do_sigma=0.1),
+    "padded": Workload("padded", 4, B=8, S=4096, Hq=16, Hkv=16, d=128, padded=True),
+    "longseq": Workload("longseq", 5, B=1, S=16384, Hq=32, Hkv=8, d=128),
+}
+
+
+@dataclasses.dataclass
+class Inputs:
+    q: torch.Tensor        # [B, S, Hq, d] bf16 (CPU)
+    k: torch.Tensor        # [B, S, Hkv, d] bf16
+    v: torch.Tensor        # [B, S, Hkv, d] bf16
+    do: torch.Tensor       # [B, S, Hq, d] bf16
+    seqlens: Optional[torch.Tensor]  # int32 [B] or None
+    scale: float
+
+
+def make_inputs(B: int, S: int, Hq: int, Hkv: int, d: int, seed: int,
+                do_sigma: float = 1.0, padded: bool = False,
+                scale: Optional[float] = None,
+                seqlen_range: Optional[tuple] = None) -> Inputs:
+    """Draw bf16-rounded N(0,1) inputs in the recipe's order.
+
+    ``seqlen_range`` (lo, hi inclusive) overrides the default padded range
+    [S//2, S]; it is used by edge-case tests (e.g. zero-length sequences).
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    q = torch.randn(B, S, Hq, d, generator=gen, dtype=torch.float32)
+    k = torch.randn(B, S, Hkv, d, generator=gen, dtype=torch.float32)
+    v = torch.randn(B, S, Hkv, d, generator=gen, dtype=torch.float32)
+    do = torch.randn(B, S, Hq, d, generator=gen, dtype=torch.float32)
+    if do_sigma != 1.0:
+        do = do * do_sigma
+    seqlens = None
+    if padded:
+        lo, hi = seqlen_range if seqlen_range is not None else (S // 2, S)
+        seqlens = torch.randint(lo, hi + 1, (B,), generator=gen, dtype=torch.int64).to(torch.int32)
+    return Inputs(q=q.to(torch.bfloat16), k=k.to(torch.bfloat16),
+                  v=v.to(torch.bfloat16), do=do.to(torch.bfloat16),
+                  seqlens=seqlens, scale=(1.0 / math.sqrt(d)) if scale is None else float(scale))
+
+
+def workload_inputs(w: Workload) -> Inputs:
+    return make_inputs(w.B, w.S, w.Hq, w.Hkv, w.d, w.seed, do_sigma=w.do_sigma, padded=w.padded)
+
+
+def valid_pairs(S: int, B: int, seqlens=None) -> int:
+    """Number of (i, j) query/key pairs with j <= i < L_b, summed over the batch.
+
+    Pure counting (no attention arithmetic): used to price algorithmic work.
+    """
+    if seqlens is None:
+        return B * S * (S + 1) // 2
+    return int(sum(int(L) * (int(L) + 1) // 2 for L in seqlens.tolist()))
+
+
+def algorithmic_flops(w_or_shape, seqlens=None) -> dict:
+    """Algorithmic flop counts: 4*d per valid pair per query head (QK^T and PV)
+    forward; backward 2.5x that (five GEMMs incl. the QK^T recompute).
+    Per-kernel shares: dK/dV kernel 8*d (S, dP, dV, dK), dQ kernel 2*d (dQ)."""
+    if isinstance(w_or_shape, Workload):
+        B, S, Hq, d = w_or_shape.B, w_or_shape.S, w_or_shape.Hq, w_or_shape.d
+    else:
+        B, S, Hq, d = w_or_shape
+    pairs = valid_pairs(S, B, seqlens)
+    fwd = 4.0 * d * Hq * pairs
+    return {"pairs_per_head": pairs, "fwd": fwd, "bwd": 2.5 * fwd, "total": 3.5 * fwd,
+            "bwd_dkdv": 2.0 * fwd, "bwd_dq": 0.5 * fwd}

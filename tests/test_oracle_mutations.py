@@ -1,0 +1,70 @@
+"""The oracle's pins must catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a private copy of the oracle's source (a
+dropped term, a wrong sign, index or scale, a transposed operand, a wrong
+normaliser) and checks that at least one pin from test_oracle.py fails on the
+mutant. The real oracle is never modified.
+"""
+import os
+import types
+
+import pytest
+
+import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+
+MUTATIONS = {
+    "drop_D_term": ("dS = P * (dP - Dh[:, None])", "dS = P * dP"),
+    "flip_dS_sign": ("dS = P * (dP - Dh[:, None])", "dS = P * (Dh[:, None] - dP)"),
+    "gqa_modulo_mapping": ("g = h // G", "g = h % Hkv"),
+    "dK_without_scale": ("dK[b, :L, g, :] += sc * (dS.T @ qh)", "dK[b, :L, g, :] += (dS.T @ qh)"),
+    "dQ_transposed_dS": ("dQ[b, :L, h, :] = sc * (dS @ kh)", "dQ[b, :L, h, :] = sc * (dS.T @ kh)"),
+    "dV_untransposed_P": ("dV[b, :L, g, :] += P.T @ doh", "dV[b, :L, g, :] += P @ doh"),
+    "lse_base2": ("lse = m + np.log(denom)", "lse = m + np.log2(denom)"),
+    "mask_off_by_one": ("np.tril(np.ones((L, L), dtype=bool))", "np.tril(np.ones((L, L), dtype=bool), 1)"),
+    "scores_unscaled": ("s = (qh @ kh.T) * dtype(scale)", "s = (qh @ kh.T)"),
+    "D_without_O": ("Dh = np.sum(doh * oh, axis=1)", "Dh = np.sum(doh, axis=1)"),
+    "padding_ignored": ("L = lens[b]\n        for h in range(Hq):\n            g = h // G\n            qh",
+                        "L = S\n        for h in range(Hq):\n            g = h // G\n            qh"),
+}
+
+
+def _mutant(old, new):
+    src = open(SRC).read()
+    assert old in src, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _pins(orc):
+    yield lambda: pins.test_hand_worked_examples("hand_s3_d2.txt", orc)
+    yield lambda: pins.test_hand_worked_examples("hand_gqa_padded.txt", orc)
+    yield lambda: pins.test_central_differences(1, 6, 2, 1, 4, None, orc)
+    yield lambda: pins.test_central_differences(2, 6, 4, 2, 3, [4, 6], orc)
+    yield lambda: pins.test_matches_torch_sdpa_fp64(2, 64, 6, 2, 16, orc)
+    yield lambda: pins.test_gqa_equals_explicit_repeat(orc)
+    yield lambda: pins.test_padding_equals_prefix_slice_and_ignores_nan(orc)
+    yield lambda: pins.test_lse_matches_torch_logsumexp_routine(orc)
+
+
+def test_unmutated_copy_passes_every_pin():
+    src = open(SRC).read()
+    mod = types.ModuleType("oracle_copy")
+    exec(compile(src, "oracle_copy", "exec"), mod.__dict__)
+    for pin in _pins(mod):
+        pin()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name):
+    old, new = MUTATIONS[name]
+    mod = _mutant(old, new)
+    caught = 0
+    for pin in _pins(mod):
+        try:
+            pin()
+        except Exception:  # assertion failures, and crashes caused by the mutant
+            caught += 1
+    assert caught > 0, f"no pin caught mutation {name}"
