@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark: causal bf16 attention fwd + bwd on one MI355X.
+
+One step = the whole path over one batch of resident synthetic inputs:
+attn_fwd -> attn_bwd_preprocess -> attn_bwd_dkdv -> attn_bwd_dq (the last two
+are exactly the two launches attn_bwd makes). Default workload: the 1B-class
+Llama attention, B=4, S=2048, Hq=32, Hkv=8, d=64, dO ~ N(0, 0.1).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload llama1b]
+
+Prints ONE JSON line on stdout (diagnostics go to stderr). Throughput counts
+algorithmic flops only: 4*d per valid causal (query, key) pair per query head
+forward, 2.5x that backward (five products including the QK^T recompute).
+
+Other modes (measurement tooling, used under rocprofv3):
+    --copy-calibration       run a plain device copy of known size (counter scale)
+    --pmc-summary DIR ...    turn rocprofv3 --pmc outputs into profiles/*_pmc.txt
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal bf16 attention fwd+bwd TFLOP/s and % of MI355X MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak (2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+KERNEL_SOURCES = ["causal_attention_fwd_amd/csrc/attn_kernels.hip", "causal_attention_fwd_amd/csrc/attn_common.h"]
+KERNEL_NAMES = {"fwd": "fwd_kernel", "pre": "preprocess_kernel", "dkdv": "bwd_dkdv_kernel", "dq": "bwd_dq_kernel"}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------- traffic
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per dispatch from a committed rocprofv3 --pmc summary, or None
+    when there is none or it was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAMES[kernel]}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_sha():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _pmc_rows(d):
+    import csv
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _avg_counter(rows, match, counter):
+    vals = {}
+    for r in rows:
+        if match in r.get("Kernel_Name", "") and r.get("Counter_Name") == counter:
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id") or str(len(vals))
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return (sum(vals.values()) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def pmc_summary(args):
+    """profiles/<kernel>_<workload>_pmc.txt from four rocprofv3 --pmc runs:
+    FETCH_SIZE and WRITE_SIZE of the bench and of the copy calibration."""
+    fetch = _pmc_rows(args.pmc_summary[0])
+    write = _pmc_rows(args.pmc_summary[1])
+    cfetch = _pmc_rows(args.pmc_summary[2])
+    cwrite = _pmc_rows(args.pmc_summary[3])
+    copy_bytes = float(args.copy_bytes)
+    # the copy kernel reads and writes copy_bytes each; counters are in KiB
+    cf, _ = _avg_counter(cfetch, args.copy_kernel, "FETCH_SIZE")
+    cw, _ = _avg_counter(cwrite, args.copy_kernel, "WRITE_SIZE")
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for key, kname in KERNEL_NAMES.items():
+        fk, n1 = _avg_counter(fetch, kname, "FETCH_SIZE")
+        wk, n2 = _avg_counter(write, kname, "WRITE_SIZE")
+        if fk is None or wk is None:
+            continue
+        traffic = fk * 1024.0 * f_scale + wk * 1024.0 * w_scale
+        path = os.path.join(ROOT, "profiles", f"{kname}_{args.workload}_pmc.txt")
+        with open(path, "w") as out:
+            out.write(f"# HBM traffic of {kname} on workload {args.workload} (rocprofv3 --pmc)\n")
+            out.write(f"# commands: {args.pmc_command}\n")
+            out.write(f"kernel_source_sha256_16: {kernel_source_sha()}\n")
+            out.write(f"dispatches_fetch: {n1}\ndispatches_write: {n2}\n")
+            out.write(f"fetch_kib_per_dispatch: {fk:.1f}\nwrite_kib_per_dispatch: {wk:.1f}\n")
+            out.write(f"copy_bytes: {copy_bytes:.0f}\n")
+            out.write(f"copy_fetch_kib: {cf:.1f}\ncopy_write_kib: {cw:.1f}\n")
+            out.write(f"scale_fetch: {f_scale:.4f}\nscale_write: {w_scale:.4f}\n")
+            out.write(f"traffic_bytes_per_dispatch: {traffic:.0f}\n")
+        log(f"wrote {path}: {traffic / 1e6:.1f} MB per dispatch")
+
+
+# ----------------------------------------------------------------------------- copy calibration
+
+def copy_calibration(args):
+    import torch
+    n = int(args.copy_bytes)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 5}))
+
+
+# ----------------------------------------------------------------------------- the benchmark
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The oracle (fp32 mode, untuned) on whole (sequence, kv head) units of the
+    same workload until about `budget_s` seconds of CPU work have been spent."""
+    import numpy as np
+    import oracle
+    from attn_workloads import valid_pairs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    q, k, v, do = (x.float().numpy() for x in (inp.q, inp.k, inp.v, inp.do))
+    sl = inp.seqlens.numpy() if inp.seqlens is not None else None
+    G = w.Hq // w.Hkv
+    units = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    for b, g in units:
+        hs = slice(g * G, (g + 1) * G)
+        oracle.backward(q[b:b + 1, :, hs], k[b:b + 1, :, g:g + 1], v[b:b + 1, :, g:g + 1], do[b:b + 1, :, hs],
+                        inp.scale, None if sl is None else sl[b:b + 1], dtype=np.float32)
+        done += 1
+        pairs = valid_pairs(w.S, 1, None if sl is None else sl[b:b + 1])
+        flops += 3.5 * 4.0 * w.d * G * pairs
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {len(units)} (sequence, kv head) units of {w.name}, fwd+bwd, numpy fp32, "
+                      f"{dt:.1f} s"}
+
+
+def run(args):
+    import torch
+    import causal_attention_fwd_amd as attn
+    from attn_workloads import WORKLOADS, algorithmic_flops, workload_inputs
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    attn.load_library()  # fails loudly when the HIP library is not built
+    w = WORKLOADS[args.workload]
+    inp = workload_inputs(w)
+    dev = torch.device("cuda")
+    q, k, v, do = (x.to(dev).contiguous() for x in (inp.q, inp.k, inp.v, inp.do))
+    sl = inp.seqlens.to(dev) if inp.seqlens is not None else None
+    B, S, Hq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, S, device=dev)
+    delta = torch.empty(B, Hq, S, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    scale = inp.scale
+    fl = algorithmic_flops(w, inp.seqlens)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        attn.attn_fwd(q, k, v, o, lse, scale, sl)
+        if ev is not None:
+            ev[1].record()
+        attn.attn_bwd_preprocess(o, do, delta, sl)
+        if ev is not None:
+            ev[2].record()
+        attn.attn_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, scale, sl)
+        if ev is not None:
+            ev[3].record()
+        attn.attn_bwd_dq(q, k, v, do, lse, delta, dq, scale, sl)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["fwd", "pre", "dkdv", "dq"]
+    per = {n: 0.0 for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n] += ev[j].elapsed_time(ev[j + 1])
+    per = {n: per[n] / args.steps for n in names}           # ms per launch
+    ms_step = wall * 1e3 / args.steps
+    tflops = fl["total"] / (ms_step * 1e-3) / 1e12
+
+    # roofline of the dominant kernel
+    dom = max(per, key=per.get)
+    if dom == "pre":
+        alg_bytes = 2.0 * B * S * Hq * d * 2 + B * Hq * S * 4.0
+        achieved = alg_bytes / (per[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        share = {"fwd": fl["fwd"], "dkdv": fl["bwd_dkdv"], "dq": fl["bwd_dq"]}[dom]
+        achieved = share / (per[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    roof["kernel"] = KERNEL_NAMES[dom]
+    roof["ms_per_launch"] = per[dom]
+    roof["traffic"] = read_traffic(dom, w.name)
+
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": dict(w.describe(), valid_pairs_per_head=fl["pairs_per_head"],
+                       algorithmic_gflop_per_step=round(fl["total"] / 1e9, 3)),
+        "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "kernel_ms": {KERNEL_NAMES[n]: round(per[n], 4) for n in names},
+        "kernel_tflops": {KERNEL_NAMES[n]: round(s / (per[n] * 1e-3) / 1e12, 1)
+                          for n, s in (("fwd", fl["fwd"]), ("dkdv", fl["bwd_dkdv"]), ("dq", fl["bwd_dq"]))},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama1b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work in cpu_baseline")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--copy-bytes", type=float, default=1 << 30)
+    ap.add_argument("--copy-kernel", default="copy")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
+    ap.add_argument("--pmc-command", default="")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (each GPU would run its own "
+              "(sequence, kv-head) units independently); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.pmc_summary:
+        pmc_summary(args)
+    elif args.copy_calibration:
+        copy_calibration(args)
+    else:
+        run(args)
+
+
+if __name__ == "__main__":
+    main()

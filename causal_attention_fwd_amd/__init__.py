@@ -1,0 +1,252 @@
+"""Python binding of the gfx950 fused causal attention library (libattn_mi355x.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/attn.h. PyTorch supplies device
+memory and the current stream. There is no CPU fallback: if the library is not
+built, or a tensor is not on a GPU, the call raises.
+
+Entry points (same names as the C ABI):
+    attn_fwd(q, k, v, o, lse, scale, seqlens=None)
+    attn_bwd_preprocess(o, d_o, delta, seqlens=None)
+    attn_bwd_workspace_bytes(B, S, Hq, Hkv, d)
+    attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens=None, workspace=None)
+    attn_bwd_dkdv(q, k, v, d_o, lse, delta, dk, dv, scale, seqlens=None)
+    attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale, seqlens=None)
+    attn_status_string(code)
+and allocating conveniences `forward(...)`, `backward(...)`.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = ["attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
+           "attn_bwd_dkdv", "attn_bwd_dq", "attn_status_string", "forward", "backward", "AttnError", "library_path", "load_library",
+           "STATUS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libattn_mi355x.so"
+
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_MISALIGNED",
+          4: "ATTN_ERR_WORKSPACE", 5: "ATTN_ERR_HIP"}
+
+# The symbols include/attn.h declares.
+EXPORTED = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_dkdv",
+            "attn_bwd_dq", "attn_status_string")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {attn_status_string(code)} (status {code})")
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("heads_q", ctypes.c_int32),
+                ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("causal", ctypes.c_int32), ("seqlens", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return os.environ.get("ATTN_MI355X_LIB", os.path.join(_HERE, LIB_NAME))
+
+
+_lib = None
+
+
+def load_library():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with `python -m causal_attention_fwd_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    shp = ctypes.POINTER(AttnShape)
+    lib.attn_fwd.argtypes = [shp, vp, vp, vp, vp, vp, vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_bwd_preprocess.argtypes = [shp, vp, vp, vp, vp]
+    lib.attn_bwd_preprocess.restype = i32
+    lib.attn_bwd_workspace_bytes.argtypes = [shp]
+    lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_bwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.attn_bwd.restype = i32
+    lib.attn_bwd_dkdv.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_bwd_dkdv.restype = i32
+    lib.attn_bwd_dq.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_bwd_dq.restype = i32
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_status_string(code: int) -> str:
+    return load_library().attn_status_string(int(code)).decode()
+
+
+def make_shape(B: int, S: int, Hq: int, Hkv: int, d: int, scale: float, seqlens_ptr: Optional[int] = None,
+               causal: int = 1) -> AttnShape:
+    return AttnShape(int(B), int(S), int(Hq), int(Hkv), int(d), float(scale), int(causal),
+                     ctypes.c_void_p(seqlens_ptr) if seqlens_ptr else None)
+
+
+# ------------------------------------------------------------------ torch marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check_gpu(name, t, dtype, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device}); there is no CPU path")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _shape_from(q, k, scale, seqlens, causal=1):
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B,S,Hq,d] and k [B,S,Hkv,d]")
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    sl = None
+    if seqlens is not None:
+        sl = _check_gpu("seqlens", seqlens, torch.int32, (B,))
+    return make_shape(B, S, Hq, Hkv, d, scale, sl, causal), (B, S, Hq, Hkv, d)
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _call(fn, where, *args):
+    code = fn(*args)
+    if code != 0:
+        raise AttnError(code, where)
+
+
+def attn_fwd(q, k, v, o, lse, scale: float, seqlens=None, causal: int = 1):
+    """O, LSE <- attention forward (writes into `o` and `lse`)."""
+    torch = _torch()
+    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal)
+    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d)),
+            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d)),
+            _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d)),
+            _check_gpu("o", o, torch.bfloat16, (B, S, Hq, d)),
+            _check_gpu("lse", lse, torch.float32, (B, Hq, S))]
+    _call(load_library().attn_fwd, "attn_fwd", ctypes.byref(shape), *[ctypes.c_void_p(p) for p in ptrs], _stream())
+
+
+def attn_bwd_preprocess(o, d_o, delta, seqlens=None):
+    """D <- rowsum(dO * O) (writes into `delta`)."""
+    torch = _torch()
+    if o.dim() != 4:
+        raise ValueError("o must be [B,S,Hq,d]")
+    B, S, Hq, d = o.shape
+    sl = _check_gpu("seqlens", seqlens, torch.int32, (B,)) if seqlens is not None else None
+    shape = make_shape(B, S, Hq, Hq, d, 1.0, sl)
+    ptrs = [_check_gpu("o", o, torch.bfloat16, (B, S, Hq, d)),
+            _check_gpu("d_o", d_o, torch.bfloat16, (B, S, Hq, d)),
+            _check_gpu("delta", delta, torch.float32, (B, Hq, S))]
+    _call(load_library().attn_bwd_preprocess, "attn_bwd_preprocess", ctypes.byref(shape),
+          *[ctypes.c_void_p(p) for p in ptrs], _stream())
+
+
+def attn_bwd_workspace_bytes(B: int, S: int, Hq: int, Hkv: int, d: int) -> int:
+    shape = make_shape(B, S, Hq, Hkv, d, 1.0 / math.sqrt(d))
+    return int(load_library().attn_bwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale: float, seqlens=None, workspace=None, causal: int = 1):
+    """dQ, dK, dV <- attention backward (writes into `dq`, `dk`, `dv`)."""
+    torch = _torch()
+    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal)
+    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d)),
+            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d)),
+            _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d)),
+            _check_gpu("d_o", d_o, torch.bfloat16, (B, S, Hq, d)),
+            _check_gpu("lse", lse, torch.float32, (B, Hq, S)),
+            _check_gpu("delta", delta, torch.float32, (B, Hq, S)),
+            _check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d)),
+            _check_gpu("dk", dk, torch.bfloat16, (B, S, Hkv, d)),
+            _check_gpu("dv", dv, torch.bfloat16, (B, S, Hkv, d))]
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _check_gpu("workspace", workspace, workspace.dtype)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _call(load_library().attn_bwd, "attn_bwd", ctypes.byref(shape), *[ctypes.c_void_p(p) for p in ptrs],
+          ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), _stream())
+
+
+def _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal):
+    torch = _torch()
+    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal)
+    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d)),
+            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d)),
+            _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d)),
+            _check_gpu("d_o", d_o, torch.bfloat16, (B, S, Hq, d)),
+            _check_gpu("lse", lse, torch.float32, (B, Hq, S)),
+            _check_gpu("delta", delta, torch.float32, (B, Hq, S))]
+    return shape, (B, S, Hq, Hkv, d), ptrs
+
+
+def attn_bwd_dkdv(q, k, v, d_o, lse, delta, dk, dv, scale: float, seqlens=None, causal: int = 1):
+    """dK, dV <- the key-block pass of the backward (writes into `dk`, `dv`)."""
+    torch = _torch()
+    shape, (B, S, Hq, Hkv, d), ptrs = _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal)
+    ptrs += [_check_gpu("dk", dk, torch.bfloat16, (B, S, Hkv, d)),
+             _check_gpu("dv", dv, torch.bfloat16, (B, S, Hkv, d))]
+    _call(load_library().attn_bwd_dkdv, "attn_bwd_dkdv", ctypes.byref(shape),
+          *[ctypes.c_void_p(p) for p in ptrs], _stream())
+
+
+def attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale: float, seqlens=None, causal: int = 1):
+    """dQ <- the query-block pass of the backward (writes into `dq`)."""
+    torch = _torch()
+    shape, (B, S, Hq, Hkv, d), ptrs = _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal)
+    ptrs += [_check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d))]
+    _call(load_library().attn_bwd_dq, "attn_bwd_dq", ctypes.byref(shape),
+          *[ctypes.c_void_p(p) for p in ptrs], _stream())
+
+
+# ------------------------------------------------------------------ allocating conveniences
+
+def forward(q, k, v, scale: Optional[float] = None, seqlens=None):
+    """Returns (O, LSE) as new tensors."""
+    torch = _torch()
+    B, S, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, scale, seqlens)
+    return o, lse
+
+
+def backward(q, k, v, o, d_o, lse, scale: Optional[float] = None, seqlens=None):
+    """Returns (dQ, dK, dV, D) as new tensors (runs the preprocess, then the backward)."""
+    torch = _torch()
+    B, S, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    delta = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    attn_bwd_preprocess(o, d_o, delta, seqlens)
+    need = attn_bwd_workspace_bytes(B, S, Hq, k.shape[2], d)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, ws)
+    return dq, dk, dv, delta

@@ -1,0 +1,121 @@
+// C ABI of the attention library: host-side validation, then launches on the
+// caller's stream. No allocation, no synchronisation, no global state.
+#include <math.h>
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+attn_status check_shape(const attn_shape* s, attn::Problem* pr) {
+  if (!s) return ATTN_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->seqlen < 1 || s->heads_q < 1 || s->heads_kv < 1) return ATTN_ERR_INVALID_ARG;
+  if (s->heads_q % s->heads_kv != 0) return ATTN_ERR_INVALID_ARG;
+  if (!(isfinite(s->scale) && s->scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+  if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (s->causal != 1) return ATTN_ERR_UNSUPPORTED;
+  if (s->seqlens && (reinterpret_cast<uintptr_t>(s->seqlens) & 3u) != 0) return ATTN_ERR_MISALIGNED;
+  pr->B = s->batch;
+  pr->S = s->seqlen;
+  pr->Hq = s->heads_q;
+  pr->Hkv = s->heads_kv;
+  pr->d = s->head_dim;
+  pr->scale = s->scale;
+  pr->seqlens = s->seqlens;
+  if (attn::max_grid(*pr) > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status check_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (!p) return ATTN_ERR_INVALID_ARG;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_MISALIGNED;
+  return ATTN_OK;
+}
+
+attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd(const attn_shape* shape, const void* q, const void* k, const void* v, void* o, float* lse,
+                     hipStream_t stream) {
+  attn::Problem pr;
+  attn_status st = check_shape(shape, &pr);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k, v, o, lse});
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_fwd(pr, q, k, v, o, lse, stream));
+}
+
+attn_status attn_bwd_preprocess(const attn_shape* shape, const void* o, const void* d_o, float* delta,
+                                hipStream_t stream) {
+  attn::Problem pr;
+  attn_status st = check_shape(shape, &pr);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({o, d_o, delta});
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_preprocess(pr, o, d_o, delta, stream));
+}
+
+size_t attn_bwd_workspace_bytes(const attn_shape* shape) {
+  (void)shape;
+  return 0;  // dQ has its own pass: no accumulation buffer
+}
+
+attn_status attn_bwd_dkdv(const attn_shape* shape, const void* q, const void* k, const void* v, const void* d_o,
+                          const float* lse, const float* delta, void* dk, void* dv, hipStream_t stream) {
+  attn::Problem pr;
+  attn_status st = check_shape(shape, &pr);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k, v, d_o, lse, delta, dk, dv});
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, stream));
+}
+
+attn_status attn_bwd_dq(const attn_shape* shape, const void* q, const void* k, const void* v, const void* d_o,
+                        const float* lse, const float* delta, void* dq, hipStream_t stream) {
+  attn::Problem pr;
+  attn_status st = check_shape(shape, &pr);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k, v, d_o, lse, delta, dq});
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd_dq(pr, q, k, v, d_o, lse, delta, dq, stream));
+}
+
+attn_status attn_bwd(const attn_shape* shape, const void* q, const void* k, const void* v, const void* d_o,
+                     const float* lse, const float* delta, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  attn::Problem pr;
+  attn_status st = check_shape(shape, &pr);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k, v, d_o, lse, delta, dq, dk, dv});
+  if (st != ATTN_OK) return st;
+  const size_t need = attn_bwd_workspace_bytes(shape);
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return ATTN_ERR_WORKSPACE;
+  st = from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, stream));
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd_dq(pr, q, k, v, d_o, lse, delta, dq, stream));
+}
+
+const char* attn_status_string(attn_status status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: null pointer, bad size, Hq % Hkv != 0 or bad scale";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: head_dim must be 64 or 128, causal must be 1";
+    case ATTN_ERR_MISALIGNED: return "ATTN_ERR_MISALIGNED: tensor pointers must be 16-byte aligned";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace smaller than attn_bwd_workspace_bytes()";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: the HIP runtime reported a launch error";
+  }
+  return "ATTN_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,754 @@
+// gfx950 kernels for fused causal attention: forward, backward preprocess,
+// backward dK/dV and backward dQ.
+//
+// The method ("Axis", Zyora Labs page, feature list): flash attention forward
+// and backward on matrix cores in which the attention probabilities never reach
+// device memory; bf16 storage, fp32 accumulation. Grouped kv heads follow the
+// "AxiomLM" page ("Key Features": grouped-query attention). The formulas are in
+// include/attn.h.
+//
+// Design (CDNA4-specific, not taken from the pages' CUDA/WMMA kernels):
+//  * every product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulators;
+//  * the forward and dQ passes compute S^T = K Q^T so that each lane owns one
+//    query row: row max/sum need a single cross-lane step (lane l <-> l+32), the
+//    row statistics (m, l, LSE, D) are per-lane scalars, and P^T / dS^T already
+//    sit in the B-operand layout of the next product (O^T = V^T P^T,
+//    dQ^T = K^T dS^T) without any shuffle;
+//  * the dK/dV pass computes S = Q K^T so that each lane owns one key column and
+//    P / dS feed dV^T = dO^T P and dK^T = Q^T dS as B operands directly;
+//  * the transposed A operands (V^T, K^T, dO^T, Q^T) come from row-major LDS tiles
+//    through the gfx950 transposing LDS read (ds_read_b64_tr_b16);
+//  * K/V (or Q/dO) tiles are double-buffered in LDS with a register prefetch of
+//    the next tile, one barrier per tile;
+//  * tiles entirely above the causal diagonal or past a sequence's valid length
+//    are never loaded or computed; the mask is applied only on tiles that need it;
+//  * the softmax runs in base 2 with scale*log2(e) folded into one multiply;
+//    LSE is exported as a natural log.
+#include "attn_common.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+struct FwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  const int32_t* seqlens;
+  int B, S, Hq, Hkv, nqb;
+  float scale;
+};
+
+struct PreArgs {
+  const bf16* o;
+  const bf16* d_o;
+  float* delta;
+  const int32_t* seqlens;
+  int B, S, Hq;
+  int64_t rows;  // B * S * Hq
+};
+
+struct BwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* d_o;
+  const float* lse;
+  const float* delta;
+  bf16* dq;
+  bf16* dk;
+  bf16* dv;
+  const int32_t* seqlens;
+  int B, S, Hq, Hkv, nblk;
+  float scale;
+};
+
+constexpr int kThreads = 256;  // four waves, one per SIMD
+
+// Cooperative loader of an R x D bf16 tile (rows of a [*, S, H, D] tensor) into
+// registers, then into a row-major LDS tile with stride D + 8 elements. Rows at
+// or beyond `limit` are zero-filled so padding can never inject NaN/Inf into a
+// product.
+template <int R, int D>
+struct TileLoader {
+  static constexpr int kChunks = R * D / 8;          // 16-byte chunks
+  static constexpr int kPerThread = kChunks / kThreads;
+  static_assert(kChunks % kThreads == 0, "tile must split evenly over the workgroup");
+  uint4 reg[kPerThread];
+
+  __device__ __forceinline__ void load(const bf16* base, int64_t row_stride, int row0, int limit) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int id = threadIdx.x + i * kThreads;
+      const int row = id / (D / 8);
+      const int col = (id % (D / 8)) * 8;
+      const int r = row0 + row;
+      if (r < limit) {
+        reg[i] = *reinterpret_cast<const uint4*>(base + (int64_t)r * row_stride + col);
+      } else {
+        reg[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(bf16* tile) const {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int id = threadIdx.x + i * kThreads;
+      const int row = id / (D / 8);
+      const int col = (id % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(tile + row * (D + 8) + col) = reg[i];
+    }
+  }
+};
+
+// ----------------------------------------------------------------------------
+// Forward. One workgroup = one (sequence, query head, block of 128*NT query
+// rows); wave w owns rows [q0 + 32*NT*w, +32*NT). Loop over 64-row K/V tiles up
+// to the block's last row.
+// ----------------------------------------------------------------------------
+template <int D, int NT>
+__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
+  constexpr int BN = 64;
+  constexpr int BM = 4 * 32 * NT;
+  constexpr int KK = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int LS = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * LS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  int qb, b, h;
+  decode_qblock(blockIdx.x, a.nqb, a.B, a.Hq, a.Hkv, qb, b, h);
+  const int S = a.S;
+  const int L = valid_len(a.seqlens, b, S);
+  const int hkv = h / (a.Hq / a.Hkv);
+  const int64_t qs = (int64_t)a.Hq * D;   // elements between consecutive positions
+  const int64_t ks = (int64_t)a.Hkv * D;
+  const bf16* Qb = a.q + ((int64_t)b * S * a.Hq + h) * D;
+  const bf16* Kb = a.k + ((int64_t)b * S * a.Hkv + hkv) * D;
+  const bf16* Vb = a.v + ((int64_t)b * S * a.Hkv + hkv) * D;
+  bf16* Ob = a.o + ((int64_t)b * S * a.Hq + h) * D;
+  float* LSEb = a.lse + ((int64_t)b * a.Hq + h) * S;
+
+  const int q0 = qb * BM;
+  const int qw = q0 + wave * 32 * NT;
+  const int ntiles = (q0 < L) ? (min(q0 + BM, L) - 1) / BN + 1 : 0;
+  const int wave_last = min(qw + 32 * NT, L) - 1;  // < qw when the wave is all padding
+  const float c = a.scale * kLog2e;
+
+  bf16x8 qf[NT][KK];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int row = qw + t * 32 + l32;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[t][kk] = row < L ? *reinterpret_cast<const bf16x8*>(Qb + (int64_t)row * qs + kk * 16 + g * 8)
+                          : zero_bf16x8();
+  }
+
+  f32x16 oacc[DT][NT];
+  float m[NT], lsum[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    m[t] = kNegInf;
+    lsum[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt][t] = zero16();
+  }
+
+  TileLoader<BN, D> kl, vl;
+  if (ntiles > 0) {
+    kl.load(Kb, ks, 0, L);
+    vl.load(Vb, ks, 0, L);
+    kl.store(smem[0][0]);
+    vl.store(smem[0][1]);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < ntiles;
+    if (more) {
+      kl.load(Kb, ks, (kt + 1) * BN, L);
+      vl.load(Vb, ks, (kt + 1) * BN, L);
+    }
+    const int j0 = kt * BN;
+    if (j0 <= wave_last) {
+      const bf16* Ks = smem[buf][0];
+      const bf16* Vs = smem[buf][1];
+      f32x16 s[2][NT];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) s[mt][t] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 af = frag_row(Ks, LS, mt * 32, kk * 16, lane);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) s[mt][t] = mfma32(af, qf[t][kk], s[mt][t]);
+        }
+      }
+      const bool need_mask = (j0 + BN - 1 > qw) || (j0 + BN > L);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int i = qw + t * 32 + l32;
+        float mx = kNegInf;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = s[mt][t][r] * c;
+            if (need_mask) {
+              const int j = j0 + mt * 32 + ((r >> 2) << 3) + (g << 2) + (r & 3);
+              if (j > i || j >= L) x = kNegInf;
+            }
+            s[mt][t][r] = x;
+            mx = fmaxf(mx, x);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m[t], mx);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = fast_exp2(m[t] - m_use);
+        m[t] = m_new;
+        float ls = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(s[mt][t][r] - m_use);
+            s[mt][t][r] = p;
+            ls += p;
+          }
+        lsum[t] = lsum[t] * alpha + ls;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][t][r] *= alpha;
+      }
+      bf16x8 pb[4][NT];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) pb[u][t] = pack8(s[u >> 1][t], (u & 1) * 8);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bf16x8 af = frag_tr(Vs, LS, u * 16, dt * 32, lane);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) oacc[dt][t] = mfma32(af, pb[u][t], oacc[dt][t]);
+        }
+    }
+    if (more) {
+      kl.store(smem[buf ^ 1][0]);
+      vl.store(smem[buf ^ 1][1]);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2; padded rows 0 / -inf.
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int i = qw + t * 32 + l32;
+    const float lt = lsum[t] + __shfl_xor(lsum[t], 32);
+    if (i < S) {
+      const bool valid = i < L;
+      const float inv = valid ? 1.f / lt : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (bf16)(oacc[dt][t][rr * 4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(Ob + (int64_t)i * qs + dt * 32 + rr * 8 + g * 4) = ov;
+        }
+      if (g == 0) LSEb[i] = valid ? (m[t] + __log2f(lt)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Preprocess: D = rowsum(dO * O). D/8 lanes per row, 16 bytes per lane.
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < a.rows) {
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(a.o + row * D + part * 8);
+    const bf16x8 d = *reinterpret_cast<const bf16x8*>(a.d_o + row * D + part * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)o[e] * (float)d[e];
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < a.rows && part == 0) {
+    // row = (b * S + s) * Hq + h
+    const int h = (int)(row % a.Hq);
+    const int64_t bs = row / a.Hq;
+    const int s = (int)(bs % a.S);
+    const int b = (int)(bs / a.S);
+    const int L = valid_len(a.seqlens, b, a.S);
+    a.delta[((int64_t)b * a.Hq + h) * a.S + s] = s < L ? acc : 0.f;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Backward dK/dV. One workgroup = one (sequence, kv head, block of 128*NTJ key
+// rows); wave w owns key rows [j0 + 32*NTJ*w, +32*NTJ), keeps its K and V rows
+// as B operands in registers and dK^T, dV^T accumulators. Loop over the query
+// heads of the group and, for each, over 64-row query tiles from the diagonal
+// to the valid length.
+// ----------------------------------------------------------------------------
+template <int D, int NTJ>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int BMQ = 64;
+  constexpr int BN = 4 * 32 * NTJ;
+  constexpr int KK = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int LS = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BMQ * LS];  // [buf][Q, dO]
+  __shared__ float sstat[2][2][BMQ];                                 // [buf][LSE*log2e, D]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  int kb, b, hkv;
+  decode_kblock(blockIdx.x, a.B, a.Hkv, kb, b, hkv);
+  const int S = a.S;
+  const int L = valid_len(a.seqlens, b, S);
+  const int G = a.Hq / a.Hkv;
+  const int64_t qs = (int64_t)a.Hq * D;
+  const int64_t ks = (int64_t)a.Hkv * D;
+  const bf16* Kb = a.k + ((int64_t)b * S * a.Hkv + hkv) * D;
+  const bf16* Vb = a.v + ((int64_t)b * S * a.Hkv + hkv) * D;
+
+  const int j0 = kb * BN;
+  const int jw = j0 + wave * 32 * NTJ;
+  const float c = a.scale * kLog2e;
+
+  bf16x8 kf[NTJ][KK], vf[NTJ][KK];
+#pragma unroll
+  for (int t = 0; t < NTJ; ++t) {
+    const int j = jw + t * 32 + l32;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int64_t off = (int64_t)j * ks + kk * 16 + g * 8;
+      kf[t][kk] = j < L ? *reinterpret_cast<const bf16x8*>(Kb + off) : zero_bf16x8();
+      vf[t][kk] = j < L ? *reinterpret_cast<const bf16x8*>(Vb + off) : zero_bf16x8();
+    }
+  }
+
+  f32x16 dk[DT][NTJ], dv[DT][NTJ];
+#pragma unroll
+  for (int ct = 0; ct < DT; ++ct)
+#pragma unroll
+    for (int t = 0; t < NTJ; ++t) {
+      dk[ct][t] = zero16();
+      dv[ct][t] = zero16();
+    }
+
+  const int qt0 = j0 / BMQ;
+  const int nq = (j0 < L) ? (L - 1) / BMQ - qt0 + 1 : 0;  // query tiles per head
+  const int iters = nq * G;
+
+  TileLoader<BMQ, D> ql, dol;
+  float st_reg = 0.f;  // threads 0..63 carry LSE*log2e, 64..127 carry D
+  auto load_tile = [&](int it) {
+    const int hh = it / nq;
+    const int qt = qt0 + (it - hh * nq);
+    const int h = hkv * G + hh;
+    const bf16* Qb = a.q + ((int64_t)b * S * a.Hq + h) * D;
+    const bf16* dOb = a.d_o + ((int64_t)b * S * a.Hq + h) * D;
+    ql.load(Qb, qs, qt * BMQ, L);
+    dol.load(dOb, qs, qt * BMQ, L);
+    const int tid = threadIdx.x;
+    if (tid < 2 * BMQ) {
+      const int i = qt * BMQ + (tid & (BMQ - 1));
+      const int64_t so = ((int64_t)b * a.Hq + h) * S + i;
+      st_reg = 0.f;
+      if (i < L) st_reg = tid < BMQ ? a.lse[so] * kLog2e : a.delta[so];
+    }
+  };
+  auto store_tile = [&](int buf) {
+    ql.store(smem[buf][0]);
+    dol.store(smem[buf][1]);
+    const int tid = threadIdx.x;
+    if (tid < 2 * BMQ) sstat[buf][tid / BMQ][tid & (BMQ - 1)] = st_reg;
+  };
+
+  if (iters > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < iters; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < iters;
+    if (more) load_tile(it + 1);
+    const int hh = it / nq;
+    const int qt = qt0 + (it - hh * nq);
+    const int i0 = qt * BMQ;
+    // skip when every query row of the tile is above this wave's key rows, or the
+    // wave's keys are all padding
+    if (i0 + BMQ - 1 >= jw && jw < L) {
+      const bf16* Qs = smem[buf][0];
+      const bf16* dOs = smem[buf][1];
+      const float* lse2 = sstat[buf][0];
+      const float* dl = sstat[buf][1];
+      f32x16 s[2][NTJ], dp[2][NTJ];
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+        for (int t = 0; t < NTJ; ++t) {
+          s[m2][t] = zero16();
+          dp[m2][t] = zero16();
+        }
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+          const bf16x8 aq = frag_row(Qs, LS, m2 * 32, kk * 16, lane);
+          const bf16x8 ad = frag_row(dOs, LS, m2 * 32, kk * 16, lane);
+#pragma unroll
+          for (int t = 0; t < NTJ; ++t) {
+            s[m2][t] = mfma32(aq, kf[t][kk], s[m2][t]);
+            dp[m2][t] = mfma32(ad, vf[t][kk], dp[m2][t]);
+          }
+        }
+      }
+      const bool need_mask = (i0 < jw + 32 * NTJ - 1) || (i0 + BMQ > L) || (jw + 32 * NTJ > L);
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int il = m2 * 32 + ((r >> 2) << 3) + (g << 2) + (r & 3);
+          const float l2 = lse2[il];
+          const float dd = dl[il];
+#pragma unroll
+          for (int t = 0; t < NTJ; ++t) {
+            float p = fast_exp2(s[m2][t][r] * c - l2);
+            float ds = p * (dp[m2][t][r] - dd);
+            if (need_mask) {
+              const int i = i0 + il;
+              const int j = jw + t * 32 + l32;
+              if (j > i || i >= L || j >= L) {
+                p = 0.f;
+                ds = 0.f;
+              }
+            }
+            s[m2][t][r] = p;
+            dp[m2][t][r] = ds;
+          }
+        }
+      bf16x8 pb[4][NTJ], sb[4][NTJ];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < NTJ; ++t) {
+          pb[u][t] = pack8(s[u >> 1][t], (u & 1) * 8);
+          sb[u][t] = pack8(dp[u >> 1][t], (u & 1) * 8);
+        }
+#pragma unroll
+      for (int ct = 0; ct < DT; ++ct)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bf16x8 ado = frag_tr(dOs, LS, u * 16, ct * 32, lane);
+          const bf16x8 aq = frag_tr(Qs, LS, u * 16, ct * 32, lane);
+#pragma unroll
+          for (int t = 0; t < NTJ; ++t) {
+            dv[ct][t] = mfma32(ado, pb[u][t], dv[ct][t]);
+            dk[ct][t] = mfma32(aq, sb[u][t], dk[ct][t]);
+          }
+        }
+    }
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: dK = scale * dK^T, dV = dV^T transposed back; lane owns key row j.
+  bf16* dKb = a.dk + ((int64_t)b * S * a.Hkv + hkv) * D;
+  bf16* dVb = a.dv + ((int64_t)b * S * a.Hkv + hkv) * D;
+#pragma unroll
+  for (int t = 0; t < NTJ; ++t) {
+    const int j = jw + t * 32 + l32;
+    if (j < S) {
+      const bool valid = j < L;
+#pragma unroll
+      for (int ct = 0; ct < DT; ++ct)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          bf16x4 kv4, vv4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kv4[e] = (bf16)(valid ? dk[ct][t][rr * 4 + e] * a.scale : 0.f);
+            vv4[e] = (bf16)(valid ? dv[ct][t][rr * 4 + e] : 0.f);
+          }
+          const int64_t off = (int64_t)j * ks + ct * 32 + rr * 8 + g * 4;
+          *reinterpret_cast<bf16x4*>(dKb + off) = kv4;
+          *reinterpret_cast<bf16x4*>(dVb + off) = vv4;
+        }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Backward dQ. Same tiling as the forward: one workgroup per (sequence, query
+// head, query block); recompute S^T and dP^T per 64-row K/V tile, then
+// dQ^T += K^T dS^T.
+// ----------------------------------------------------------------------------
+template <int D, int NT>
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BN = 64;
+  constexpr int BM = 4 * 32 * NT;
+  constexpr int KK = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int LS = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * LS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  int qb, b, h;
+  decode_qblock(blockIdx.x, a.nblk, a.B, a.Hq, a.Hkv, qb, b, h);
+  const int S = a.S;
+  const int L = valid_len(a.seqlens, b, S);
+  const int hkv = h / (a.Hq / a.Hkv);
+  const int64_t qs = (int64_t)a.Hq * D;
+  const int64_t ks = (int64_t)a.Hkv * D;
+  const bf16* Qb = a.q + ((int64_t)b * S * a.Hq + h) * D;
+  const bf16* dOb = a.d_o + ((int64_t)b * S * a.Hq + h) * D;
+  const bf16* Kb = a.k + ((int64_t)b * S * a.Hkv + hkv) * D;
+  const bf16* Vb = a.v + ((int64_t)b * S * a.Hkv + hkv) * D;
+  const float* LSEb = a.lse + ((int64_t)b * a.Hq + h) * S;
+  const float* Db = a.delta + ((int64_t)b * a.Hq + h) * S;
+  bf16* dQb = a.dq + ((int64_t)b * S * a.Hq + h) * D;
+
+  const int q0 = qb * BM;
+  const int qw = q0 + wave * 32 * NT;
+  const int ntiles = (q0 < L) ? (min(q0 + BM, L) - 1) / BN + 1 : 0;
+  const int wave_last = min(qw + 32 * NT, L) - 1;
+  const float c = a.scale * kLog2e;
+
+  bf16x8 qf[NT][KK], df[NT][KK];
+  float l2[NT], dd[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int row = qw + t * 32 + l32;
+    const bool valid = row < L;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int64_t off = (int64_t)row * qs + kk * 16 + g * 8;
+      qf[t][kk] = valid ? *reinterpret_cast<const bf16x8*>(Qb + off) : zero_bf16x8();
+      df[t][kk] = valid ? *reinterpret_cast<const bf16x8*>(dOb + off) : zero_bf16x8();
+    }
+    l2[t] = valid ? LSEb[row] * kLog2e : 0.f;
+    dd[t] = valid ? Db[row] : 0.f;
+  }
+
+  f32x16 acc[DT][NT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[dt][t] = zero16();
+
+  TileLoader<BN, D> kl, vl;
+  if (ntiles > 0) {
+    kl.load(Kb, ks, 0, L);
+    vl.load(Vb, ks, 0, L);
+    kl.store(smem[0][0]);
+    vl.store(smem[0][1]);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < ntiles;
+    if (more) {
+      kl.load(Kb, ks, (kt + 1) * BN, L);
+      vl.load(Vb, ks, (kt + 1) * BN, L);
+    }
+    const int j0 = kt * BN;
+    if (j0 <= wave_last) {
+      const bf16* Ks = smem[buf][0];
+      const bf16* Vs = smem[buf][1];
+      f32x16 s[2][NT], dp[2][NT];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          s[mt][t] = zero16();
+          dp[mt][t] = zero16();
+        }
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 ak = frag_row(Ks, LS, mt * 32, kk * 16, lane);
+          const bf16x8 av = frag_row(Vs, LS, mt * 32, kk * 16, lane);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            s[mt][t] = mfma32(ak, qf[t][kk], s[mt][t]);
+            dp[mt][t] = mfma32(av, df[t][kk], dp[mt][t]);
+          }
+        }
+      }
+      const bool need_mask = (j0 + BN - 1 > qw) || (j0 + BN > L) || (qw + 32 * NT > L);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int i = qw + t * 32 + l32;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float p = fast_exp2(s[mt][t][r] * c - l2[t]);
+            float ds = p * (dp[mt][t][r] - dd[t]);
+            if (need_mask) {
+              const int j = j0 + mt * 32 + ((r >> 2) << 3) + (g << 2) + (r & 3);
+              if (j > i || j >= L || i >= L) ds = 0.f;
+            }
+            dp[mt][t][r] = ds;
+          }
+      }
+      bf16x8 sb[4][NT];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sb[u][t] = pack8(dp[u >> 1][t], (u & 1) * 8);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bf16x8 ak = frag_tr(Ks, LS, u * 16, dt * 32, lane);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[dt][t] = mfma32(ak, sb[u][t], acc[dt][t]);
+        }
+    }
+    if (more) {
+      kl.store(smem[buf ^ 1][0]);
+      vl.store(smem[buf ^ 1][1]);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int i = qw + t * 32 + l32;
+    if (i < S) {
+      const bool valid = i < L;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (bf16)(valid ? acc[dt][t][rr * 4 + e] * a.scale : 0.f);
+          *reinterpret_cast<bf16x4*>(dQb + (int64_t)i * qs + dt * 32 + rr * 8 + g * 4) = ov;
+        }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Launchers
+// ----------------------------------------------------------------------------
+namespace {
+
+// Rows per query block of the forward / dQ passes, and per key block of the
+// dK/dV pass, for each head dimension.
+template <int D> struct Tiles;
+template <> struct Tiles<64> { static constexpr int FWD_NT = 2, DQ_NT = 2, DKDV_NTJ = 1; };
+template <> struct Tiles<128> { static constexpr int FWD_NT = 1, DQ_NT = 1, DKDV_NTJ = 1; };
+
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+template <typename Args>
+hipError_t launch(const void* fn, int64_t grid, Args args, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
+}
+
+template <int D>
+hipError_t fwd_d(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,
+                 hipStream_t stream) {
+  constexpr int NT = Tiles<D>::FWD_NT;
+  FwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, pr.seqlens,
+            pr.B, pr.S, pr.Hq, pr.Hkv, cdiv(pr.S, 128 * NT), pr.scale};
+  return launch((const void*)&fwd_kernel<D, NT>, (int64_t)a.nqb * pr.B * pr.Hq, a, stream);
+}
+
+template <int D>
+hipError_t pre_d(const Problem& pr, const void* o, const void* d_o, float* delta, hipStream_t stream) {
+  PreArgs a{(const bf16*)o, (const bf16*)d_o, delta, pr.seqlens, pr.B, pr.S, pr.Hq,
+            (int64_t)pr.B * pr.S * pr.Hq};
+  constexpr int rows_per_block = kThreads / (D / 8);
+  return launch((const void*)&preprocess_kernel<D>, (a.rows + rows_per_block - 1) / rows_per_block, a, stream);
+}
+
+template <int D>
+hipError_t dkdv_d(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
+                  const float* lse, const float* delta, void* dk, void* dv, hipStream_t stream) {
+  constexpr int NTJ = Tiles<D>::DKDV_NTJ;
+  BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
+            nullptr, (bf16*)dk, (bf16*)dv, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
+            cdiv(pr.S, 128 * NTJ), pr.scale};
+  return launch((const void*)&bwd_dkdv_kernel<D, NTJ>, (int64_t)a.nblk * pr.B * pr.Hkv, a, stream);
+}
+
+template <int D>
+hipError_t dq_d(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
+                const float* lse, const float* delta, void* dq, hipStream_t stream) {
+  constexpr int NT = Tiles<D>::DQ_NT;
+  BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
+            (bf16*)dq, nullptr, nullptr, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
+            cdiv(pr.S, 128 * NT), pr.scale};
+  return launch((const void*)&bwd_dq_kernel<D, NT>, (int64_t)a.nblk * pr.B * pr.Hq, a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,
+                      hipStream_t stream) {
+  return pr.d == 64 ? fwd_d<64>(pr, q, k, v, o, lse, stream) : fwd_d<128>(pr, q, k, v, o, lse, stream);
+}
+
+hipError_t launch_preprocess(const Problem& pr, const void* o, const void* d_o, float* delta, hipStream_t stream) {
+  return pr.d == 64 ? pre_d<64>(pr, o, d_o, delta, stream) : pre_d<128>(pr, o, d_o, delta, stream);
+}
+
+hipError_t launch_bwd_dkdv(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
+                           const float* lse, const float* delta, void* dk, void* dv, hipStream_t stream) {
+  return pr.d == 64 ? dkdv_d<64>(pr, q, k, v, d_o, lse, delta, dk, dv, stream)
+                    : dkdv_d<128>(pr, q, k, v, d_o, lse, delta, dk, dv, stream);
+}
+
+hipError_t launch_bwd_dq(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
+                         const float* lse, const float* delta, void* dq, hipStream_t stream) {
+  return pr.d == 64 ? dq_d<64>(pr, q, k, v, d_o, lse, delta, dq, stream)
+                    : dq_d<128>(pr, q, k, v, d_o, lse, delta, dq, stream);
+}
+
+int64_t max_grid(const Problem& pr) {
+  // smallest blocks: 128 query rows (forward/dQ), 128 key rows (dK/dV), 16 rows (preprocess)
+  const int64_t nb = (pr.S + 127) / 128;
+  int64_t m = nb * pr.B * pr.Hq;
+  const int64_t pre = ((int64_t)pr.B * pr.S * pr.Hq + 15) / 16;
+  return m > pre ? m : pre;
+}
+
+}  // namespace attn

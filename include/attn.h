@@ -1,0 +1,140 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused causal attention library.
+ *
+ * Operation. Causal scaled-dot-product softmax attention for transformer
+ * training, forward and full backward, with grouped-query heads. The pages
+ * this follows describe it as fused flash attention, forward and backward,
+ * whose probabilities never reach memory, stored in bf16 and accumulated in
+ * fp32 ("Axis", Zyora Labs page, feature list), with query heads sharing kv
+ * heads ("AxiomLM" PyPI page, "Key Features": grouped-query attention). For a
+ * sequence b with valid prefix length L_b, query head h and kv head
+ * g = h / (Hq / Hkv):
+ *
+ *   s_ij  = scale * <Q[b,i,h,:], K[b,j,g,:]>      valid when j <= i < L_b
+ *   LSE_i = ln sum_{j <= i} exp(s_ij)              (-inf when i >= L_b)
+ *   P_ij  = exp(s_ij - LSE_i)
+ *   O_i   = sum_j P_ij V[b,j,g,:]                  (0 when i >= L_b)
+ *   D_i   = <dO_i, O_i>
+ *   dS_ij = P_ij (<dO_i, V_j> - D_i)
+ *   dQ_i  = scale sum_j dS_ij K_j
+ *   dK_j  = scale sum_{h in group g} sum_i dS_ij Q_i
+ *   dV_j  = sum_{h in group g} sum_i P_ij dO_i
+ *
+ * The S x S matrices (scores, P, dS) are never written to device memory:
+ * every call needs O(B * S * H * d) memory only.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or synchronises; work is enqueued on `stream` (0 =
+ *    the null stream) in call order. Buffers must stay alive until the stream
+ *    has run the work.
+ *  - Layouts are dense row-major: Q, O, dO, dQ are [B, S, Hq, d]; K, V, dK, dV
+ *    are [B, S, Hkv, d]; all bf16 (bfloat16 bit patterns). LSE and D are fp32
+ *    [B, Hq, S].
+ *  - Outputs are fully overwritten, including padded rows (zeros, LSE = -inf);
+ *    gradients are not accumulated into existing contents.
+ *  - Every tensor pointer must be 16-byte aligned (seqlens: 4-byte aligned).
+ *  - Arguments are validated on the host before any HIP call; an invalid call
+ *    returns an error code and enqueues nothing. A launch error reported by
+ *    the HIP runtime returns ATTN_ERR_HIP. There is no global error state and
+ *    the functions are thread-safe.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, Hq % Hkv != 0,
+                                non-finite or non-positive scale */
+  ATTN_ERR_UNSUPPORTED = 2,  /* head_dim not in {64, 128}, causal == 0,
+                                sizes whose element count overflows int32 indexing */
+  ATTN_ERR_MISALIGNED = 3,   /* a pointer is not 16-byte aligned */
+  ATTN_ERR_WORKSPACE = 4,    /* workspace smaller than attn_bwd_workspace_bytes() */
+  ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+} attn_status;
+
+typedef struct attn_shape {
+  int32_t batch;       /* B >= 1 */
+  int32_t seqlen;      /* S >= 1 (query and key lengths are equal) */
+  int32_t heads_q;     /* Hq >= 1, a multiple of heads_kv */
+  int32_t heads_kv;    /* Hkv >= 1 */
+  int32_t head_dim;    /* d: 64 or 128 */
+  float scale;         /* softmax scale, finite and > 0 (typically 1/sqrt(d)) */
+  int32_t causal;      /* must be 1 (non-causal attention is not provided) */
+  /* Optional DEVICE int32[B]: valid prefix length L_b of each sequence (right
+     padding). NULL means every sequence has length S. Values are clamped into
+     [0, S] on the device; positions i >= L_b take no part in any sum, may hold
+     any bits (including NaN), and receive zero outputs/gradients. */
+  const int32_t* seqlens;
+} attn_shape;
+
+/*
+ * Forward: O = softmax(scale * Q K^T + causal/padding mask) V, and the fp32
+ * natural-log row normaliser LSE. Q [B,S,Hq,d], K/V [B,S,Hkv,d], O [B,S,Hq,d]
+ * bf16; LSE [B,Hq,S] fp32. Deterministic (bitwise repeatable).
+ */
+attn_status attn_fwd(const attn_shape* shape, const void* q, const void* k, const void* v,
+                     void* o, float* lse, hipStream_t stream);
+
+/*
+ * Backward preprocess: D[b,h,i] = sum_c dO[b,i,h,c] * O[b,i,h,c] accumulated in
+ * fp32 from the bf16 inputs (0 on padded rows). O, dO [B,S,Hq,d] bf16; D
+ * [B,Hq,S] fp32.
+ */
+attn_status attn_bwd_preprocess(const attn_shape* shape, const void* o, const void* d_o,
+                                float* delta, hipStream_t stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for `shape`: O(B*S*H*d) at most,
+ * never O(S^2). The current algorithm computes dQ in a separate pass and needs
+ * none (returns 0). Returns 0 for a NULL shape.
+ */
+size_t attn_bwd_workspace_bytes(const attn_shape* shape);
+
+/*
+ * Backward: dQ, dK, dV from Q, K, V, dO, the forward's LSE and the
+ * preprocess's D. The probabilities are recomputed from LSE tile by tile.
+ * dQ [B,S,Hq,d], dK/dV [B,S,Hkv,d] bf16 (dK/dV summed over each kv head's
+ * query-head group). `workspace` may be NULL when attn_bwd_workspace_bytes()
+ * is 0; otherwise it must be 16-byte aligned and hold at least that many
+ * bytes. Deterministic (bitwise repeatable).
+ */
+attn_status attn_bwd(const attn_shape* shape, const void* q, const void* k, const void* v,
+                     const void* d_o, const float* lse, const float* delta,
+                     void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
+ * The two passes attn_bwd runs, exported separately. They read the same inputs,
+ * write disjoint outputs and do not depend on each other, so a caller may run
+ * them in either order or concurrently on two streams; attn_bwd enqueues
+ * attn_bwd_dkdv then attn_bwd_dq on one stream.
+ *   attn_bwd_dkdv: dK, dV [B,S,Hkv,d] bf16 (one pass per key block over the
+ *                  query rows of every head in the kv head's group).
+ *   attn_bwd_dq:   dQ [B,S,Hq,d] bf16 (one pass per query block over its keys).
+ * Same validation, layouts and error codes as attn_bwd.
+ */
+attn_status attn_bwd_dkdv(const attn_shape* shape, const void* q, const void* k, const void* v,
+                          const void* d_o, const float* lse, const float* delta,
+                          void* dk, void* dv, hipStream_t stream);
+attn_status attn_bwd_dq(const attn_shape* shape, const void* q, const void* k, const void* v,
+                        const void* d_o, const float* lse, const float* delta,
+                        void* dq, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* attn_status_string(attn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

@@ -1,0 +1,102 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the C ABI
+binding, run the oracle on the same seeded inputs, compare.
+
+Tolerances (per tensor, over the compared slice):
+  O, dQ, dK, dV : relative Frobenius error <= 1e-2 and max |gpu - ref| <= 5e-2
+  LSE           : identical -inf pattern, max |gpu - ref| <= 1e-3 on finite rows
+  D             : relative Frobenius error <= 1e-2 (D is computed from the bf16 O)
+and no NaN/Inf anywhere in the GPU outputs except LSE's -inf on padded rows.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import causal_attention_fwd_amd as attn
+import oracle
+
+TOL_REL_FRO = 1e-2
+TOL_MAX_ABS = 5e-2
+TOL_LSE = 1e-3
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_gpu(inp):
+    dev = torch.device("cuda")
+    t = {k: getattr(inp, k).to(dev).contiguous() for k in ("q", "k", "v", "do")}
+    t["seqlens"] = inp.seqlens.to(dev) if inp.seqlens is not None else None
+    return t
+
+
+def run_gpu(inp, t=None):
+    """fwd -> preprocess -> bwd on the GPU; returns host fp32 numpy arrays."""
+    t = t or to_gpu(inp)
+    o, lse = attn.forward(t["q"], t["k"], t["v"], inp.scale, t["seqlens"])
+    dq, dk, dv, delta = attn.backward(t["q"], t["k"], t["v"], o, t["do"], lse, inp.scale, t["seqlens"])
+    torch.cuda.synchronize()
+    host = lambda x: x.float().cpu().numpy()  # noqa: E731
+    return {"O": host(o), "LSE": host(lse), "D": host(delta), "dQ": host(dq), "dK": host(dk), "dV": host(dv)}
+
+
+def host_inputs(inp):
+    q, k, v, do = (x.float().numpy() for x in (inp.q, inp.k, inp.v, inp.do))
+    sl = inp.seqlens.numpy() if inp.seqlens is not None else None
+    return q, k, v, do, sl
+
+
+def oracle_unit(inp, b, hkv, dtype=np.float64):
+    """Oracle on one (sequence, kv head) unit: the kv head and its query-head group."""
+    q, k, v, do, sl = host_inputs(inp)
+    G = q.shape[2] // k.shape[2]
+    hs = slice(hkv * G, (hkv + 1) * G)
+    sub_sl = None if sl is None else sl[b:b + 1]
+    ref = oracle.backward(q[b:b + 1, :, hs], k[b:b + 1, :, hkv:hkv + 1], v[b:b + 1, :, hkv:hkv + 1],
+                          do[b:b + 1, :, hs], inp.scale, sub_sl, dtype=dtype)
+    return ref
+
+
+def slice_unit(gpu, b, hkv, G):
+    hs = slice(hkv * G, (hkv + 1) * G)
+    return {"O": gpu["O"][b:b + 1, :, hs], "dQ": gpu["dQ"][b:b + 1, :, hs],
+            "dK": gpu["dK"][b:b + 1, :, hkv:hkv + 1], "dV": gpu["dV"][b:b + 1, :, hkv:hkv + 1],
+            "LSE": gpu["LSE"][b:b + 1, hs], "D": gpu["D"][b:b + 1, hs]}
+
+
+def metrics(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    diff = got - ref
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(diff) / nref if nref > 0 else np.linalg.norm(diff)
+    return float(rel), float(np.max(np.abs(diff))) if diff.size else 0.0
+
+
+def compare(gpu, ref, label=""):
+    """Assert the parity bar; returns a dict of the measured errors."""
+    report = {}
+    for key in ("O", "dQ", "dK", "dV"):
+        g = gpu[key]
+        assert np.all(np.isfinite(g)), f"{label} {key}: non-finite GPU values"
+        rel, mx = metrics(g, ref[key])
+        report[key] = (rel, mx)
+        assert rel <= TOL_REL_FRO and mx <= TOL_MAX_ABS, f"{label} {key}: rel_fro={rel:.3e} max_abs={mx:.3e}"
+    g, r = gpu["LSE"], np.asarray(ref["LSE"], dtype=np.float64)
+    assert not np.any(np.isnan(g)), f"{label} LSE: NaN"
+    assert np.array_equal(np.isneginf(g), np.isneginf(r)), f"{label} LSE: -inf pattern differs"
+    assert not np.any(np.isposinf(g)), f"{label} LSE: +inf"
+    fin = np.isfinite(r)
+    mx = float(np.max(np.abs(g[fin] - r[fin]))) if np.any(fin) else 0.0
+    report["LSE"] = (0.0, mx)
+    assert mx <= TOL_LSE, f"{label} LSE: max_abs={mx:.3e}"
+    assert np.all(np.isfinite(gpu["D"])), f"{label} D: non-finite"
+    rel, mx = metrics(gpu["D"], ref["D"])
+    report["D"] = (rel, mx)
+    assert rel <= TOL_REL_FRO, f"{label} D: rel_fro={rel:.3e}"
+    say(f"  {label}: " + "  ".join(f"{k} rel={v[0]:.2e} max={v[1]:.2e}" for k, v in report.items()))
+    return report

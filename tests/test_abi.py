@@ -1,0 +1,169 @@
+"""C-ABI checks that need no GPU (CPU only).
+
+The library loads here (ROCm is installed even without a device), exports every
+function include/attn.h declares, and rejects invalid calls with the documented
+status code before any HIP call. No call in this file reaches a kernel launch:
+every call made with placeholder pointers fails host validation first.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import causal_attention_fwd_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn.library_path()):
+        from causal_attention_fwd_amd import build as b
+        b.build()
+    return attn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(attn_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(attn.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", attn.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (attn_[a-z_]+)$", out, re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings(lib):
+    for code, name in attn.STATUS.items():
+        assert attn.attn_status_string(code).startswith(name)
+    assert "UNKNOWN" in attn.attn_status_string(99)
+
+
+def _shape(**kw):
+    base = dict(B=2, S=128, Hq=4, Hkv=2, d=64, scale=0.125, seqlens_ptr=None, causal=1)
+    base.update(kw)
+    return attn.make_shape(base["B"], base["S"], base["Hq"], base["Hkv"], base["d"], base["scale"],
+                           base["seqlens_ptr"], base["causal"])
+
+
+P = ctypes.c_void_p
+GOOD = 0x10000          # placeholder, 16-byte aligned (never dereferenced: validation fails first)
+ODD = 0x10008           # 8-byte aligned only
+
+
+def _fwd(lib, shape, ptrs=(GOOD,) * 5):
+    return lib.attn_fwd(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], P(0))
+
+
+def _bwd(lib, shape, ptrs=(GOOD,) * 9, ws=None, ws_bytes=0):
+    return lib.attn_bwd(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs],
+                        P(ws), ctypes.c_size_t(ws_bytes), P(0))
+
+
+def _dkdv(lib, shape, ptrs=(GOOD,) * 8):
+    return lib.attn_bwd_dkdv(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], P(0))
+
+
+def _dq(lib, shape, ptrs=(GOOD,) * 7):
+    return lib.attn_bwd_dq(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], P(0))
+
+
+def _pre(lib, shape, ptrs=(GOOD,) * 3):
+    return lib.attn_bwd_preprocess(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], P(0))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 1), (dict(S=0), 1), (dict(Hq=0), 1), (dict(Hkv=0), 1), (dict(S=-5), 1),
+    (dict(Hq=6, Hkv=4), 1), (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
+    (dict(scale=0.0), 1), (dict(scale=-0.1), 1),
+    (dict(d=32), 2), (dict(d=96), 2), (dict(d=256), 2), (dict(causal=0), 2),
+    (dict(seqlens_ptr=GOOD + 2), 3),
+    (dict(B=2 ** 30, S=2 ** 20), 2),
+])
+def test_invalid_shapes_rejected(lib, kw, code):
+    shape = _shape(**kw)
+    assert _fwd(lib, shape) == code
+    assert _pre(lib, shape) == code
+    assert _bwd(lib, shape) == code
+    assert _dkdv(lib, shape) == code
+    assert _dq(lib, shape) == code
+
+
+def test_null_shape_and_pointers(lib):
+    assert _fwd(lib, None) == 1
+    assert _pre(lib, None) == 1
+    assert _bwd(lib, None) == 1
+    for i in range(5):
+        ptrs = [GOOD] * 5
+        ptrs[i] = 0
+        assert _fwd(lib, _shape(), ptrs) == 1
+    for i in range(3):
+        ptrs = [GOOD] * 3
+        ptrs[i] = 0
+        assert _pre(lib, _shape(), ptrs) == 1
+    for i in range(9):
+        ptrs = [GOOD] * 9
+        ptrs[i] = 0
+        assert _bwd(lib, _shape(), ptrs) == 1
+    for i in range(8):
+        ptrs = [GOOD] * 8
+        ptrs[i] = 0
+        assert _dkdv(lib, _shape(), ptrs) == 1
+    for i in range(7):
+        ptrs = [GOOD] * 7
+        ptrs[i] = 0
+        assert _dq(lib, _shape(), ptrs) == 1
+    assert _dkdv(lib, None) == 1
+    assert _dq(lib, None) == 1
+
+
+def test_misaligned_pointers(lib):
+    for i in range(5):
+        ptrs = [GOOD] * 5
+        ptrs[i] = ODD
+        assert _fwd(lib, _shape(), ptrs) == 3
+    for i in range(9):
+        ptrs = [GOOD] * 9
+        ptrs[i] = ODD
+        assert _bwd(lib, _shape(), ptrs) == 3
+    for i in range(8):
+        ptrs = [GOOD] * 8
+        ptrs[i] = ODD
+        assert _dkdv(lib, _shape(), ptrs) == 3
+
+
+def test_workspace_bytes_is_linear_not_quadratic(lib):
+    for S in (128, 4096, 16384, 1 << 20):
+        shape = _shape(B=1, S=S, Hq=32, Hkv=8, d=128)
+        ws = lib.attn_bwd_workspace_bytes(ctypes.byref(shape))
+        assert ws <= 1 * S * 32 * 128 * 4
+    assert lib.attn_bwd_workspace_bytes(None) == 0
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 64, 2, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        attn.attn_fwd(q, q, q, q, lse, 0.125)
+
+
+def test_product_path_never_uses_the_oracle():
+    pkg = os.path.join(ROOT, "causal_attention_fwd_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
+                assert "oracle/" not in text, f

@@ -1,0 +1,187 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small shapes are compared element by element over every output; the five
+named workloads run at their full sizes, in the launch configuration the
+benchmark times, and are compared on whole (sequence, kv head) units sampled
+from the batch, plus properties that hold at any size (padding zeros, no
+NaN/Inf).
+"""
+import numpy as np
+import pytest
+import torch
+
+import causal_attention_fwd_amd as attn
+from attn_workloads import WORKLOADS, make_inputs, workload_inputs
+
+from parity import compare, host_inputs, oracle_unit, run_gpu, say, slice_unit, to_gpu
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ small shapes, every element
+
+FUZZ = [
+    # B, S, Hq, Hkv, d, padded-length range or None
+    (1, 1, 1, 1, 64, None),
+    (1, 17, 2, 1, 64, None),
+    (2, 63, 4, 2, 64, None),
+    (1, 64, 3, 1, 64, None),
+    (1, 65, 2, 2, 128, None),
+    (3, 127, 8, 1, 64, None),
+    (1, 128, 4, 4, 128, None),
+    (2, 129, 6, 2, 64, None),
+    (1, 200, 8, 2, 128, None),
+    (3, 300, 4, 1, 64, (0, 300)),
+    (3, 257, 2, 2, 128, (1, 257)),
+    (2, 1000, 6, 3, 64, (500, 1000)),
+    (1, 520, 16, 2, 128, None),
+    (2, 384, 5, 5, 64, (383, 384)),
+]
+
+
+@pytest.mark.parametrize("case", FUZZ, ids=lambda c: "B{}_S{}_H{}-{}_d{}_{}".format(*c[:5], "pad" if c[5] else "dense"))
+def test_fuzz_every_element(case):
+    B, S, Hq, Hkv, d, rng = case
+    seed = 1000 + B * 7 + S * 13 + Hq * 17 + d
+    say(f"fuzz case B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} pad={rng} seed={seed}: attn_fwd/preprocess/attn_bwd")
+    inp = make_inputs(B, S, Hq, Hkv, d, seed, padded=rng is not None, seqlen_range=rng)
+    gpu = run_gpu(inp)
+    q, k, v, do, sl = host_inputs(inp)
+    ref = oracle.backward(q, k, v, do, inp.scale, sl)
+    compare(gpu, ref, f"fuzz{case}")
+
+
+def test_zero_length_sequences():
+    say("edge: every sequence has valid length 0")
+    B, S, Hq, Hkv, d = 2, 96, 4, 2, 64
+    inp = make_inputs(B, S, Hq, Hkv, d, 7, padded=True, seqlen_range=(0, 0))
+    gpu = run_gpu(inp)
+    for key in ("O", "dQ", "dK", "dV", "D"):
+        assert np.all(gpu[key] == 0.0), key
+    assert np.all(np.isneginf(gpu["LSE"]))
+
+
+# ------------------------------------------------------------------ the five workloads at full size
+
+def _units(w, inp):
+    """(b, kv head) units compared against the oracle for a workload."""
+    if w.name in ("tiny", "gqa124m"):
+        return None  # every unit
+    if w.name == "llama1b":
+        return [(0, 0), (3, 7), (2, 5)]
+    if w.name == "padded":
+        L = inp.seqlens.tolist()
+        return [(int(np.argmin(L)), 0), (int(np.argmax(L)), 15), (3, 9)]
+    if w.name == "longseq":
+        return [(0, 5)]
+    raise KeyError(w.name)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.timeout(600)
+def test_workload_parity(name):
+    w = WORKLOADS[name]
+    say(f"workload {name}: {w.describe()} seed={w.seed}")
+    inp = workload_inputs(w)
+    gpu = run_gpu(inp)
+    say(f"workload {name}: GPU done, oracle running")
+    units = _units(w, inp)
+    if units is None:
+        q, k, v, do, sl = host_inputs(inp)
+        compare(gpu, oracle.backward(q, k, v, do, inp.scale, sl), name)
+    else:
+        dtype = np.float32 if name == "longseq" else np.float64
+        G = w.Hq // w.Hkv
+        for b, hkv in units:
+            say(f"workload {name}: unit b={b} kv_head={hkv}")
+            ref = oracle_unit(inp, b, hkv, dtype)
+            compare(slice_unit(gpu, b, hkv, G), ref, f"{name}[b={b},g={hkv}]")
+    # properties over the whole output
+    for key in ("O", "dQ", "dK", "dV", "D"):
+        assert np.all(np.isfinite(gpu[key])), key
+    if inp.seqlens is not None:
+        for b, L in enumerate(inp.seqlens.tolist()):
+            for key in ("O", "dQ", "dK", "dV"):
+                assert np.all(gpu[key][b, L:] == 0.0), (key, b)
+            assert np.all(np.isneginf(gpu["LSE"][b, :, L:]))
+            assert np.all(np.isfinite(gpu["LSE"][b, :, :L]))
+    else:
+        assert np.all(np.isfinite(gpu["LSE"]))
+
+
+# ------------------------------------------------------------------ contracts
+
+def test_nan_in_padding_does_not_leak():
+    say("contract: NaN-filled padded positions")
+    B, S, Hq, Hkv, d = 3, 333, 4, 2, 128
+    inp = make_inputs(B, S, Hq, Hkv, d, 31, padded=True, seqlen_range=(100, 300))
+    clean = run_gpu(inp)
+    for name in ("q", "k", "v", "do"):
+        x = getattr(inp, name)
+        for b, L in enumerate(inp.seqlens.tolist()):
+            x[b, L:] = float("nan")
+    dirty = run_gpu(inp)
+    for key in clean:
+        np.testing.assert_array_equal(clean[key], dirty[key], err_msg=key)
+
+
+def test_deterministic_and_stream_ordered():
+    say("contract: bitwise repeatability and a non-default stream")
+    inp = make_inputs(2, 700, 8, 2, 64, 41)
+    first = run_gpu(inp)
+    second = run_gpu(inp)
+    for key in first:
+        np.testing.assert_array_equal(first[key], second[key], err_msg=key)
+    s = torch.cuda.Stream()
+    t = to_gpu(inp)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        third = run_gpu(inp, t)
+    for key in first:
+        np.testing.assert_array_equal(first[key], third[key], err_msg=key)
+
+
+def test_library_allocates_nothing():
+    say("contract: no device allocation inside the library")
+    inp = make_inputs(1, 512, 4, 2, 64, 5)
+    t = to_gpu(inp)
+    B, S, Hq, d = inp.q.shape
+    o = torch.empty_like(t["q"])
+    lse = torch.empty(B, Hq, S, device="cuda")
+    delta = torch.empty(B, Hq, S, device="cuda")
+    dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(3):
+        attn.attn_fwd(t["q"], t["k"], t["v"], o, lse, inp.scale)
+        attn.attn_bwd_preprocess(o, t["do"], delta)
+        attn.attn_bwd(t["q"], t["k"], t["v"], t["do"], lse, delta, dq, dk, dv, inp.scale)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free0 == free1
+
+
+def test_preprocess_alone_tight():
+    say("preprocess on independent random O/dO")
+    inp = make_inputs(2, 300, 6, 6, 128, 77, padded=True, seqlen_range=(150, 300))
+    t = to_gpu(inp)
+    delta = torch.empty(2, 6, 300, device="cuda")
+    attn.attn_bwd_preprocess(t["q"], t["do"], delta, t["seqlens"])   # q stands in for an O tensor
+    torch.cuda.synchronize()
+    q, _, _, do, sl = host_inputs(inp)
+    ref = oracle.preprocess(q, do, sl)
+    got = delta.cpu().numpy()
+    # fp32 accumulation of 128 exact bf16 products: |err| <= 128 * 2^-24 * sum|q*do|
+    bound = 128 * 2.0 ** -24 * np.einsum("bshc->bhs", np.abs(q * do)) + 1e-30
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_invalid_call_raises_without_launch():
+    t = to_gpu(make_inputs(1, 64, 2, 1, 64, 3))
+    o = torch.empty_like(t["q"])
+    lse = torch.empty(1, 2, 64, device="cuda")
+    with pytest.raises(attn.AttnError) as e:
+        attn.attn_fwd(t["q"], t["k"], t["v"], o, lse, float("nan"))
+    assert e.value.code == 1
