@@ -48,6 +48,16 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max / sum of x over lanes l and l ^ 32 (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Row fragment from an LDS tile stored row-major with `stride` elements per row:
 // lane l gets tile[row0 + l%32][col0 + (l/32)*8 .. +7] (one 16-byte read).
 __device__ __forceinline__ bf16x8 frag_row(const bf16* tile, int stride, int row0, int col0, int lane) {
@@ -70,13 +80,22 @@ __device__ __forceinline__ bf16x8 frag_tr(const bf16* tile, int stride, int row0
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Eight consecutive C-tile registers (r0 .. r0+7) rounded to a bf16 operand.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Eight consecutive C-tile registers (r0 .. r0+7) rounded (RNE) to a bf16
+// operand: four v_cvt_pk_bf16_f32, one per register pair.
 __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int r0) {
-  bf16x8 v;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (bf16)c[r0 + e];
-  return v;
+  const bf16x2v p0 = __builtin_convertvector((f32x2v){c[r0 + 0], c[r0 + 1]}, bf16x2v);
+  const bf16x2v p1 = __builtin_convertvector((f32x2v){c[r0 + 2], c[r0 + 3]}, bf16x2v);
+  const bf16x2v p2 = __builtin_convertvector((f32x2v){c[r0 + 4], c[r0 + 5]}, bf16x2v);
+  const bf16x2v p3 = __builtin_convertvector((f32x2v){c[r0 + 6], c[r0 + 7]}, bf16x2v);
+  return (bf16x8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
+
+// Offset of C-tile register r's row (or column) from the lane's base row
+// (r/4)*8 + r%4; the lane's base adds (lane/32)*4.
+__device__ __forceinline__ constexpr int creg_off(int r) { return ((r >> 2) << 3) + (r & 3); }
 
 // Query-block tiles (forward, dQ): grid = nqb * B * Hq workgroups. Longest
 // causal rows first (largest q block first). When the kv groups split evenly
@@ -103,20 +122,25 @@ __device__ __forceinline__ void decode_qblock(int bid, int nqb, int B, int Hq, i
   }
 }
 
-// Key-block tiles (dK/dV): grid = nkb * B * Hkv. Longest first = the first key
-// block (it sees every query row); kv groups pinned to XCDs as above.
-__device__ __forceinline__ void decode_kblock(int bid, int B, int Hkv, int& kb, int& b, int& hkv) {
+// Key-block tiles (dK/dV): grid = nkb * B * Hkv. A key block's work grows with
+// the number of query rows below it, so the first half of the dispatch order
+// walks key blocks 0, 1, ... (longest first) and the second half walks them
+// from the far end, so that when two workgroups share a CU, a long block tends
+// to pair with a short one. kv groups are pinned to XCDs as above.
+__device__ __forceinline__ void decode_kblock(int bid, int nkb, int B, int Hkv, int& kb, int& b, int& hkv) {
   const int units = B * Hkv;
-  int unit;
+  int unit, ks;
   if ((units & 7) == 0) {
     const int xcd = bid & 7, slot = bid >> 3;
     const int upx = units >> 3;
-    kb = slot / upx;
-    unit = xcd * upx + (slot - kb * upx);
+    ks = slot / upx;
+    unit = xcd * upx + (slot - ks * upx);
   } else {
-    kb = bid / units;
-    unit = bid - kb * units;
+    ks = bid / units;
+    unit = bid - ks * units;
   }
+  const int half = (nkb + 1) >> 1;
+  kb = ks < half ? ks : nkb - 1 - (ks - half);
   b = unit / Hkv;
   hkv = unit - b * Hkv;
 }

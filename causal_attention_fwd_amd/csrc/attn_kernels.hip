@@ -105,16 +105,111 @@ struct TileLoader {
 // ----------------------------------------------------------------------------
 // Forward. One workgroup = one (sequence, query head, block of 128*NT query
 // rows); wave w owns rows [q0 + 32*NT*w, +32*NT). Loop over 64-row K/V tiles up
-// to the block's last row.
+// to the block's last row. OCC waves per SIMD (register budget 512/OCC).
+//
+// Online softmax with a lazily refreshed reference: each row keeps the maximum
+// it last rescaled to (mu). A tile's exponents use mu unless the row maximum
+// has grown by more than 2^8 (in base-2 units), in which case the accumulator
+// and running sum are rescaled to the new maximum. Exponents therefore stay
+// <= 2^8, well inside fp32 and bf16 range, and the rescale almost never runs
+// once the first tile has set mu. O = acc / l and LSE = mu*scale + ln l use the
+// same mu, so the result is exact whatever mu is.
 // ----------------------------------------------------------------------------
 template <int D, int NT>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
+struct FwdState {
+  bf16x8 qf[NT][D / 16];
+  f32x16 oacc[D / 32][NT];
+  float mu[NT], lsum[NT];
+};
+
+// One 64-key tile for one wave. MASK: keys past min(row, L-1) are excluded;
+// lim[t] = min(i, L-1) - j0 - (lane/32)*4 for the lane's row i of n-tile t.
+template <int D, int NT, bool MASK>
+__device__ __forceinline__ void fwd_tile(FwdState<D, NT>& st, const bf16* Ks, const bf16* Vs, int lane, float c,
+                                         const int (&lim)[NT]) {
+  constexpr int KK = D / 16, DT = D / 32, LS = D + 8;
+  constexpr float kHeadroom = 8.f;  // log2 of the largest exponent allowed before a rescale
+  f32x16 s[2][NT];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) s[mt][t] = zero16();
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const bf16x8 af = frag_row(Ks, LS, mt * 32, kk * 16, lane);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) s[mt][t] = mfma32(af, st.qf[t][kk], s[mt][t]);
+    }
+  }
+  if (MASK) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (mt * 32 + creg_off(r) > lim[t]) s[mt][t][r] = kNegInf;
+  }
+  float alpha[NT];
+  bool rescale = false;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][t][r]);
+    mx = xhalf_max(mx);
+    // (mx - mu) * c is NaN (no refresh) when both are -inf
+    const bool refresh = (mx - st.mu[t]) * c > kHeadroom;
+    alpha[t] = refresh ? fast_exp2((st.mu[t] - mx) * c) : 1.f;
+    rescale |= refresh;
+    st.mu[t] = refresh ? mx : st.mu[t];
+    const float mc = st.mu[t] == kNegInf ? 0.f : st.mu[t] * c;
+    float ls = 0.f;  // fp32 sum of the unrounded probabilities (LSE needs it)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[mt][t][r], c, -mc));
+        s[mt][t][r] = p;
+        ls += p;
+      }
+    st.lsum[t] = st.lsum[t] * alpha[t] + ls;
+  }
+  if (__ballot(rescale)) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.oacc[dt][t][r] *= alpha[t];
+  }
+  bf16x8 pb[4][NT];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) pb[u][t] = pack8(s[u >> 1][t], (u & 1) * 8);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bf16x8 af = frag_tr(Vs, LS, u * 16, dt * 32, lane);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) st.oacc[dt][t] = mfma32(af, pb[u][t], st.oacc[dt][t]);
+    }
+}
+
+template <int D, int NT, int OCC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void fwd_kernel(FwdArgs a) {
   constexpr int BN = 64;
   constexpr int BM = 4 * 32 * NT;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
-  constexpr int LS = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * LS];
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * (D + 8)];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -140,24 +235,18 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   const int wave_last = min(qw + 32 * NT, L) - 1;  // < qw when the wave is all padding
   const float c = a.scale * kLog2e;
 
-  bf16x8 qf[NT][KK];
+  FwdState<D, NT> st;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int row = qw + t * 32 + l32;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qf[t][kk] = row < L ? *reinterpret_cast<const bf16x8*>(Qb + (int64_t)row * qs + kk * 16 + g * 8)
-                          : zero_bf16x8();
-  }
-
-  f32x16 oacc[DT][NT];
-  float m[NT], lsum[NT];
+      st.qf[t][kk] = row < L ? *reinterpret_cast<const bf16x8*>(Qb + (int64_t)row * qs + kk * 16 + g * 8)
+                             : zero_bf16x8();
+    st.mu[t] = kNegInf;
+    st.lsum[t] = 0.f;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    m[t] = kNegInf;
-    lsum[t] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt][t] = zero16();
+    for (int dt = 0; dt < DT; ++dt) st.oacc[dt][t] = zero16();
   }
 
   TileLoader<BN, D> kl, vl;
@@ -178,72 +267,15 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     }
     const int j0 = kt * BN;
     if (j0 <= wave_last) {
-      const bf16* Ks = smem[buf][0];
-      const bf16* Vs = smem[buf][1];
-      f32x16 s[2][NT];
+      if ((j0 + BN - 1 > qw) || (j0 + BN > L)) {
+        int lim[NT];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) s[mt][t] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 af = frag_row(Ks, LS, mt * 32, kk * 16, lane);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) s[mt][t] = mfma32(af, qf[t][kk], s[mt][t]);
-        }
+        for (int t = 0; t < NT; ++t) lim[t] = min(qw + t * 32 + l32, L - 1) - j0 - g * 4;
+        fwd_tile<D, NT, true>(st, smem[buf][0], smem[buf][1], lane, c, lim);
+      } else {
+        const int lim[NT] = {};
+        fwd_tile<D, NT, false>(st, smem[buf][0], smem[buf][1], lane, c, lim);
       }
-      const bool need_mask = (j0 + BN - 1 > qw) || (j0 + BN > L);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int i = qw + t * 32 + l32;
-        float mx = kNegInf;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = s[mt][t][r] * c;
-            if (need_mask) {
-              const int j = j0 + mt * 32 + ((r >> 2) << 3) + (g << 2) + (r & 3);
-              if (j > i || j >= L) x = kNegInf;
-            }
-            s[mt][t][r] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m[t], mx);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m[t] - m_use);
-        m[t] = m_new;
-        float ls = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(s[mt][t][r] - m_use);
-            s[mt][t][r] = p;
-            ls += p;
-          }
-        lsum[t] = lsum[t] * alpha + ls;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][t][r] *= alpha;
-      }
-      bf16x8 pb[4][NT];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) pb[u][t] = pack8(s[u >> 1][t], (u & 1) * 8);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16x8 af = frag_tr(Vs, LS, u * 16, dt * 32, lane);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) oacc[dt][t] = mfma32(af, pb[u][t], oacc[dt][t]);
-        }
     }
     if (more) {
       kl.store(smem[buf ^ 1][0]);
@@ -252,11 +284,11 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     __syncthreads();
   }
 
-  // Epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2; padded rows 0 / -inf.
+  // Epilogue: O = acc / l (bf16), LSE = mu*scale + ln l; padded rows 0 / -inf.
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int i = qw + t * 32 + l32;
-    const float lt = lsum[t] + __shfl_xor(lsum[t], 32);
+    const float lt = xhalf_sum(st.lsum[t]);
     if (i < S) {
       const bool valid = i < L;
       const float inv = valid ? 1.f / lt : 0.f;
@@ -266,10 +298,10 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
         for (int rr = 0; rr < 4; ++rr) {
           bf16x4 ov;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = (bf16)(oacc[dt][t][rr * 4 + e] * inv);
+          for (int e = 0; e < 4; ++e) ov[e] = (bf16)(st.oacc[dt][t][rr * 4 + e] * inv);
           *reinterpret_cast<bf16x4*>(Ob + (int64_t)i * qs + dt * 32 + rr * 8 + g * 4) = ov;
         }
-      if (g == 0) LSEb[i] = valid ? (m[t] + __log2f(lt)) * kLn2 : kNegInf;
+      if (g == 0) LSEb[i] = valid ? (st.mu[t] * c + __log2f(lt)) * kLn2 : kNegInf;
     }
   }
 }
@@ -310,14 +342,98 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
 // to the valid length.
 // ----------------------------------------------------------------------------
 template <int D, int NTJ>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
+struct DkdvState {
+  bf16x8 kf[NTJ][D / 16], vf[NTJ][D / 16];
+  f32x16 dk[D / 32][NTJ], dv[D / 32][NTJ];
+};
+
+// One 64-row query tile for one wave. MASK: query row i of register (m2, r)
+// takes part only if lo[t] <= m2*32 + creg_off(r) <= hi[t] (causal, and both
+// positions inside the valid length).
+template <int D, int NTJ, bool MASK>
+__device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs, const bf16* dOs, const float* lse2,
+                                          const float* dl, int lane, float c, const int (&lo)[NTJ],
+                                          const int (&hi)[NTJ]) {
+  constexpr int KK = D / 16, DT = D / 32, LS = D + 8;
+  const int g = lane >> 5;
+  f32x16 s[2][NTJ], dp[2][NTJ];
+#pragma unroll
+  for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+    for (int t = 0; t < NTJ; ++t) {
+      s[m2][t] = zero16();
+      dp[m2][t] = zero16();
+    }
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2) {
+      const bf16x8 aq = frag_row(Qs, LS, m2 * 32, kk * 16, lane);
+      const bf16x8 ad = frag_row(dOs, LS, m2 * 32, kk * 16, lane);
+#pragma unroll
+      for (int t = 0; t < NTJ; ++t) {
+        s[m2][t] = mfma32(aq, st.kf[t][kk], s[m2][t]);
+        dp[m2][t] = mfma32(ad, st.vf[t][kk], dp[m2][t]);
+      }
+    }
+  }
+  // P = exp2(S*c - LSE*log2e), dS = P (dP - D); rows m2*32 + rr*8 + g*4 + e of
+  // the lane's registers rr*4 + e, read four at a time
+#pragma unroll
+  for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int il0 = m2 * 32 + rr * 8 + g * 4;
+      const float4 l2 = *reinterpret_cast<const float4*>(lse2 + il0);
+      const float4 d4 = *reinterpret_cast<const float4*>(dl + il0);
+      const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
+      const float ddv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rr * 4 + e;
+#pragma unroll
+        for (int t = 0; t < NTJ; ++t) {
+          float p = fast_exp2(__builtin_fmaf(s[m2][t][r], c, -l2v[e]));
+          if (MASK) {
+            const int off = m2 * 32 + rr * 8 + e;
+            if (off < lo[t] || off > hi[t]) p = 0.f;
+          }
+          dp[m2][t][r] = p * (dp[m2][t][r] - ddv[e]);
+          s[m2][t][r] = p;
+        }
+      }
+    }
+  bf16x8 pb[4][NTJ], sb[4][NTJ];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int t = 0; t < NTJ; ++t) {
+      pb[u][t] = pack8(s[u >> 1][t], (u & 1) * 8);
+      sb[u][t] = pack8(dp[u >> 1][t], (u & 1) * 8);
+    }
+#pragma unroll
+  for (int ct = 0; ct < DT; ++ct)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bf16x8 ado = frag_tr(dOs, LS, u * 16, ct * 32, lane);
+      const bf16x8 aq = frag_tr(Qs, LS, u * 16, ct * 32, lane);
+#pragma unroll
+      for (int t = 0; t < NTJ; ++t) {
+        st.dv[ct][t] = mfma32(ado, pb[u][t], st.dv[ct][t]);
+        st.dk[ct][t] = mfma32(aq, sb[u][t], st.dk[ct][t]);
+      }
+    }
+}
+
+template <int D, int NTJ, int OCC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BMQ = 64;
   constexpr int BN = 4 * 32 * NTJ;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
-  constexpr int LS = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BMQ * LS];  // [buf][Q, dO]
-  __shared__ float sstat[2][2][BMQ];                                 // [buf][LSE*log2e, D]
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BMQ * (D + 8)];  // [buf][Q, dO]
+  __shared__ __attribute__((aligned(16))) float sstat[2][2][BMQ];         // [buf][LSE*log2e, D]
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -325,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int l32 = lane & 31;
 
   int kb, b, hkv;
-  decode_kblock(blockIdx.x, a.B, a.Hkv, kb, b, hkv);
+  decode_kblock(blockIdx.x, a.nblk, a.B, a.Hkv, kb, b, hkv);
   const int S = a.S;
   const int L = valid_len(a.seqlens, b, S);
   const int G = a.Hq / a.Hkv;
@@ -338,26 +454,22 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int jw = j0 + wave * 32 * NTJ;
   const float c = a.scale * kLog2e;
 
-  bf16x8 kf[NTJ][KK], vf[NTJ][KK];
+  DkdvState<D, NTJ> st;
 #pragma unroll
   for (int t = 0; t < NTJ; ++t) {
     const int j = jw + t * 32 + l32;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int64_t off = (int64_t)j * ks + kk * 16 + g * 8;
-      kf[t][kk] = j < L ? *reinterpret_cast<const bf16x8*>(Kb + off) : zero_bf16x8();
-      vf[t][kk] = j < L ? *reinterpret_cast<const bf16x8*>(Vb + off) : zero_bf16x8();
+      st.kf[t][kk] = j < L ? *reinterpret_cast<const bf16x8*>(Kb + off) : zero_bf16x8();
+      st.vf[t][kk] = j < L ? *reinterpret_cast<const bf16x8*>(Vb + off) : zero_bf16x8();
+    }
+#pragma unroll
+    for (int ct = 0; ct < DT; ++ct) {
+      st.dk[ct][t] = zero16();
+      st.dv[ct][t] = zero16();
     }
   }
-
-  f32x16 dk[DT][NTJ], dv[DT][NTJ];
-#pragma unroll
-  for (int ct = 0; ct < DT; ++ct)
-#pragma unroll
-    for (int t = 0; t < NTJ; ++t) {
-      dk[ct][t] = zero16();
-      dv[ct][t] = zero16();
-    }
 
   const int qt0 = j0 / BMQ;
   const int nq = (j0 < L) ? (L - 1) / BMQ - qt0 + 1 : 0;  // query tiles per head
@@ -404,75 +516,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
     // skip when every query row of the tile is above this wave's key rows, or the
     // wave's keys are all padding
     if (i0 + BMQ - 1 >= jw && jw < L) {
-      const bf16* Qs = smem[buf][0];
-      const bf16* dOs = smem[buf][1];
-      const float* lse2 = sstat[buf][0];
-      const float* dl = sstat[buf][1];
-      f32x16 s[2][NTJ], dp[2][NTJ];
-#pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2)
+      if ((i0 < jw + 32 * NTJ - 1) || (i0 + BMQ > L) || (jw + 32 * NTJ > L)) {
+        int lo[NTJ], hi[NTJ];
 #pragma unroll
         for (int t = 0; t < NTJ; ++t) {
-          s[m2][t] = zero16();
-          dp[m2][t] = zero16();
+          const int j = jw + t * 32 + l32;
+          lo[t] = j - i0 - g * 4;                              // i >= j
+          hi[t] = (j < L) ? L - 1 - i0 - g * 4 : -1;           // i < L, and no rows when j >= L
         }
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2) {
-          const bf16x8 aq = frag_row(Qs, LS, m2 * 32, kk * 16, lane);
-          const bf16x8 ad = frag_row(dOs, LS, m2 * 32, kk * 16, lane);
-#pragma unroll
-          for (int t = 0; t < NTJ; ++t) {
-            s[m2][t] = mfma32(aq, kf[t][kk], s[m2][t]);
-            dp[m2][t] = mfma32(ad, vf[t][kk], dp[m2][t]);
-          }
-        }
+        dkdv_tile<D, NTJ, true>(st, smem[buf][0], smem[buf][1], sstat[buf][0], sstat[buf][1], lane, c, lo, hi);
+      } else {
+        const int lo[NTJ] = {}, hi[NTJ] = {};
+        dkdv_tile<D, NTJ, false>(st, smem[buf][0], smem[buf][1], sstat[buf][0], sstat[buf][1], lane, c, lo, hi);
       }
-      const bool need_mask = (i0 < jw + 32 * NTJ - 1) || (i0 + BMQ > L) || (jw + 32 * NTJ > L);
-#pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int il = m2 * 32 + ((r >> 2) << 3) + (g << 2) + (r & 3);
-          const float l2 = lse2[il];
-          const float dd = dl[il];
-#pragma unroll
-          for (int t = 0; t < NTJ; ++t) {
-            float p = fast_exp2(s[m2][t][r] * c - l2);
-            float ds = p * (dp[m2][t][r] - dd);
-            if (need_mask) {
-              const int i = i0 + il;
-              const int j = jw + t * 32 + l32;
-              if (j > i || i >= L || j >= L) {
-                p = 0.f;
-                ds = 0.f;
-              }
-            }
-            s[m2][t][r] = p;
-            dp[m2][t][r] = ds;
-          }
-        }
-      bf16x8 pb[4][NTJ], sb[4][NTJ];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int t = 0; t < NTJ; ++t) {
-          pb[u][t] = pack8(s[u >> 1][t], (u & 1) * 8);
-          sb[u][t] = pack8(dp[u >> 1][t], (u & 1) * 8);
-        }
-#pragma unroll
-      for (int ct = 0; ct < DT; ++ct)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16x8 ado = frag_tr(dOs, LS, u * 16, ct * 32, lane);
-          const bf16x8 aq = frag_tr(Qs, LS, u * 16, ct * 32, lane);
-#pragma unroll
-          for (int t = 0; t < NTJ; ++t) {
-            dv[ct][t] = mfma32(ado, pb[u][t], dv[ct][t]);
-            dk[ct][t] = mfma32(aq, sb[u][t], dk[ct][t]);
-          }
-        }
     }
     if (more) store_tile(buf ^ 1);
     __syncthreads();
@@ -493,8 +549,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
           bf16x4 kv4, vv4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            kv4[e] = (bf16)(valid ? dk[ct][t][rr * 4 + e] * a.scale : 0.f);
-            vv4[e] = (bf16)(valid ? dv[ct][t][rr * 4 + e] : 0.f);
+            kv4[e] = (bf16)(valid ? st.dk[ct][t][rr * 4 + e] * a.scale : 0.f);
+            vv4[e] = (bf16)(valid ? st.dv[ct][t][rr * 4 + e] : 0.f);
           }
           const int64_t off = (int64_t)j * ks + ct * 32 + rr * 8 + g * 4;
           *reinterpret_cast<bf16x4*>(dKb + off) = kv4;
@@ -510,13 +566,72 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 // dQ^T += K^T dS^T.
 // ----------------------------------------------------------------------------
 template <int D, int NT>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
+struct DqState {
+  bf16x8 qf[NT][D / 16], df[NT][D / 16];
+  float l2[NT], dd[NT];
+  f32x16 acc[D / 32][NT];
+};
+
+// One 64-key tile for one wave. MASK: key register offset must be <= lim[t]
+// (lim < 0 excludes the whole row).
+template <int D, int NT, bool MASK>
+__device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, const bf16* Vs, int lane, float c,
+                                        const int (&lim)[NT]) {
+  constexpr int KK = D / 16, DT = D / 32, LS = D + 8;
+  f32x16 s[2][NT], dp[2][NT];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      s[mt][t] = zero16();
+      dp[mt][t] = zero16();
+    }
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const bf16x8 ak = frag_row(Ks, LS, mt * 32, kk * 16, lane);
+      const bf16x8 av = frag_row(Vs, LS, mt * 32, kk * 16, lane);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        s[mt][t] = mfma32(ak, st.qf[t][kk], s[mt][t]);
+        dp[mt][t] = mfma32(av, st.df[t][kk], dp[mt][t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(s[mt][t][r], c, -st.l2[t]));
+        if (MASK && mt * 32 + creg_off(r) > lim[t]) p = 0.f;
+        dp[mt][t][r] = p * (dp[mt][t][r] - st.dd[t]);
+      }
+  bf16x8 sb[4][NT];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sb[u][t] = pack8(dp[u >> 1][t], (u & 1) * 8);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bf16x8 ak = frag_tr(Ks, LS, u * 16, dt * 32, lane);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) st.acc[dt][t] = mfma32(ak, sb[u][t], st.acc[dt][t]);
+    }
+}
+
+template <int D, int NT, int OCC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = 64;
   constexpr int BM = 4 * 32 * NT;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
-  constexpr int LS = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * LS];
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * (D + 8)];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -544,8 +659,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
   const int wave_last = min(qw + 32 * NT, L) - 1;
   const float c = a.scale * kLog2e;
 
-  bf16x8 qf[NT][KK], df[NT][KK];
-  float l2[NT], dd[NT];
+  DqState<D, NT> st;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int row = qw + t * 32 + l32;
@@ -553,18 +667,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int64_t off = (int64_t)row * qs + kk * 16 + g * 8;
-      qf[t][kk] = valid ? *reinterpret_cast<const bf16x8*>(Qb + off) : zero_bf16x8();
-      df[t][kk] = valid ? *reinterpret_cast<const bf16x8*>(dOb + off) : zero_bf16x8();
+      st.qf[t][kk] = valid ? *reinterpret_cast<const bf16x8*>(Qb + off) : zero_bf16x8();
+      st.df[t][kk] = valid ? *reinterpret_cast<const bf16x8*>(dOb + off) : zero_bf16x8();
     }
-    l2[t] = valid ? LSEb[row] * kLog2e : 0.f;
-    dd[t] = valid ? Db[row] : 0.f;
+    st.l2[t] = valid ? LSEb[row] * kLog2e : 0.f;
+    st.dd[t] = valid ? Db[row] : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.acc[dt][t] = zero16();
   }
-
-  f32x16 acc[DT][NT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[dt][t] = zero16();
 
   TileLoader<BN, D> kl, vl;
   if (ntiles > 0) {
@@ -584,59 +694,18 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
     }
     const int j0 = kt * BN;
     if (j0 <= wave_last) {
-      const bf16* Ks = smem[buf][0];
-      const bf16* Vs = smem[buf][1];
-      f32x16 s[2][NT], dp[2][NT];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      if ((j0 + BN - 1 > qw) || (j0 + BN > L) || (qw + 32 * NT > L)) {
+        int lim[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          s[mt][t] = zero16();
-          dp[mt][t] = zero16();
+          const int i = qw + t * 32 + l32;
+          lim[t] = i < L ? min(i, L - 1) - j0 - g * 4 : -1;
         }
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 ak = frag_row(Ks, LS, mt * 32, kk * 16, lane);
-          const bf16x8 av = frag_row(Vs, LS, mt * 32, kk * 16, lane);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            s[mt][t] = mfma32(ak, qf[t][kk], s[mt][t]);
-            dp[mt][t] = mfma32(av, df[t][kk], dp[mt][t]);
-          }
-        }
+        dq_tile<D, NT, true>(st, smem[buf][0], smem[buf][1], lane, c, lim);
+      } else {
+        const int lim[NT] = {};
+        dq_tile<D, NT, false>(st, smem[buf][0], smem[buf][1], lane, c, lim);
       }
-      const bool need_mask = (j0 + BN - 1 > qw) || (j0 + BN > L) || (qw + 32 * NT > L);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int i = qw + t * 32 + l32;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float p = fast_exp2(s[mt][t][r] * c - l2[t]);
-            float ds = p * (dp[mt][t][r] - dd[t]);
-            if (need_mask) {
-              const int j = j0 + mt * 32 + ((r >> 2) << 3) + (g << 2) + (r & 3);
-              if (j > i || j >= L || i >= L) ds = 0.f;
-            }
-            dp[mt][t][r] = ds;
-          }
-      }
-      bf16x8 sb[4][NT];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) sb[u][t] = pack8(dp[u >> 1][t], (u & 1) * 8);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16x8 ak = frag_tr(Ks, LS, u * 16, dt * 32, lane);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) acc[dt][t] = mfma32(ak, sb[u][t], acc[dt][t]);
-        }
     }
     if (more) {
       kl.store(smem[buf ^ 1][0]);
@@ -656,7 +725,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
         for (int rr = 0; rr < 4; ++rr) {
           bf16x4 ov;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = (bf16)(valid ? acc[dt][t][rr * 4 + e] * a.scale : 0.f);
+          for (int e = 0; e < 4; ++e) ov[e] = (bf16)(valid ? st.acc[dt][t][rr * 4 + e] * a.scale : 0.f);
           *reinterpret_cast<bf16x4*>(dQb + (int64_t)i * qs + dt * 32 + rr * 8 + g * 4) = ov;
         }
     }
@@ -668,11 +737,50 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 // ----------------------------------------------------------------------------
 namespace {
 
-// Rows per query block of the forward / dQ passes, and per key block of the
-// dK/dV pass, for each head dimension.
+// Per head dimension: 32-row tiles per wave (NT: query rows in the forward and
+// dQ passes; the dK/dV pass always gives each wave 32 key rows) and waves per
+// SIMD (OCC: the register budget per wave is 512 / OCC).
+#ifndef ATTN_FWD_NT64
+#define ATTN_FWD_NT64 2
+#endif
+#ifndef ATTN_FWD_OCC64
+#define ATTN_FWD_OCC64 2
+#endif
+#ifndef ATTN_DQ_NT64
+#define ATTN_DQ_NT64 1
+#endif
+#ifndef ATTN_DQ_OCC64
+#define ATTN_DQ_OCC64 2
+#endif
+#ifndef ATTN_DKDV_OCC64
+#define ATTN_DKDV_OCC64 2
+#endif
+#ifndef ATTN_FWD_NT128
+#define ATTN_FWD_NT128 1
+#endif
+#ifndef ATTN_FWD_OCC128
+#define ATTN_FWD_OCC128 2
+#endif
+#ifndef ATTN_DQ_NT128
+#define ATTN_DQ_NT128 1
+#endif
+#ifndef ATTN_DQ_OCC128
+#define ATTN_DQ_OCC128 1
+#endif
+#ifndef ATTN_DKDV_OCC128
+#define ATTN_DKDV_OCC128 1
+#endif
 template <int D> struct Tiles;
-template <> struct Tiles<64> { static constexpr int FWD_NT = 2, DQ_NT = 2, DKDV_NTJ = 1; };
-template <> struct Tiles<128> { static constexpr int FWD_NT = 1, DQ_NT = 1, DKDV_NTJ = 1; };
+template <> struct Tiles<64> {
+  static constexpr int FWD_NT = ATTN_FWD_NT64, FWD_OCC = ATTN_FWD_OCC64;
+  static constexpr int DQ_NT = ATTN_DQ_NT64, DQ_OCC = ATTN_DQ_OCC64;
+  static constexpr int DKDV_NTJ = 1, DKDV_OCC = ATTN_DKDV_OCC64;
+};
+template <> struct Tiles<128> {
+  static constexpr int FWD_NT = ATTN_FWD_NT128, FWD_OCC = ATTN_FWD_OCC128;
+  static constexpr int DQ_NT = ATTN_DQ_NT128, DQ_OCC = ATTN_DQ_OCC128;
+  static constexpr int DKDV_NTJ = 1, DKDV_OCC = ATTN_DKDV_OCC128;
+};
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -689,7 +797,7 @@ hipError_t fwd_d(const Problem& pr, const void* q, const void* k, const void* v,
   constexpr int NT = Tiles<D>::FWD_NT;
   FwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, pr.seqlens,
             pr.B, pr.S, pr.Hq, pr.Hkv, cdiv(pr.S, 128 * NT), pr.scale};
-  return launch((const void*)&fwd_kernel<D, NT>, (int64_t)a.nqb * pr.B * pr.Hq, a, stream);
+  return launch((const void*)&fwd_kernel<D, NT, Tiles<D>::FWD_OCC>, (int64_t)a.nqb * pr.B * pr.Hq, a, stream);
 }
 
 template <int D>
@@ -707,7 +815,7 @@ hipError_t dkdv_d(const Problem& pr, const void* q, const void* k, const void* v
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             nullptr, (bf16*)dk, (bf16*)dv, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
             cdiv(pr.S, 128 * NTJ), pr.scale};
-  return launch((const void*)&bwd_dkdv_kernel<D, NTJ>, (int64_t)a.nblk * pr.B * pr.Hkv, a, stream);
+  return launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC>, (int64_t)a.nblk * pr.B * pr.Hkv, a, stream);
 }
 
 template <int D>
@@ -717,7 +825,7 @@ hipError_t dq_d(const Problem& pr, const void* q, const void* k, const void* v, 
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             (bf16*)dq, nullptr, nullptr, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
             cdiv(pr.S, 128 * NT), pr.scale};
-  return launch((const void*)&bwd_dq_kernel<D, NT>, (int64_t)a.nblk * pr.B * pr.Hq, a, stream);
+  return launch((const void*)&bwd_dq_kernel<D, NT, Tiles<D>::DQ_OCC>, (int64_t)a.nblk * pr.B * pr.Hq, a, stream);
 }
 
 }  // namespace
