@@ -48,6 +48,13 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wait for every outstanding vector-memory load (s_waitcnt vmcnt(0); expcnt and
+// lgkmcnt left alone). Issued once after the register-resident operand loads so
+// that no load is still pending on any path into a main loop; otherwise the
+// compiler keeps a conservative vmcnt wait inside the loop that also drains
+// the next tile's prefetch every iteration.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Max / sum of x over lanes l and l ^ 32 (v_permlane32_swap: no LDS round trip).
 __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -123,11 +130,13 @@ __device__ __forceinline__ void decode_qblock(int bid, int nqb, int B, int Hq, i
 }
 
 // Key-block tiles (dK/dV): grid = nkb * B * Hkv. A key block's work grows with
-// the number of query rows below it, so the first half of the dispatch order
-// walks key blocks 0, 1, ... (longest first) and the second half walks them
-// from the far end, so that when two workgroups share a CU, a long block tends
-// to pair with a short one. kv groups are pinned to XCDs as above.
-__device__ __forceinline__ void decode_kblock(int bid, int nkb, int B, int Hkv, int& kb, int& b, int& hkv) {
+// the number of query rows below it, so blocks are dispatched longest first
+// (key block 0 first). With `pair_ends`, the second half of the dispatch order
+// walks the key blocks from the far end instead, so that when two workgroups
+// share a CU from the start, a long block tends to pair with a short one. kv
+// groups are pinned to XCDs as for query blocks.
+__device__ __forceinline__ void decode_kblock(int bid, int nkb, int B, int Hkv, bool pair_ends, int& kb, int& b,
+                                              int& hkv) {
   const int units = B * Hkv;
   int unit, ks;
   if ((units & 7) == 0) {
@@ -140,7 +149,7 @@ __device__ __forceinline__ void decode_kblock(int bid, int nkb, int B, int Hkv, 
     unit = bid - ks * units;
   }
   const int half = (nkb + 1) >> 1;
-  kb = ks < half ? ks : nkb - 1 - (ks - half);
+  kb = (!pair_ends || ks < half) ? ks : nkb - 1 - (ks - half);
   b = unit / Hkv;
   hkv = unit - b * Hkv;
 }

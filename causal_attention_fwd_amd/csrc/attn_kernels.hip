@@ -66,6 +66,29 @@ struct BwdArgs {
 
 constexpr int kThreads = 256;  // four waves, one per SIMD
 
+#ifdef ATTN_TRACE
+// Profiling builds only: per-workgroup (hardware id, XCC id, start, end)
+// timestamps of the last launch of each kernel kind, read back by the host.
+__device__ unsigned long long g_trace[4][65536][4];
+#define ATTN_TRACE_BEGIN()                                    \
+  unsigned long long trace_t0 = __builtin_amdgcn_s_memrealtime();
+#define ATTN_TRACE_END(kind)                                                                        \
+  if (threadIdx.x == 0 && blockIdx.x < 65536) {                                                     \
+    g_trace[kind][blockIdx.x][0] = __builtin_amdgcn_s_getreg(0xF804);                             \
+    g_trace[kind][blockIdx.x][1] = __builtin_amdgcn_s_getreg(0xF814);                             \
+    g_trace[kind][blockIdx.x][2] = trace_t0;                                                        \
+    g_trace[kind][blockIdx.x][3] = __builtin_amdgcn_s_memrealtime();                              \
+  }
+extern "C" void* attn_trace_buffer() {
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_trace)) != hipSuccess) return nullptr;
+  return p;
+}
+#else
+#define ATTN_TRACE_BEGIN()
+#define ATTN_TRACE_END(kind)
+#endif
+
 // Cooperative loader of an R x D bf16 tile (rows of a [*, S, H, D] tensor) into
 // registers, then into a row-major LDS tile with stride D + 8 elements. Rows at
 // or beyond `limit` are zero-filled so padding can never inject NaN/Inf into a
@@ -77,10 +100,11 @@ struct TileLoader {
   static_assert(kChunks % kThreads == 0, "tile must split evenly over the workgroup");
   uint4 reg[kPerThread];
 
-  __device__ __forceinline__ void load(const bf16* base, int64_t row_stride, int row0, int limit) {
+  __device__ __forceinline__ void load(const bf16* base, int64_t row_stride, int row0, int limit,
+                                      int tid = threadIdx.x) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int id = threadIdx.x + i * kThreads;
+      const int id = tid + i * kThreads;
       const int row = id / (D / 8);
       const int col = (id % (D / 8)) * 8;
       const int r = row0 + row;
@@ -91,10 +115,10 @@ struct TileLoader {
       }
     }
   }
-  __device__ __forceinline__ void store(bf16* tile) const {
+  __device__ __forceinline__ void store(bf16* tile, int tid = threadIdx.x) const {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int id = threadIdx.x + i * kThreads;
+      const int id = tid + i * kThreads;
       const int row = id / (D / 8);
       const int col = (id % (D / 8)) * 8;
       *reinterpret_cast<uint4*>(tile + row * (D + 8) + col) = reg[i];
@@ -216,6 +240,7 @@ void fwd_kernel(FwdArgs a) {
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
+  ATTN_TRACE_BEGIN();
   int qb, b, h;
   decode_qblock(blockIdx.x, a.nqb, a.B, a.Hq, a.Hkv, qb, b, h);
   const int S = a.S;
@@ -248,6 +273,7 @@ void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.oacc[dt][t] = zero16();
   }
+  wait_vmem();
 
   TileLoader<BN, D> kl, vl;
   if (ntiles > 0) {
@@ -304,6 +330,7 @@ void fwd_kernel(FwdArgs a) {
       if (g == 0) LSEb[i] = valid ? (st.mu[t] * c + __log2f(lt)) * kLn2 : kNegInf;
     }
   }
+  ATTN_TRACE_END(0);
 }
 
 // ----------------------------------------------------------------------------
@@ -425,23 +452,31 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
     }
 }
 
-template <int D, int NTJ, int OCC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+// GROUPS = 1: four waves. GROUPS = 2: eight waves in two groups of four that
+// own the same key rows and split the (head, query tile) sequence by parity;
+// their partial dK/dV are summed through LDS at the end. With two groups each
+// SIMD keeps two waves busy for the whole block, however long it is.
+template <int D, int NTJ, int OCC, int GROUPS>
+__global__ __launch_bounds__(kThreads * GROUPS) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BMQ = 64;
   constexpr int BN = 4 * 32 * NTJ;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BMQ * (D + 8)];  // [buf][Q, dO]
-  __shared__ __attribute__((aligned(16))) float sstat[2][2][BMQ];         // [buf][LSE*log2e, D]
+  constexpr int TILE = BMQ * (D + 8);
+  __shared__ __attribute__((aligned(16))) bf16 smem[GROUPS][2][2][TILE];  // [group][buf][Q, dO]
+  __shared__ __attribute__((aligned(16))) float sstat[GROUPS][2][2][BMQ];  // [group][buf][LSE*log2e, D]
 
+  ATTN_TRACE_BEGIN();
+  const int grp = threadIdx.x >> 8;
+  const int gtid = threadIdx.x & (kThreads - 1);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = gtid >> 6;
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
   int kb, b, hkv;
-  decode_kblock(blockIdx.x, a.nblk, a.B, a.Hkv, kb, b, hkv);
+  decode_kblock(blockIdx.x, a.nblk, a.B, a.Hkv, GROUPS == 1, kb, b, hkv);
   const int S = a.S;
   const int L = valid_len(a.seqlens, b, S);
   const int G = a.Hq / a.Hkv;
@@ -470,68 +505,105 @@ void bwd_dkdv_kernel(BwdArgs a) {
       st.dv[ct][t] = zero16();
     }
   }
+  wait_vmem();
 
   const int qt0 = j0 / BMQ;
   const int nq = (j0 < L) ? (L - 1) / BMQ - qt0 + 1 : 0;  // query tiles per head
-  const int iters = nq * G;
+  const int iters = nq * G;                               // (head, query tile) pairs
+  const int trips = (iters + GROUPS - 1) / GROUPS;        // this group does it = trip*GROUPS + grp
 
   TileLoader<BMQ, D> ql, dol;
-  float st_reg = 0.f;  // threads 0..63 carry LSE*log2e, 64..127 carry D
+  float st_reg = 0.f;  // threads 0..63 of a group carry LSE, 64..127 carry D
   auto load_tile = [&](int it) {
     const int hh = it / nq;
     const int qt = qt0 + (it - hh * nq);
     const int h = hkv * G + hh;
     const bf16* Qb = a.q + ((int64_t)b * S * a.Hq + h) * D;
     const bf16* dOb = a.d_o + ((int64_t)b * S * a.Hq + h) * D;
-    ql.load(Qb, qs, qt * BMQ, L);
-    dol.load(dOb, qs, qt * BMQ, L);
-    const int tid = threadIdx.x;
-    if (tid < 2 * BMQ) {
-      const int i = qt * BMQ + (tid & (BMQ - 1));
-      const int64_t so = ((int64_t)b * a.Hq + h) * S + i;
+    ql.load(Qb, qs, qt * BMQ, L, gtid);
+    dol.load(dOb, qs, qt * BMQ, L, gtid);
+    if (gtid < 2 * BMQ) {
+      // raw value only: any arithmetic on it here would make the compiler wait
+      // for this load (and the tile prefetch above) before the tile's compute
+      const int i = qt * BMQ + (gtid & (BMQ - 1));
+      const float* src = gtid < BMQ ? a.lse : a.delta;
       st_reg = 0.f;
-      if (i < L) st_reg = tid < BMQ ? a.lse[so] * kLog2e : a.delta[so];
+      if (i < L) st_reg = src[((int64_t)b * a.Hq + h) * S + i];
     }
   };
   auto store_tile = [&](int buf) {
-    ql.store(smem[buf][0]);
-    dol.store(smem[buf][1]);
-    const int tid = threadIdx.x;
-    if (tid < 2 * BMQ) sstat[buf][tid / BMQ][tid & (BMQ - 1)] = st_reg;
+    ql.store(smem[grp][buf][0], gtid);
+    dol.store(smem[grp][buf][1], gtid);
+    if (gtid < 2 * BMQ) sstat[grp][buf][gtid / BMQ][gtid & (BMQ - 1)] = gtid < BMQ ? st_reg * kLog2e : st_reg;
   };
 
-  if (iters > 0) {
-    load_tile(0);
+  if (grp < iters) {
+    load_tile(grp);
     store_tile(0);
   }
   __syncthreads();
 
-  for (int it = 0; it < iters; ++it) {
-    const int buf = it & 1;
-    const bool more = it + 1 < iters;
-    if (more) load_tile(it + 1);
-    const int hh = it / nq;
-    const int qt = qt0 + (it - hh * nq);
-    const int i0 = qt * BMQ;
-    // skip when every query row of the tile is above this wave's key rows, or the
-    // wave's keys are all padding
-    if (i0 + BMQ - 1 >= jw && jw < L) {
-      if ((i0 < jw + 32 * NTJ - 1) || (i0 + BMQ > L) || (jw + 32 * NTJ > L)) {
-        int lo[NTJ], hi[NTJ];
+  for (int trip = 0; trip < trips; ++trip) {
+    const int it = trip * GROUPS + grp;
+    const int buf = trip & 1;
+    const bool more = it + GROUPS < iters;
+    if (more) load_tile(it + GROUPS);
+    if (it < iters) {
+      const int hh = it / nq;
+      const int qt = qt0 + (it - hh * nq);
+      const int i0 = qt * BMQ;
+      // skip when every query row of the tile is above this wave's key rows, or
+      // the wave's keys are all padding
+      if (i0 + BMQ - 1 >= jw && jw < L) {
+        const bf16* Qs = smem[grp][buf][0];
+        const bf16* dOs = smem[grp][buf][1];
+        if ((i0 < jw + 32 * NTJ - 1) || (i0 + BMQ > L) || (jw + 32 * NTJ > L)) {
+          int lo[NTJ], hi[NTJ];
 #pragma unroll
-        for (int t = 0; t < NTJ; ++t) {
-          const int j = jw + t * 32 + l32;
-          lo[t] = j - i0 - g * 4;                              // i >= j
-          hi[t] = (j < L) ? L - 1 - i0 - g * 4 : -1;           // i < L, and no rows when j >= L
+          for (int t = 0; t < NTJ; ++t) {
+            const int j = jw + t * 32 + l32;
+            lo[t] = j - i0 - g * 4;                     // i >= j
+            hi[t] = (j < L) ? L - 1 - i0 - g * 4 : -1;  // i < L, and no rows when j >= L
+          }
+          dkdv_tile<D, NTJ, true>(st, Qs, dOs, sstat[grp][buf][0], sstat[grp][buf][1], lane, c, lo, hi);
+        } else {
+          const int lo[NTJ] = {}, hi[NTJ] = {};
+          dkdv_tile<D, NTJ, false>(st, Qs, dOs, sstat[grp][buf][0], sstat[grp][buf][1], lane, c, lo, hi);
         }
-        dkdv_tile<D, NTJ, true>(st, smem[buf][0], smem[buf][1], sstat[buf][0], sstat[buf][1], lane, c, lo, hi);
-      } else {
-        const int lo[NTJ] = {}, hi[NTJ] = {};
-        dkdv_tile<D, NTJ, false>(st, smem[buf][0], smem[buf][1], sstat[buf][0], sstat[buf][1], lane, c, lo, hi);
       }
     }
     if (more) store_tile(buf ^ 1);
     __syncthreads();
+  }
+
+  if constexpr (GROUPS == 2) {
+    // group 1 hands its partial sums to group 0 through LDS (the tile buffers
+    // are free after the loop's last barrier): [wave][register][lane] floats
+    constexpr int NREG = 2 * DT * NTJ * 16;
+    static_assert(4 * NREG * 64 * sizeof(float) <= sizeof(smem), "reduction buffer");
+    float* red = reinterpret_cast<float*>(&smem[0][0][0][0]) + wave * NREG * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int ct = 0; ct < DT; ++ct)
+#pragma unroll
+        for (int t = 0; t < NTJ; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            red[(((ct * NTJ + t) * 2 + 0) * 16 + r) * 64] = st.dk[ct][t][r];
+            red[(((ct * NTJ + t) * 2 + 1) * 16 + r) * 64] = st.dv[ct][t][r];
+          }
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int ct = 0; ct < DT; ++ct)
+#pragma unroll
+      for (int t = 0; t < NTJ; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          st.dk[ct][t][r] += red[(((ct * NTJ + t) * 2 + 0) * 16 + r) * 64];
+          st.dv[ct][t][r] += red[(((ct * NTJ + t) * 2 + 1) * 16 + r) * 64];
+        }
   }
 
   // Epilogue: dK = scale * dK^T, dV = dV^T transposed back; lane owns key row j.
@@ -558,6 +630,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
     }
   }
+  ATTN_TRACE_END(2);
 }
 
 // ----------------------------------------------------------------------------
@@ -638,6 +711,7 @@ void bwd_dq_kernel(BwdArgs a) {
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
+  ATTN_TRACE_BEGIN();
   int qb, b, h;
   decode_qblock(blockIdx.x, a.nblk, a.B, a.Hq, a.Hkv, qb, b, h);
   const int S = a.S;
@@ -675,6 +749,7 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.acc[dt][t] = zero16();
   }
+  wait_vmem();
 
   TileLoader<BN, D> kl, vl;
   if (ntiles > 0) {
@@ -730,6 +805,7 @@ void bwd_dq_kernel(BwdArgs a) {
         }
     }
   }
+  ATTN_TRACE_END(3);
 }
 
 // ----------------------------------------------------------------------------
@@ -755,6 +831,9 @@ namespace {
 #ifndef ATTN_DKDV_OCC64
 #define ATTN_DKDV_OCC64 2
 #endif
+#ifndef ATTN_DKDV_GROUPS64
+#define ATTN_DKDV_GROUPS64 2
+#endif
 #ifndef ATTN_FWD_NT128
 #define ATTN_FWD_NT128 1
 #endif
@@ -774,21 +853,21 @@ template <int D> struct Tiles;
 template <> struct Tiles<64> {
   static constexpr int FWD_NT = ATTN_FWD_NT64, FWD_OCC = ATTN_FWD_OCC64;
   static constexpr int DQ_NT = ATTN_DQ_NT64, DQ_OCC = ATTN_DQ_OCC64;
-  static constexpr int DKDV_NTJ = 1, DKDV_OCC = ATTN_DKDV_OCC64;
+  static constexpr int DKDV_NTJ = 1, DKDV_OCC = ATTN_DKDV_OCC64, DKDV_GROUPS = ATTN_DKDV_GROUPS64;
 };
 template <> struct Tiles<128> {
   static constexpr int FWD_NT = ATTN_FWD_NT128, FWD_OCC = ATTN_FWD_OCC128;
   static constexpr int DQ_NT = ATTN_DQ_NT128, DQ_OCC = ATTN_DQ_OCC128;
-  static constexpr int DKDV_NTJ = 1, DKDV_OCC = ATTN_DKDV_OCC128;
+  static constexpr int DKDV_NTJ = 1, DKDV_OCC = ATTN_DKDV_OCC128, DKDV_GROUPS = 1;
 };
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 template <typename Args>
-hipError_t launch(const void* fn, int64_t grid, Args args, hipStream_t stream) {
+hipError_t launch(const void* fn, int64_t grid, Args args, hipStream_t stream, int threads = kThreads) {
   if (grid <= 0) return hipSuccess;
   void* kargs[] = {&args};
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(threads), kargs, 0, stream);
 }
 
 template <int D>
@@ -815,7 +894,9 @@ hipError_t dkdv_d(const Problem& pr, const void* q, const void* k, const void* v
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             nullptr, (bf16*)dk, (bf16*)dv, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
             cdiv(pr.S, 128 * NTJ), pr.scale};
-  return launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC>, (int64_t)a.nblk * pr.B * pr.Hkv, a, stream);
+  constexpr int GR = Tiles<D>::DKDV_GROUPS;
+  return launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR>, (int64_t)a.nblk * pr.B * pr.Hkv, a,
+                stream, kThreads * GR);
 }
 
 template <int D>
