@@ -15,6 +15,7 @@ forward, 2.5x that backward (five products including the QK^T recompute).
 Other modes (measurement tooling, used under rocprofv3):
     --copy-calibration       run a plain device copy of known size (counter scale)
     --pmc-summary DIR ...    turn rocprofv3 --pmc outputs into profiles/*_pmc.txt
+    --trace-summary DIR      turn a rocprofv3 --kernel-trace --stats run into profiles/*_trace.txt
 """
 from __future__ import annotations
 
@@ -120,6 +121,43 @@ def pmc_summary(args):
             out.write(f"scale_fetch: {f_scale:.4f}\nscale_write: {w_scale:.4f}\n")
             out.write(f"traffic_bytes_per_dispatch: {traffic:.0f}\n")
         log(f"wrote {path}: {traffic / 1e6:.1f} MB per dispatch")
+
+
+def trace_summary(args):
+    """profiles/<kernel>_<workload>_trace.txt from a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    from attn_workloads import WORKLOADS, algorithmic_flops, workload_inputs
+    w = WORKLOADS[args.workload]
+    seqlens = workload_inputs(w).seqlens if w.padded else None
+    fl = algorithmic_flops(w, seqlens)
+    share = {"fwd_kernel": fl["fwd"], "bwd_dkdv_kernel": fl["bwd_dkdv"], "bwd_dq_kernel": fl["bwd_dq"]}
+    B, S, Hq, d = w.B, w.S, w.Hq, w.d
+    pre_bytes = 2.0 * B * S * Hq * d * 2 + B * Hq * S * 4.0
+    files = glob.glob(os.path.join(args.trace_summary, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no kernel_stats.csv under {args.trace_summary}")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for row in csv.DictReader(open(files[0])):
+        kname = next((k for k in KERNEL_NAMES.values() if k in row["Name"]), None)
+        if kname is None:
+            continue
+        avg_us = float(row["AverageNs"]) / 1e3
+        path = os.path.join(ROOT, "profiles", f"{kname}_{w.name}_trace.txt")
+        with open(path, "w") as out:
+            out.write(f"# rocprofv3 kernel-trace summary: {kname} on workload {w.name} {w.describe()}\n")
+            out.write(f"# command: {args.pmc_command}\n")
+            out.write(f"kernel: {row['Name']}\n")
+            out.write(f"kernel_source_sha256_16: {kernel_source_sha()}\n")
+            out.write(f"calls: {row['Calls']}\n")
+            out.write(f"average_us: {avg_us:.2f}\nmin_us: {float(row['MinNs']) / 1e3:.2f}\n"
+                      f"max_us: {float(row['MaxNs']) / 1e3:.2f}\n")
+            if kname in share:
+                out.write(f"algorithmic_gflop_per_launch: {share[kname] / 1e9:.3f}\n")
+                out.write(f"achieved_tflops_at_average: {share[kname] / (avg_us * 1e-6) / 1e12:.1f}\n")
+            else:
+                out.write(f"algorithmic_bytes_per_launch: {pre_bytes:.0f}\n")
+                out.write(f"achieved_gbs_at_average: {pre_bytes / (avg_us * 1e-6) / 1e9:.1f}\n")
+        log(f"wrote {path}: {avg_us:.1f} us")
 
 
 # ----------------------------------------------------------------------------- copy calibration
@@ -272,7 +310,8 @@ def main():
     ap.add_argument("--copy-bytes", type=float, default=1 << 30)
     ap.add_argument("--copy-kernel", default="copy")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
-    ap.add_argument("--pmc-command", default="")
+    ap.add_argument("--pmc-command", default="", help="command line recorded in the written summaries")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -281,6 +320,8 @@ def main():
         sys.exit(2)
     if args.pmc_summary:
         pmc_summary(args)
+    elif args.trace_summary:
+        trace_summary(args)
     elif args.copy_calibration:
         copy_calibration(args)
     else:

@@ -46,7 +46,7 @@ struct PreArgs {
   float* delta;
   const int32_t* seqlens;
   int B, S, Hq;
-  int64_t rows;  // B * S * Hq
+  int64_t rows;  // B * Hq * S
 };
 
 struct BwdArgs {
@@ -334,31 +334,31 @@ void fwd_kernel(FwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Preprocess: D = rowsum(dO * O). D/8 lanes per row, 16 bytes per lane.
+// Preprocess: D = rowsum(dO * O). D/8 lanes per row, 16 bytes per lane. Rows are
+// walked in D's own [B, Hq, S] order so each wave writes a contiguous run of D
+// (the O/dO rows it reads are whole 128/256-byte segments either way).
 // ----------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
   constexpr int LPR = D / 8;  // lanes per row
-  const int64_t row = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
+  const int64_t r = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;  // index into D
   const int part = threadIdx.x % LPR;
   float acc = 0.f;
-  if (row < a.rows) {
-    const bf16x8 o = *reinterpret_cast<const bf16x8*>(a.o + row * D + part * 8);
-    const bf16x8 d = *reinterpret_cast<const bf16x8*>(a.d_o + row * D + part * 8);
+  int s = 0, b = 0;
+  if (r < a.rows) {
+    s = (int)(r % a.S);
+    const int64_t bh = r / a.S;
+    const int h = (int)(bh % a.Hq);
+    b = (int)(bh / a.Hq);
+    const int64_t off = (((int64_t)b * a.S + s) * a.Hq + h) * D + part * 8;
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(a.o + off);
+    const bf16x8 d = *reinterpret_cast<const bf16x8*>(a.d_o + off);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)o[e] * (float)d[e];
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < a.rows && part == 0) {
-    // row = (b * S + s) * Hq + h
-    const int h = (int)(row % a.Hq);
-    const int64_t bs = row / a.Hq;
-    const int s = (int)(bs % a.S);
-    const int b = (int)(bs / a.S);
-    const int L = valid_len(a.seqlens, b, a.S);
-    a.delta[((int64_t)b * a.Hq + h) * a.S + s] = s < L ? acc : 0.f;
-  }
+  if (r < a.rows && part == 0) a.delta[r] = s < valid_len(a.seqlens, b, a.S) ? acc : 0.f;
 }
 
 // ----------------------------------------------------------------------------
