@@ -20,6 +20,9 @@ attn_status check_shape(const attn_shape* s, attn::Problem* pr) {
   if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (s->causal != 1) return ATTN_ERR_UNSUPPORTED;
   if (s->seqlens && (reinterpret_cast<uintptr_t>(s->seqlens) & 3u) != 0) return ATTN_ERR_MISALIGNED;
+  // tiles are fetched through buffer resources with 32-bit byte offsets that
+  // span up to 128 rows of one sequence: 128 * heads * head_dim * 2 < 2^31
+  if ((int64_t)s->heads_q * s->head_dim > (int64_t)1 << 22) return ATTN_ERR_UNSUPPORTED;
   pr->B = s->batch;
   pr->S = s->seqlen;
   pr->Hq = s->heads_q;

@@ -65,26 +65,129 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Row fragment from an LDS tile stored row-major with `stride` elements per row:
-// lane l gets tile[row0 + l%32][col0 + (l/32)*8 .. +7] (one 16-byte read).
-__device__ __forceinline__ bf16x8 frag_row(const bf16* tile, int stride, int row0, int col0, int lane) {
-  return *reinterpret_cast<const bf16x8*>(tile + (row0 + (lane & 31)) * stride + col0 + ((lane >> 5) << 3));
+// LDS tile layout. Rows of D bf16 are cut into 16-byte chunks (CH = D/8 per
+// row) and grouped by 8 rows into blocks of D*16 bytes plus 128 bytes of
+// padding. Inside a block the chunks are stored chunk-major: chunk c of the
+// block's row x (0..7) sits in 16-byte slot c*8 + (x ^ h(c)), h(c) = 4*((c/2)%2).
+//  * Every 64 consecutive slots (1 KB) are 8 rows x 8 chunks, i.e. 8 row
+//    segments of 128 contiguous bytes in global memory: one direct-to-LDS wave
+//    load (lane i -> slot i) per KB, coalesced.
+//  * Row fragments (16 consecutive rows, one chunk each, per 16 lanes): 8 rows
+//    fill 128 contiguous bytes and the next 8 start one block later, which the
+//    padding shifts by 128 bytes mod 256: all 64 banks once.
+//  * Transposed fragments (4 rows x 2 chunks per 16 lanes; the next 16 lanes
+//    two chunks further): the two halves use row slots 0-3 and 4-7 thanks to
+//    h, so 32 lanes cover all 64 banks once.
+//  * For row offsets that are multiples of 8 and column offsets that are
+//    multiples of 16 an address is a lane term (one of two, picked by the
+//    column offset) plus a constant, so the unrolled loops need few address
+//    registers.
+template <int D>
+struct TileLayout {
+  static constexpr int kBlockElems = D * 8 + 64;  // 8 rows + 128 bytes of padding
+  template <int R>
+  static constexpr int elems() {
+    static_assert(R % 8 == 0, "tiles hold whole 8-row blocks");
+    return R / 8 * kBlockElems;
+  }
+};
+
+// Row fragment: lane l gets tile[row0 + l%32][col0 + (l/32)*8 .. +7] (one
+// 16-byte read). row0 % 8 == 0, col0 % 16 == 0.
+template <int D>
+__device__ __forceinline__ bf16x8 frag_row(const bf16* tile, int row0, int col0, int lane) {
+  constexpr int BE = TileLayout<D>::kBlockElems;
+  const int h = ((col0 >> 4) & 1) << 2;
+  const int c = (col0 >> 3) + (lane >> 5);
+  const int off = ((row0 >> 3) + ((lane & 31) >> 3)) * BE + (c * 8 + ((lane & 7) ^ h)) * 8;
+  return *reinterpret_cast<const bf16x8*>(tile + off);
 }
 
 // Transposed fragment: lane l gets tile[row0 + (e/4)*8 + (l/32)*4 + e%4][col0 + l%32]
 // for e = 0..7, i.e. the k order of a C tile's registers. Two ds_read_b64_tr_b16:
-// in each 16-lane group, lane t's value e comes from the 8-byte chunk addressed by
-// lane 4e + t/4, element t%4; each lane therefore addresses row (l/32)*4 + (l%16)/4
-// and columns ((l/16)%2)*16 + (l%4)*4 .. +3.
-__device__ __forceinline__ bf16x8 frag_tr(const bf16* tile, int stride, int row0, int col0, int lane) {
+// in each 16-lane group, lane t's value e comes from the 8-byte piece addressed
+// by lane 4e + t/4, element t%4; each lane therefore addresses row
+// (l/32)*4 + (l%16)/4 (and 8 more) and columns ((l/16)%2)*16 + (l%4)*4 .. +3.
+// row0 % 8 == 0, col0 % 16 == 0.
+template <int D>
+__device__ __forceinline__ bf16x8 frag_tr(const bf16* tile, int row0, int col0, int lane) {
+  constexpr int BE = TileLayout<D>::kBlockElems;
   const int s = lane & 15;
-  const int r = row0 + ((lane >> 5) << 2) + (s >> 2);
-  const int c = col0 + (((lane >> 4) & 1) << 4) + ((s & 3) << 2);
-  const bf16* p = tile + r * stride + c;
+  const int b4 = (lane >> 4) & 1;
+  const int c = (col0 >> 3) + 2 * b4 + ((s & 3) >> 1);   // chunk
+  const int h = (((col0 >> 4) + b4) & 1) << 2;            // h(c): c/2 = col0/16 + b4
+  const int x = (((lane >> 5) << 2) + (s >> 2)) ^ h;      // row within the block, swizzled
+  const bf16* p = tile + (row0 >> 3) * BE + (c * 8 + x) * 8 + (s & 1) * 4;
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * stride));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + BE));
   s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS load of rows [row0, row0 + R) of one (sequence, head)
+// slice of a [B, S, H, D] tensor (row_stride elements between rows) into a
+// tile of the layout above, with buffer_load_dwordx4 ... lds: each wave
+// instruction fills one KB of slots, lane i landing in slot i, so lane i
+// fetches the chunk the layout puts there. The buffer resource starts at row0
+// and ends after the last row below L, so rows at or past L arrive as zeros
+// (the hardware range check) and every offset stays below R * row_stride * 2
+// bytes. No VGPRs hold the data; completion is tracked by vmcnt (wait_vmem)
+// and made visible to the other waves by a barrier.
+template <int R, int D, int NWAVES>
+__device__ __forceinline__ void tile_load_lds(const bf16* base, int64_t row_stride, int row0, int L, bf16* tile,
+                                              int wave, int lane) {
+  constexpr int KB_PER_BLOCK = D / 64;           // 1 KB pieces per 8-row block
+  constexpr int NKB = R / 8 * KB_PER_BLOCK;      // wave instructions per tile
+  static_assert(NKB % NWAVES == 0, "tile must split evenly over the waves");
+  const int rows = min(L - row0, R);
+  const int bytes = rows > 0 ? (int)(((int64_t)(rows - 1) * row_stride + D) * 2) : 0;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base + (int64_t)row0 * row_stride), (short)0, bytes,
+                                        0x00020000);
+#pragma unroll
+  for (int j = 0; j < NKB / NWAVES; ++j) {
+    const int kb = wave * (NKB / NWAVES) + j;
+    const int blk = kb / KB_PER_BLOCK;
+    const int c = (kb % KB_PER_BLOCK) * 8 + (lane >> 3);
+    const int row = blk * 8 + ((lane & 7) ^ (((c >> 1) & 1) << 2));
+    const int voff = (int)(row * row_stride + c * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + blk * TileLayout<D>::kBlockElems +
+                                                               (kb % KB_PER_BLOCK) * 512),
+                                             16, voff, 0, 0, 0);
+  }
+}
+
+// Two-stage pipeline over n tiles held in two LDS buffers (distinct arrays, so
+// the compiler can tell the buffer being filled from the one being read and
+// needs no vmcnt wait before the reads): the fetch of tile t+1 is in flight
+// while tile t is computed. fetch(t, buf) issues the loads, land(t, buf) runs
+// once they have arrived (for data staged through registers), compute(t, buf)
+// reads the tile; the barrier after each compute publishes the next tile and
+// frees the one just read.
+template <class Buf, class Fetch, class Land, class Compute>
+__device__ __forceinline__ void tile_pipeline(int n, const Buf& b0, const Buf& b1, Fetch&& fetch, Land&& land,
+                                              Compute&& compute) {
+  if (n > 0) fetch(0, b0);
+  wait_vmem();
+  if (n > 0) land(0, b0);
+  __syncthreads();
+  for (int t = 0; t < n; t += 2) {
+    const bool more1 = t + 1 < n;
+    if (more1) fetch(t + 1, b1);
+    compute(t, b0);
+    wait_vmem();
+    if (more1) land(t + 1, b1);
+    __syncthreads();
+    if (!more1) break;
+    const bool more2 = t + 2 < n;
+    if (more2) fetch(t + 2, b0);
+    compute(t + 1, b1);
+    wait_vmem();
+    if (more2) land(t + 2, b0);
+    __syncthreads();
+  }
 }
 
 typedef float f32x2v __attribute__((ext_vector_type(2)));

@@ -89,41 +89,12 @@ extern "C" void* attn_trace_buffer() {
 #define ATTN_TRACE_END(kind)
 #endif
 
-// Cooperative loader of an R x D bf16 tile (rows of a [*, S, H, D] tensor) into
-// registers, then into a row-major LDS tile with stride D + 8 elements. Rows at
-// or beyond `limit` are zero-filled so padding can never inject NaN/Inf into a
-// product.
-template <int R, int D>
-struct TileLoader {
-  static constexpr int kChunks = R * D / 8;          // 16-byte chunks
-  static constexpr int kPerThread = kChunks / kThreads;
-  static_assert(kChunks % kThreads == 0, "tile must split evenly over the workgroup");
-  uint4 reg[kPerThread];
-
-  __device__ __forceinline__ void load(const bf16* base, int64_t row_stride, int row0, int limit,
-                                      int tid = threadIdx.x) {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int id = tid + i * kThreads;
-      const int row = id / (D / 8);
-      const int col = (id % (D / 8)) * 8;
-      const int r = row0 + row;
-      if (r < limit) {
-        reg[i] = *reinterpret_cast<const uint4*>(base + (int64_t)r * row_stride + col);
-      } else {
-        reg[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(bf16* tile, int tid = threadIdx.x) const {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int id = tid + i * kThreads;
-      const int row = id / (D / 8);
-      const int col = (id % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(tile + row * (D + 8) + col) = reg[i];
-    }
-  }
+// One stage of a K/V (or Q/dO) tile pipeline: two swizzled LDS tiles, and the
+// stage's index for side data kept in indexed arrays.
+struct KVBuf {
+  bf16* k;
+  bf16* v;
+  int idx;
 };
 
 // ----------------------------------------------------------------------------
@@ -151,7 +122,7 @@ struct FwdState {
 template <int D, int NT, bool MASK>
 __device__ __forceinline__ void fwd_tile(FwdState<D, NT>& st, const bf16* Ks, const bf16* Vs, int lane, float c,
                                          const int (&lim)[NT]) {
-  constexpr int KK = D / 16, DT = D / 32, LS = D + 8;
+  constexpr int KK = D / 16, DT = D / 32;
   constexpr float kHeadroom = 8.f;  // log2 of the largest exponent allowed before a rescale
   f32x16 s[2][NT];
 #pragma unroll
@@ -162,7 +133,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, NT>& st, const bf16* Ks, co
   for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const bf16x8 af = frag_row(Ks, LS, mt * 32, kk * 16, lane);
+      const bf16x8 af = frag_row<D>(Ks, mt * 32, kk * 16, lane);
 #pragma unroll
       for (int t = 0; t < NT; ++t) s[mt][t] = mfma32(af, st.qf[t][kk], s[mt][t]);
     }
@@ -220,7 +191,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, NT>& st, const bf16* Ks, co
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const bf16x8 af = frag_tr(Vs, LS, u * 16, dt * 32, lane);
+      const bf16x8 af = frag_tr<D>(Vs, u * 16, dt * 32, lane);
 #pragma unroll
       for (int t = 0; t < NT; ++t) st.oacc[dt][t] = mfma32(af, pb[u][t], st.oacc[dt][t]);
     }
@@ -233,7 +204,8 @@ void fwd_kernel(FwdArgs a) {
   constexpr int BM = 4 * 32 * NT;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * (D + 8)];
+  constexpr int KVT = TileLayout<D>::template elems<BN>();
+  __shared__ __attribute__((aligned(16))) bf16 sK0[KVT], sV0[KVT], sK1[KVT], sV1[KVT];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -275,40 +247,25 @@ void fwd_kernel(FwdArgs a) {
   }
   wait_vmem();
 
-  TileLoader<BN, D> kl, vl;
-  if (ntiles > 0) {
-    kl.load(Kb, ks, 0, L);
-    vl.load(Vb, ks, 0, L);
-    kl.store(smem[0][0]);
-    vl.store(smem[0][1]);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < ntiles;
-    if (more) {
-      kl.load(Kb, ks, (kt + 1) * BN, L);
-      vl.load(Vb, ks, (kt + 1) * BN, L);
-    }
+  const KVBuf b0{sK0, sV0, 0}, b1{sK1, sV1, 1};
+  auto fetch = [&](int kt, const KVBuf& buf) {
+    tile_load_lds<BN, D, 4>(Kb, ks, kt * BN, L, buf.k, wave, lane);
+    tile_load_lds<BN, D, 4>(Vb, ks, kt * BN, L, buf.v, wave, lane);
+  };
+  auto compute = [&](int kt, const KVBuf& buf) {
     const int j0 = kt * BN;
-    if (j0 <= wave_last) {
-      if ((j0 + BN - 1 > qw) || (j0 + BN > L)) {
-        int lim[NT];
+    if (j0 > wave_last) return;
+    if ((j0 + BN - 1 > qw) || (j0 + BN > L)) {
+      int lim[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) lim[t] = min(qw + t * 32 + l32, L - 1) - j0 - g * 4;
-        fwd_tile<D, NT, true>(st, smem[buf][0], smem[buf][1], lane, c, lim);
-      } else {
-        const int lim[NT] = {};
-        fwd_tile<D, NT, false>(st, smem[buf][0], smem[buf][1], lane, c, lim);
-      }
+      for (int t = 0; t < NT; ++t) lim[t] = min(qw + t * 32 + l32, L - 1) - j0 - g * 4;
+      fwd_tile<D, NT, true>(st, buf.k, buf.v, lane, c, lim);
+    } else {
+      const int lim[NT] = {};
+      fwd_tile<D, NT, false>(st, buf.k, buf.v, lane, c, lim);
     }
-    if (more) {
-      kl.store(smem[buf ^ 1][0]);
-      vl.store(smem[buf ^ 1][1]);
-    }
-    __syncthreads();
-  }
+  };
+  tile_pipeline(ntiles, b0, b1, fetch, [](int, const KVBuf&) {}, compute);
 
   // Epilogue: O = acc / l (bf16), LSE = mu*scale + ln l; padded rows 0 / -inf.
 #pragma unroll
@@ -381,7 +338,7 @@ template <int D, int NTJ, bool MASK>
 __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs, const bf16* dOs, const float* lse2,
                                           const float* dl, int lane, float c, const int (&lo)[NTJ],
                                           const int (&hi)[NTJ]) {
-  constexpr int KK = D / 16, DT = D / 32, LS = D + 8;
+  constexpr int KK = D / 16, DT = D / 32;
   const int g = lane >> 5;
   f32x16 s[2][NTJ], dp[2][NTJ];
 #pragma unroll
@@ -395,8 +352,8 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
   for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
-      const bf16x8 aq = frag_row(Qs, LS, m2 * 32, kk * 16, lane);
-      const bf16x8 ad = frag_row(dOs, LS, m2 * 32, kk * 16, lane);
+      const bf16x8 aq = frag_row<D>(Qs, m2 * 32, kk * 16, lane);
+      const bf16x8 ad = frag_row<D>(dOs, m2 * 32, kk * 16, lane);
 #pragma unroll
       for (int t = 0; t < NTJ; ++t) {
         s[m2][t] = mfma32(aq, st.kf[t][kk], s[m2][t]);
@@ -442,8 +399,8 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
   for (int ct = 0; ct < DT; ++ct)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const bf16x8 ado = frag_tr(dOs, LS, u * 16, ct * 32, lane);
-      const bf16x8 aq = frag_tr(Qs, LS, u * 16, ct * 32, lane);
+      const bf16x8 ado = frag_tr<D>(dOs, u * 16, ct * 32, lane);
+      const bf16x8 aq = frag_tr<D>(Qs, u * 16, ct * 32, lane);
 #pragma unroll
       for (int t = 0; t < NTJ; ++t) {
         st.dv[ct][t] = mfma32(ado, pb[u][t], st.dv[ct][t]);
@@ -463,8 +420,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BN = 4 * 32 * NTJ;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
-  constexpr int TILE = BMQ * (D + 8);
-  __shared__ __attribute__((aligned(16))) bf16 smem[GROUPS][2][2][TILE];  // [group][buf][Q, dO]
+  constexpr int TILE = TileLayout<D>::template elems<BMQ>();
+  // [group] tiles; Q and dO of the two pipeline stages live in distinct arrays
+  __shared__ __attribute__((aligned(16))) bf16 sQ0[GROUPS * TILE], sO0[GROUPS * TILE], sQ1[GROUPS * TILE],
+      sO1[GROUPS * TILE];
   __shared__ __attribute__((aligned(16))) float sstat[GROUPS][2][2][BMQ];  // [group][buf][LSE*log2e, D]
 
   ATTN_TRACE_BEGIN();
@@ -512,76 +471,67 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int iters = nq * G;                               // (head, query tile) pairs
   const int trips = (iters + GROUPS - 1) / GROUPS;        // this group does it = trip*GROUPS + grp
 
-  TileLoader<BMQ, D> ql, dol;
   float st_reg = 0.f;  // threads 0..63 of a group carry LSE, 64..127 carry D
-  auto load_tile = [&](int it) {
+  const KVBuf b0{sQ0 + grp * TILE, sO0 + grp * TILE, 0}, b1{sQ1 + grp * TILE, sO1 + grp * TILE, 1};
+  // this group handles (head, query tile) pair it = trip * GROUPS + grp
+  auto fetch = [&](int trip, const KVBuf& buf) {
+    const int it = trip * GROUPS + grp;
+    if (it >= iters) return;
     const int hh = it / nq;
     const int qt = qt0 + (it - hh * nq);
     const int h = hkv * G + hh;
-    const bf16* Qb = a.q + ((int64_t)b * S * a.Hq + h) * D;
-    const bf16* dOb = a.d_o + ((int64_t)b * S * a.Hq + h) * D;
-    ql.load(Qb, qs, qt * BMQ, L, gtid);
-    dol.load(dOb, qs, qt * BMQ, L, gtid);
     if (gtid < 2 * BMQ) {
       // raw value only: any arithmetic on it here would make the compiler wait
-      // for this load (and the tile prefetch above) before the tile's compute
+      // for this load before the tile's compute
       const int i = qt * BMQ + (gtid & (BMQ - 1));
       const float* src = gtid < BMQ ? a.lse : a.delta;
       st_reg = 0.f;
       if (i < L) st_reg = src[((int64_t)b * a.Hq + h) * S + i];
     }
+    const bf16* Qb = a.q + ((int64_t)b * S * a.Hq + h) * D;
+    const bf16* dOb = a.d_o + ((int64_t)b * S * a.Hq + h) * D;
+    tile_load_lds<BMQ, D, 4>(Qb, qs, qt * BMQ, L, buf.k, wave, lane);
+    tile_load_lds<BMQ, D, 4>(dOb, qs, qt * BMQ, L, buf.v, wave, lane);
   };
-  auto store_tile = [&](int buf) {
-    ql.store(smem[grp][buf][0], gtid);
-    dol.store(smem[grp][buf][1], gtid);
-    if (gtid < 2 * BMQ) sstat[grp][buf][gtid / BMQ][gtid & (BMQ - 1)] = gtid < BMQ ? st_reg * kLog2e : st_reg;
+  auto land = [&](int trip, const KVBuf& buf) {
+    if (trip * GROUPS + grp < iters && gtid < 2 * BMQ)
+      sstat[grp][buf.idx][gtid / BMQ][gtid & (BMQ - 1)] = gtid < BMQ ? st_reg * kLog2e : st_reg;
   };
-
-  if (grp < iters) {
-    load_tile(grp);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int trip = 0; trip < trips; ++trip) {
+  auto compute = [&](int trip, const KVBuf& buf) {
     const int it = trip * GROUPS + grp;
-    const int buf = trip & 1;
-    const bool more = it + GROUPS < iters;
-    if (more) load_tile(it + GROUPS);
-    if (it < iters) {
-      const int hh = it / nq;
-      const int qt = qt0 + (it - hh * nq);
-      const int i0 = qt * BMQ;
-      // skip when every query row of the tile is above this wave's key rows, or
-      // the wave's keys are all padding
-      if (i0 + BMQ - 1 >= jw && jw < L) {
-        const bf16* Qs = smem[grp][buf][0];
-        const bf16* dOs = smem[grp][buf][1];
-        if ((i0 < jw + 32 * NTJ - 1) || (i0 + BMQ > L) || (jw + 32 * NTJ > L)) {
-          int lo[NTJ], hi[NTJ];
+    if (it >= iters) return;
+    const int hh = it / nq;
+    const int qt = qt0 + (it - hh * nq);
+    const int i0 = qt * BMQ;
+    // skip when every query row of the tile is above this wave's key rows, or
+    // the wave's keys are all padding
+    if (i0 + BMQ - 1 < jw || jw >= L) return;
+    const float* ls = sstat[grp][buf.idx][0];
+    const float* ds = sstat[grp][buf.idx][1];
+    if ((i0 < jw + 32 * NTJ - 1) || (i0 + BMQ > L) || (jw + 32 * NTJ > L)) {
+      int lo[NTJ], hi[NTJ];
 #pragma unroll
-          for (int t = 0; t < NTJ; ++t) {
-            const int j = jw + t * 32 + l32;
-            lo[t] = j - i0 - g * 4;                     // i >= j
-            hi[t] = (j < L) ? L - 1 - i0 - g * 4 : -1;  // i < L, and no rows when j >= L
-          }
-          dkdv_tile<D, NTJ, true>(st, Qs, dOs, sstat[grp][buf][0], sstat[grp][buf][1], lane, c, lo, hi);
-        } else {
-          const int lo[NTJ] = {}, hi[NTJ] = {};
-          dkdv_tile<D, NTJ, false>(st, Qs, dOs, sstat[grp][buf][0], sstat[grp][buf][1], lane, c, lo, hi);
-        }
+      for (int t = 0; t < NTJ; ++t) {
+        const int j = jw + t * 32 + l32;
+        lo[t] = j - i0 - g * 4;                     // i >= j
+        hi[t] = (j < L) ? L - 1 - i0 - g * 4 : -1;  // i < L, and no rows when j >= L
       }
+      dkdv_tile<D, NTJ, true>(st, buf.k, buf.v, ls, ds, lane, c, lo, hi);
+    } else {
+      const int lo[NTJ] = {}, hi[NTJ] = {};
+      dkdv_tile<D, NTJ, false>(st, buf.k, buf.v, ls, ds, lane, c, lo, hi);
     }
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
-  }
+  };
+  tile_pipeline(trips, b0, b1, fetch, land, compute);
 
   if constexpr (GROUPS == 2) {
     // group 1 hands its partial sums to group 0 through LDS (the tile buffers
-    // are free after the loop's last barrier): [wave][register][lane] floats
+    // are free after the loop's last barrier): wave w writes [register][lane]
+    // floats into the w-th tile array
     constexpr int NREG = 2 * DT * NTJ * 16;
-    static_assert(4 * NREG * 64 * sizeof(float) <= sizeof(smem), "reduction buffer");
-    float* red = reinterpret_cast<float*>(&smem[0][0][0][0]) + wave * NREG * 64 + lane;
+    static_assert(NREG * 64 * sizeof(float) <= sizeof(sQ0), "reduction buffer");
+    bf16* const arr = wave == 0 ? sQ0 : wave == 1 ? sO0 : wave == 2 ? sQ1 : sO1;
+    float* red = reinterpret_cast<float*>(arr) + lane;
     if (grp == 1) {
 #pragma unroll
       for (int ct = 0; ct < DT; ++ct)
@@ -650,7 +600,7 @@ struct DqState {
 template <int D, int NT, bool MASK>
 __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, const bf16* Vs, int lane, float c,
                                         const int (&lim)[NT]) {
-  constexpr int KK = D / 16, DT = D / 32, LS = D + 8;
+  constexpr int KK = D / 16, DT = D / 32;
   f32x16 s[2][NT], dp[2][NT];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -663,8 +613,8 @@ __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, cons
   for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const bf16x8 ak = frag_row(Ks, LS, mt * 32, kk * 16, lane);
-      const bf16x8 av = frag_row(Vs, LS, mt * 32, kk * 16, lane);
+      const bf16x8 ak = frag_row<D>(Ks, mt * 32, kk * 16, lane);
+      const bf16x8 av = frag_row<D>(Vs, mt * 32, kk * 16, lane);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         s[mt][t] = mfma32(ak, st.qf[t][kk], s[mt][t]);
@@ -691,7 +641,7 @@ __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, cons
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const bf16x8 ak = frag_tr(Ks, LS, u * 16, dt * 32, lane);
+      const bf16x8 ak = frag_tr<D>(Ks, u * 16, dt * 32, lane);
 #pragma unroll
       for (int t = 0; t < NT; ++t) st.acc[dt][t] = mfma32(ak, sb[u][t], st.acc[dt][t]);
     }
@@ -704,7 +654,8 @@ void bwd_dq_kernel(BwdArgs a) {
   constexpr int BM = 4 * 32 * NT;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * (D + 8)];
+  constexpr int KVT = TileLayout<D>::template elems<BN>();
+  __shared__ __attribute__((aligned(16))) bf16 sK0[KVT], sV0[KVT], sK1[KVT], sV1[KVT];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -751,43 +702,29 @@ void bwd_dq_kernel(BwdArgs a) {
   }
   wait_vmem();
 
-  TileLoader<BN, D> kl, vl;
-  if (ntiles > 0) {
-    kl.load(Kb, ks, 0, L);
-    vl.load(Vb, ks, 0, L);
-    kl.store(smem[0][0]);
-    vl.store(smem[0][1]);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < ntiles;
-    if (more) {
-      kl.load(Kb, ks, (kt + 1) * BN, L);
-      vl.load(Vb, ks, (kt + 1) * BN, L);
-    }
+  // K/V tiles stream straight into LDS (no staging registers), double-buffered.
+  const KVBuf b0{sK0, sV0, 0}, b1{sK1, sV1, 1};
+  auto fetch = [&](int kt, const KVBuf& buf) {
+    tile_load_lds<BN, D, 4>(Kb, ks, kt * BN, L, buf.k, wave, lane);
+    tile_load_lds<BN, D, 4>(Vb, ks, kt * BN, L, buf.v, wave, lane);
+  };
+  auto compute = [&](int kt, const KVBuf& buf) {
     const int j0 = kt * BN;
-    if (j0 <= wave_last) {
-      if ((j0 + BN - 1 > qw) || (j0 + BN > L) || (qw + 32 * NT > L)) {
-        int lim[NT];
+    if (j0 > wave_last) return;
+    if ((j0 + BN - 1 > qw) || (j0 + BN > L) || (qw + 32 * NT > L)) {
+      int lim[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int i = qw + t * 32 + l32;
-          lim[t] = i < L ? min(i, L - 1) - j0 - g * 4 : -1;
-        }
-        dq_tile<D, NT, true>(st, smem[buf][0], smem[buf][1], lane, c, lim);
-      } else {
-        const int lim[NT] = {};
-        dq_tile<D, NT, false>(st, smem[buf][0], smem[buf][1], lane, c, lim);
+      for (int t = 0; t < NT; ++t) {
+        const int i = qw + t * 32 + l32;
+        lim[t] = i < L ? min(i, L - 1) - j0 - g * 4 : -1;
       }
+      dq_tile<D, NT, true>(st, buf.k, buf.v, lane, c, lim);
+    } else {
+      const int lim[NT] = {};
+      dq_tile<D, NT, false>(st, buf.k, buf.v, lane, c, lim);
     }
-    if (more) {
-      kl.store(smem[buf ^ 1][0]);
-      vl.store(smem[buf ^ 1][1]);
-    }
-    __syncthreads();
-  }
+  };
+  tile_pipeline(ntiles, b0, b1, fetch, [](int, const KVBuf&) {}, compute);
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) {

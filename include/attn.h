@@ -56,7 +56,8 @@ typedef enum attn_status {
   ATTN_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, Hq % Hkv != 0,
                                 non-finite or non-positive scale */
   ATTN_ERR_UNSUPPORTED = 2,  /* head_dim not in {64, 128}, causal == 0,
-                                sizes whose element count overflows int32 indexing */
+                                heads_q * head_dim > 2^22 (tile offsets are
+                                32-bit), or a grid beyond 2^31 - 1 blocks */
   ATTN_ERR_MISALIGNED = 3,   /* a pointer is not 16-byte aligned */
   ATTN_ERR_WORKSPACE = 4,    /* workspace smaller than attn_bwd_workspace_bytes() */
   ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
