@@ -53,6 +53,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // that no load is still pending on any path into a main loop; otherwise the
 // compiler keeps a conservative vmcnt wait inside the loop that also drains
 // the next tile's prefetch every iteration.
+// Index of the calling wave in its workgroup, in a scalar register: the
+// compiler cannot tell that threadIdx.x / 64 is uniform, and a buffer resource
+// derived from it would otherwise live in VGPRs, wrapping each buffer
+// instruction in a readfirstlane loop.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Max / sum of x over lanes l and l ^ 32 (v_permlane32_swap: no LDS round trip).
@@ -141,11 +147,16 @@ __device__ __forceinline__ void tile_load_lds(const bf16* base, int64_t row_stri
   constexpr int KB_PER_BLOCK = D / 64;           // 1 KB pieces per 8-row block
   constexpr int NKB = R / 8 * KB_PER_BLOCK;      // wave instructions per tile
   static_assert(NKB % NWAVES == 0, "tile must split evenly over the waves");
+  // the descriptor is uniform; readfirstlane keeps it in SGPRs whatever
+  // register class the compiler picked for its inputs (a descriptor in VGPRs
+  // would wrap every load in a readfirstlane loop)
   const int rows = min(L - row0, R);
-  const int bytes = rows > 0 ? (int)(((int64_t)(rows - 1) * row_stride + D) * 2) : 0;
+  const int bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? ((rows - 1) * (int)row_stride + D) * 2 : 0);
+  const uint64_t addr = reinterpret_cast<uint64_t>(base + (int64_t)row0 * row_stride);
+  const uint64_t addr_u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
   const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base + (int64_t)row0 * row_stride), (short)0, bytes,
-                                        0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(addr_u), (short)0, bytes, 0x00020000);
 #pragma unroll
   for (int j = 0; j < NKB / NWAVES; ++j) {
     const int kb = wave * (NKB / NWAVES) + j;

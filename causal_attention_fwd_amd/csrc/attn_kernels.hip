@@ -89,6 +89,24 @@ extern "C" void* attn_trace_buffer() {
 #define ATTN_TRACE_END(kind)
 #endif
 
+#ifndef ATTN_PRIO_DKDV
+#define ATTN_PRIO_DKDV 1
+#endif
+#ifndef ATTN_PRIO_DQ
+#define ATTN_PRIO_DQ 1
+#endif
+// Wave priority while a wave issues its first run of MFMAs (0: leave the
+// default), so that the pipe is refilled promptly while a sibling wave on the
+// same SIMD runs VALU work.
+template <int PRIO>
+__device__ __forceinline__ void prio_mfma() {
+  if constexpr (PRIO != 0) __builtin_amdgcn_s_setprio(PRIO);
+}
+template <int PRIO>
+__device__ __forceinline__ void prio_base() {
+  if constexpr (PRIO != 0) __builtin_amdgcn_s_setprio(0);
+}
+
 // One stage of a K/V (or Q/dO) tile pipeline: two swizzled LDS tiles, and the
 // stage's index for side data kept in indexed arrays.
 struct KVBuf {
@@ -336,18 +354,32 @@ struct DkdvState {
 // positions inside the valid length).
 template <int D, int NTJ, bool MASK>
 __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs, const bf16* dOs, const float* lse2,
-                                          const float* dl, int lane, float c, const int (&lo)[NTJ],
+                                          const float* ndl, int lane, float c, const int (&lo)[NTJ],
                                           const int (&hi)[NTJ]) {
   constexpr int KK = D / 16, DT = D / 32;
   const int g = lane >> 5;
+  // dP starts from -D (row i of register rr*4 + e is m2*32 + rr*8 + g*4 + e,
+  // four consecutive rows per 16-byte read), so that the accumulator ends as
+  // dP - D and dS = P (dP - D) is one multiply
   f32x16 s[2][NTJ], dp[2][NTJ];
 #pragma unroll
-  for (int m2 = 0; m2 < 2; ++m2)
+  for (int m2 = 0; m2 < 2; ++m2) {
+    f32x16 nd;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float4 d4 = *reinterpret_cast<const float4*>(ndl + m2 * 32 + rr * 8 + g * 4);
+      nd[rr * 4 + 0] = d4.x;
+      nd[rr * 4 + 1] = d4.y;
+      nd[rr * 4 + 2] = d4.z;
+      nd[rr * 4 + 3] = d4.w;
+    }
 #pragma unroll
     for (int t = 0; t < NTJ; ++t) {
       s[m2][t] = zero16();
-      dp[m2][t] = zero16();
+      dp[m2][t] = nd;
     }
+  }
+  prio_mfma<ATTN_PRIO_DKDV>();
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -361,6 +393,7 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
       }
     }
   }
+  prio_base<ATTN_PRIO_DKDV>();
   // P = exp2(S*c - LSE*log2e), dS = P (dP - D); rows m2*32 + rr*8 + g*4 + e of
   // the lane's registers rr*4 + e, read four at a time
 #pragma unroll
@@ -369,9 +402,7 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
     for (int rr = 0; rr < 4; ++rr) {
       const int il0 = m2 * 32 + rr * 8 + g * 4;
       const float4 l2 = *reinterpret_cast<const float4*>(lse2 + il0);
-      const float4 d4 = *reinterpret_cast<const float4*>(dl + il0);
       const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
-      const float ddv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = rr * 4 + e;
@@ -382,7 +413,7 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
             const int off = m2 * 32 + rr * 8 + e;
             if (off < lo[t] || off > hi[t]) p = 0.f;
           }
-          dp[m2][t][r] = p * (dp[m2][t][r] - ddv[e]);
+          dp[m2][t][r] = p * dp[m2][t][r];
           s[m2][t][r] = p;
         }
       }
@@ -424,10 +455,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
   // [group] tiles; Q and dO of the two pipeline stages live in distinct arrays
   __shared__ __attribute__((aligned(16))) bf16 sQ0[GROUPS * TILE], sO0[GROUPS * TILE], sQ1[GROUPS * TILE],
       sO1[GROUPS * TILE];
-  __shared__ __attribute__((aligned(16))) float sstat[GROUPS][2][2][BMQ];  // [group][buf][LSE*log2e, D]
+  __shared__ __attribute__((aligned(16))) float sstat[GROUPS][2][2][BMQ];  // [group][buf][LSE*log2e, -D]
 
   ATTN_TRACE_BEGIN();
-  const int grp = threadIdx.x >> 8;
+  const int grp = wave_id() >> 2;
   const int gtid = threadIdx.x & (kThreads - 1);
   const int lane = threadIdx.x & 63;
   const int wave = gtid >> 6;
@@ -495,7 +526,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   };
   auto land = [&](int trip, const KVBuf& buf) {
     if (trip * GROUPS + grp < iters && gtid < 2 * BMQ)
-      sstat[grp][buf.idx][gtid / BMQ][gtid & (BMQ - 1)] = gtid < BMQ ? st_reg * kLog2e : st_reg;
+      sstat[grp][buf.idx][gtid / BMQ][gtid & (BMQ - 1)] = gtid < BMQ ? st_reg * kLog2e : -st_reg;
   };
   auto compute = [&](int trip, const KVBuf& buf) {
     const int it = trip * GROUPS + grp;
@@ -609,6 +640,7 @@ __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, cons
       s[mt][t] = zero16();
       dp[mt][t] = zero16();
     }
+  prio_mfma<ATTN_PRIO_DQ>();
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -622,6 +654,7 @@ __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, cons
       }
     }
   }
+  prio_base<ATTN_PRIO_DQ>();
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -763,7 +796,7 @@ namespace {
 #define ATTN_DQ_NT64 1
 #endif
 #ifndef ATTN_DQ_OCC64
-#define ATTN_DQ_OCC64 2
+#define ATTN_DQ_OCC64 3
 #endif
 #ifndef ATTN_DKDV_OCC64
 #define ATTN_DKDV_OCC64 2
