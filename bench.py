@@ -16,6 +16,7 @@ Other modes (measurement tooling, used under rocprofv3):
     --copy-calibration       run a plain device copy of known size (counter scale)
     --pmc-summary DIR ...    turn rocprofv3 --pmc outputs into profiles/*_pmc.txt
     --trace-summary DIR      turn a rocprofv3 --kernel-trace --stats run into profiles/*_trace.txt
+    --sq-summary DIR ...     turn rocprofv3 --pmc runs of SQ counters into profiles/*_sq.txt
 """
 from __future__ import annotations
 
@@ -121,6 +122,47 @@ def pmc_summary(args):
             out.write(f"scale_fetch: {f_scale:.4f}\nscale_write: {w_scale:.4f}\n")
             out.write(f"traffic_bytes_per_dispatch: {traffic:.0f}\n")
         log(f"wrote {path}: {traffic / 1e6:.1f} MB per dispatch")
+
+
+def sq_summary(args):
+    """profiles/<kernel>_<workload>_sq.txt from rocprofv3 --pmc runs of SQ
+    counters (any split over runs), averaged per dispatch, with the derived
+    utilisation figures: MFMA busy and VALU active per SIMD (the SQ counters
+    sum over SIMDs and count quad-cycles where noted), GRBM_GUI_ACTIVE summed
+    over the 8 XCDs."""
+    rows = []
+    for d in args.sq_summary:
+        rows += _pmc_rows(d)
+    counters = sorted({r["Counter_Name"] for r in rows})
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for kname in KERNEL_NAMES.values():
+        vals = {}
+        for c in counters:
+            v, n = _avg_counter(rows, kname, c)
+            if v is not None:
+                vals[c] = (v, n)
+        if not vals:
+            continue
+        path = os.path.join(ROOT, "profiles", f"{kname}_{args.workload}_sq.txt")
+        with open(path, "w") as out:
+            out.write(f"# SQ counters of {kname} on workload {args.workload} (per dispatch, mean over dispatches)\n")
+            out.write(f"# commands: {args.pmc_command}\n")
+            out.write(f"kernel_source_sha256_16: {kernel_source_sha()}\n")
+            for c, (v, n) in vals.items():
+                out.write(f"{c}: {v:.6g}  ({n} dispatches)\n")
+            simds, xcds = 1024, 8
+            if "GRBM_GUI_ACTIVE" in vals:
+                cyc = vals["GRBM_GUI_ACTIVE"][0] / xcds
+                out.write(f"elapsed_cycles_per_xcd: {cyc:.0f}\n")
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+                    out.write(f"mfma_busy_fraction: {vals['SQ_VALU_MFMA_BUSY_CYCLES'][0] / (cyc * simds):.3f}\n")
+                if "SQ_ACTIVE_INST_VALU" in vals:  # quad-cycles
+                    out.write(f"valu_active_fraction: {4 * vals['SQ_ACTIVE_INST_VALU'][0] / (cyc * simds):.3f}\n")
+                if "SQ_LDS_IDX_ACTIVE" in vals:
+                    out.write(f"lds_active_fraction_per_cu: {vals['SQ_LDS_IDX_ACTIVE'][0] / (cyc * 256):.3f}\n")
+            if "SQ_INSTS_MFMA" in vals:
+                out.write(f"mfma_flop_executed: {vals['SQ_INSTS_MFMA'][0] * 32768:.4g}  (32x32x16 bf16 = 32768 flop each)\n")
+        log(f"wrote {path}")
 
 
 def trace_summary(args):
@@ -310,6 +352,7 @@ def main():
     ap.add_argument("--copy-bytes", type=float, default=1 << 30)
     ap.add_argument("--copy-kernel", default="copy")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
+    ap.add_argument("--sq-summary", nargs="+", metavar="DIR")
     ap.add_argument("--pmc-command", default="", help="command line recorded in the written summaries")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR")
     args = ap.parse_args()
@@ -322,6 +365,8 @@ def main():
         pmc_summary(args)
     elif args.trace_summary:
         trace_summary(args)
+    elif args.sq_summary:
+        sq_summary(args)
     elif args.copy_calibration:
         copy_calibration(args)
     else:
