@@ -17,6 +17,10 @@ What it computes (the plain definition, materialising every probability):
     reimplemented from the documented formula.
   * "AxiomLM" (PyPI page), "Key Features": grouped-query attention, kv heads
     shared by consecutive groups of query heads (head h reads kv head h // G).
+  * "Axis" (Rust/cuTile page), "Sudoku as an acceptance test": its transformer
+    uses bidirectional multi-head attention, the same softmax attention with
+    no causal restriction (``causal=False`` below: every key of the valid
+    prefix, j < L, enters every row's sum instead of j <= i).
 
 The pages never print the formula; this is the textbook reading. For one
 sequence with valid prefix length L (right padding) and one query head:
@@ -29,6 +33,7 @@ sequence with valid prefix length L (right padding) and one query head:
   dQ_i  = scale * sum_j dS_ij k_j
   dK_j  = scale * sum_{h in group} sum_i dS_ij q_i
   dV_j  = sum_{h in group} sum_i P_ij dO_i
+With causal=False every "j <= i" above reads "j < L".
 These are the exact gradients of f = sum(O * dO) with respect to Q, K, V.
 Only positions inside the valid prefix ever enter a sum, so whatever a padded
 position holds (even NaN) cannot reach an output.
@@ -66,18 +71,19 @@ def _check(q, k, v):
     return B, S, Hq, Hkv, d
 
 
-def probabilities(qh, kh, scale: float, dtype=np.float64):
-    """Causal softmax of one (sequence, query head) over its valid prefix.
+def probabilities(qh, kh, scale: float, dtype=np.float64, causal: bool = True):
+    """Softmax of one (sequence, query head) over its valid prefix.
 
     qh, kh: [L, d] (the valid prefix only). Returns (P [L, L], lse [L]).
-    Every row i has at least the key j = 0, so every row is a proper
-    distribution over keys 0..i; entries above the diagonal are exactly 0."""
+    Causal: every row i has at least the key j = 0, so every row is a proper
+    distribution over keys 0..i; entries above the diagonal are exactly 0.
+    Not causal: every row is a distribution over all L keys."""
     qh = np.asarray(qh, dtype=dtype)
     kh = np.asarray(kh, dtype=dtype)
     L = qh.shape[0]
-    causal = np.tril(np.ones((L, L), dtype=bool))
+    allowed = np.tril(np.ones((L, L), dtype=bool)) if causal else np.ones((L, L), dtype=bool)
     s = (qh @ kh.T) * dtype(scale)
-    s = np.where(causal, s, -np.inf)
+    s = np.where(allowed, s, -np.inf)
     m = np.max(s, axis=1) if L > 0 else np.zeros((0,), dtype=dtype)
     e = np.exp(s - m[:, None])          # exactly 0 above the diagonal
     denom = np.sum(e, axis=1)
@@ -86,7 +92,7 @@ def probabilities(qh, kh, scale: float, dtype=np.float64):
     return P.astype(dtype), lse.astype(dtype)
 
 
-def forward(q, k, v, scale: float, seqlens=None, dtype=np.float64):
+def forward(q, k, v, scale: float, seqlens=None, dtype=np.float64, causal: bool = True):
     """Attention forward: returns (O [B,S,Hq,d], LSE [B,Hq,S]) in ``dtype``."""
     q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     B, S, Hq, Hkv, d = _check(q, k, v)
@@ -98,7 +104,7 @@ def forward(q, k, v, scale: float, seqlens=None, dtype=np.float64):
         L = lens[b]
         for h in range(Hq):
             g = h // G
-            P, lse = probabilities(q[b, :L, h, :], k[b, :L, g, :], scale, dtype)
+            P, lse = probabilities(q[b, :L, h, :], k[b, :L, g, :], scale, dtype, causal)
             O[b, :L, h, :] = P @ np.asarray(v[b, :L, g, :], dtype=dtype)
             LSE[b, h, :L] = lse
     return O, LSE
@@ -121,7 +127,7 @@ def preprocess(o, do, seqlens=None, dtype=np.float64):
     return D
 
 
-def backward(q, k, v, do, scale: float, seqlens=None, dtype=np.float64):
+def backward(q, k, v, do, scale: float, seqlens=None, dtype=np.float64, causal: bool = True):
     """Attention backward from scratch (the forward is recomputed here).
 
     Returns a dict with O, LSE, D, dQ, dK, dV (all in ``dtype``)."""
@@ -146,7 +152,7 @@ def backward(q, k, v, do, scale: float, seqlens=None, dtype=np.float64):
             kh = np.asarray(k[b, :L, g, :], dtype=dtype)
             vh = np.asarray(v[b, :L, g, :], dtype=dtype)
             doh = np.asarray(do[b, :L, h, :], dtype=dtype)
-            P, lse = probabilities(qh, kh, scale, dtype)
+            P, lse = probabilities(qh, kh, scale, dtype, causal)
             oh = P @ vh
             Dh = np.sum(doh * oh, axis=1)
             dP = doh @ vh.T

@@ -46,12 +46,13 @@ def load_golden(name):
     B, S, Hq, Hkv, d = (int(meta[k]) for k in ("B", "S", "Hq", "Hkv", "d"))
     scale = _value(meta["scale"])
     seqlens = None if meta["seqlens"] == "none" else [int(x) for x in meta["seqlens"].split(",")]
+    causal = meta.get("causal", "1") == "1"
     shapes = {"Q": (B, S, Hq, d), "K": (B, S, Hkv, d), "V": (B, S, Hkv, d), "dO": (B, S, Hq, d),
               "O": (B, S, Hq, d), "dQ": (B, S, Hq, d), "dK": (B, S, Hkv, d), "dV": (B, S, Hkv, d),
               "LSE": (B, Hq, S), "D": (B, Hq, S)}
     arrays = {k: np.array([_value(t) for t in v.split()], dtype=np.float64).reshape(shapes[k])
               for k, v in fields.items()}
-    return arrays, scale, seqlens
+    return arrays, scale, seqlens, causal
 
 
 def rand_inputs(B, S, Hq, Hkv, d, seed, q_scale=1.0):
@@ -70,17 +71,17 @@ def objective(q, k, v, do, scale, seqlens=None, orc=oracle):
 
 # ----------------------------------------------------------------- golden
 
-@pytest.mark.parametrize("name", ["hand_s3_d2.txt", "hand_gqa_padded.txt"])
+@pytest.mark.parametrize("name", ["hand_s3_d2.txt", "hand_gqa_padded.txt", "hand_noncausal_s3_d2.txt"])
 def test_hand_worked_examples(name, orc=oracle):
-    g, scale, seqlens = load_golden(name)
-    out = orc.backward(g["Q"], g["K"], g["V"], g["dO"], scale, seqlens)
+    g, scale, seqlens, causal = load_golden(name)
+    out = orc.backward(g["Q"], g["K"], g["V"], g["dO"], scale, seqlens, causal=causal)
     for key in ("O", "LSE", "D", "dQ", "dK", "dV"):
         exp, got = g[key], out[key]
         assert np.array_equal(np.isinf(exp), np.isinf(got)), key
         fin = np.isfinite(exp)
         assert np.all(np.isfinite(got[fin])), key
         np.testing.assert_allclose(got[fin], exp[fin], rtol=0, atol=1e-12, err_msg=key)
-    O, LSE = orc.forward(g["Q"], g["K"], g["V"], scale, seqlens)
+    O, LSE = orc.forward(g["Q"], g["K"], g["V"], scale, seqlens, causal=causal)
     np.testing.assert_array_equal(O, out["O"])
     np.testing.assert_array_equal(LSE, out["LSE"])
     D = orc.preprocess(out["O"], g["dO"], seqlens)

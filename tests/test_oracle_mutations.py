@@ -11,6 +11,7 @@ import types
 import pytest
 
 import test_oracle as pins
+import test_oracle_noncausal as ncpins
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
 
@@ -27,6 +28,13 @@ MUTATIONS = {
     "D_without_O": ("Dh = np.sum(doh * oh, axis=1)", "Dh = np.sum(doh, axis=1)"),
     "padding_ignored": ("L = lens[b]\n        for h in range(Hq):\n            g = h // G\n            qh",
                         "L = S\n        for h in range(Hq):\n            g = h // G\n            qh"),
+    # the bidirectional path
+    "noncausal_still_causal": ("if causal else np.ones((L, L), dtype=bool)",
+                               "if True else np.ones((L, L), dtype=bool)"),
+    "noncausal_upper_triangle": ("if causal else np.ones((L, L), dtype=bool)",
+                                 "if causal else np.triu(np.ones((L, L), dtype=bool))"),
+    "backward_ignores_causal_flag": ("P, lse = probabilities(qh, kh, scale, dtype, causal)",
+                                     "P, lse = probabilities(qh, kh, scale, dtype)"),
 }
 
 
@@ -47,6 +55,10 @@ def _pins(orc):
     yield lambda: pins.test_gqa_equals_explicit_repeat(orc)
     yield lambda: pins.test_padding_equals_prefix_slice_and_ignores_nan(orc)
     yield lambda: pins.test_lse_matches_torch_logsumexp_routine(orc)
+    yield lambda: pins.test_hand_worked_examples("hand_noncausal_s3_d2.txt", orc)
+    yield lambda: ncpins.test_matches_torch_sdpa_fp64(2, 64, 6, 2, 16, [64, 41], orc)
+    yield lambda: ncpins.test_uniform_scores_full_mean(orc)
+    yield lambda: ncpins.test_permutation_equivariance(orc)
 
 
 def test_unmutated_copy_passes_every_pin():
