@@ -106,17 +106,19 @@ def workload_inputs(w: Workload) -> Inputs:
     return make_inputs(w.B, w.S, w.Hq, w.Hkv, w.d, w.seed, do_sigma=w.do_sigma, padded=w.padded)
 
 
-def valid_pairs(S: int, B: int, seqlens=None) -> int:
-    """Number of (i, j) query/key pairs with j <= i < L_b, summed over the batch.
+def valid_pairs(S: int, B: int, seqlens=None, causal: bool = True) -> int:
+    """Number of (i, j) query/key pairs with j <= i < L_b (causal) or with
+    i, j < L_b (bidirectional), summed over the batch.
 
     Pure counting (no attention arithmetic): used to price algorithmic work.
     """
-    if seqlens is None:
-        return B * S * (S + 1) // 2
-    return int(sum(int(L) * (int(L) + 1) // 2 for L in seqlens.tolist()))
+    lens = [S] * B if seqlens is None else [int(L) for L in seqlens.tolist()]
+    if causal:
+        return int(sum(L * (L + 1) // 2 for L in lens))
+    return int(sum(L * L for L in lens))
 
 
-def algorithmic_flops(w_or_shape, seqlens=None) -> dict:
+def algorithmic_flops(w_or_shape, seqlens=None, causal: bool = True) -> dict:
     """Algorithmic flop counts: 4*d per valid pair per query head (QK^T and PV)
     forward; backward 2.5x that (five GEMMs incl. the QK^T recompute).
     Per-kernel shares: dK/dV kernel 8*d (S, dP, dV, dK), dQ kernel 2*d (dQ)."""
@@ -124,7 +126,7 @@ def algorithmic_flops(w_or_shape, seqlens=None) -> dict:
         B, S, Hq, d = w_or_shape.B, w_or_shape.S, w_or_shape.Hq, w_or_shape.d
     else:
         B, S, Hq, d = w_or_shape
-    pairs = valid_pairs(S, B, seqlens)
+    pairs = valid_pairs(S, B, seqlens, causal)
     fwd = 4.0 * d * Hq * pairs
     return {"pairs_per_head": pairs, "fwd": fwd, "bwd": 2.5 * fwd, "total": 3.5 * fwd,
             "bwd_dkdv": 2.0 * fwd, "bwd_dq": 0.5 * fwd}

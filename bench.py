@@ -217,7 +217,7 @@ def copy_calibration(args):
 
 # ----------------------------------------------------------------------------- the benchmark
 
-def cpu_baseline(w, inp, budget_s: float):
+def cpu_baseline(w, inp, budget_s: float, causal: bool = True):
     """The oracle (fp32 mode, untuned) on whole (sequence, kv head) units of the
     same workload until about `budget_s` seconds of CPU work have been spent."""
     import numpy as np
@@ -236,9 +236,9 @@ def cpu_baseline(w, inp, budget_s: float):
     for b, g in units:
         hs = slice(g * G, (g + 1) * G)
         oracle.backward(q[b:b + 1, :, hs], k[b:b + 1, :, g:g + 1], v[b:b + 1, :, g:g + 1], do[b:b + 1, :, hs],
-                        inp.scale, None if sl is None else sl[b:b + 1], dtype=np.float32)
+                        inp.scale, None if sl is None else sl[b:b + 1], dtype=np.float32, causal=causal)
         done += 1
-        pairs = valid_pairs(w.S, 1, None if sl is None else sl[b:b + 1])
+        pairs = valid_pairs(w.S, 1, None if sl is None else sl[b:b + 1], causal)
         flops += 3.5 * 4.0 * w.d * G * pairs
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -268,21 +268,23 @@ def run(args):
     delta = torch.empty(B, Hq, S, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     scale = inp.scale
-    fl = algorithmic_flops(w, inp.seqlens)
+    causal = not args.non_causal
+    fl = algorithmic_flops(w, inp.seqlens, causal)
+    cz = int(causal)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        attn.attn_fwd(q, k, v, o, lse, scale, sl)
+        attn.attn_fwd(q, k, v, o, lse, scale, sl, cz)
         if ev is not None:
             ev[1].record()
         attn.attn_bwd_preprocess(o, do, delta, sl)
         if ev is not None:
             ev[2].record()
-        attn.attn_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, scale, sl)
+        attn.attn_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, scale, sl, cz)
         if ev is not None:
             ev[3].record()
-        attn.attn_bwd_dq(q, k, v, do, lse, delta, dq, scale, sl)
+        attn.attn_bwd_dq(q, k, v, do, lse, delta, dq, scale, sl, cz)
         if ev is not None:
             ev[4].record()
 
@@ -318,13 +320,13 @@ def run(args):
                 "frac": achieved / PEAK_BF16_TFLOPS}
     roof["kernel"] = KERNEL_NAMES[dom]
     roof["ms_per_launch"] = per[dom]
-    roof["traffic"] = read_traffic(dom, w.name)
+    roof["traffic"] = read_traffic(dom, w.name) if causal else None
 
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": dict(w.describe(), valid_pairs_per_head=fl["pairs_per_head"],
+        "config": dict(w.describe(), causal=causal, valid_pairs_per_head=fl["pairs_per_head"],
                        algorithmic_gflop_per_step=round(fl["total"] / 1e9, 3)),
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernel_ms": {KERNEL_NAMES[n]: round(per[n], 4) for n in names},
@@ -334,7 +336,7 @@ def run(args):
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, causal)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
@@ -348,6 +350,8 @@ def main():
     ap.add_argument("--workload", default="llama1b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work in cpu_baseline")
+    ap.add_argument("--non-causal", action="store_true",
+                    help="bidirectional attention (causal = 0): every key of the valid prefix, all pairs priced")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--copy-bytes", type=float, default=1 << 30)
     ap.add_argument("--copy-kernel", default="copy")

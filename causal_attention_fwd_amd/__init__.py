@@ -225,7 +225,7 @@ def attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale: float, seqlens=None, causal
 
 # ------------------------------------------------------------------ allocating conveniences
 
-def forward(q, k, v, scale: Optional[float] = None, seqlens=None):
+def forward(q, k, v, scale: Optional[float] = None, seqlens=None, causal: bool = True):
     """Returns (O, LSE) as new tensors."""
     torch = _torch()
     B, S, Hq, d = q.shape
@@ -233,11 +233,11 @@ def forward(q, k, v, scale: Optional[float] = None, seqlens=None):
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, o, lse, scale, seqlens)
+    attn_fwd(q, k, v, o, lse, scale, seqlens, int(causal))
     return o, lse
 
 
-def backward(q, k, v, o, d_o, lse, scale: Optional[float] = None, seqlens=None):
+def backward(q, k, v, o, d_o, lse, scale: Optional[float] = None, seqlens=None, causal: bool = True):
     """Returns (dQ, dK, dV, D) as new tensors (runs the preprocess, then the backward)."""
     torch = _torch()
     B, S, Hq, d = q.shape
@@ -248,5 +248,5 @@ def backward(q, k, v, o, d_o, lse, scale: Optional[float] = None, seqlens=None):
     need = attn_bwd_workspace_bytes(B, S, Hq, k.shape[2], d)
     ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, ws)
+    attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, ws, int(causal))
     return dq, dk, dv, delta

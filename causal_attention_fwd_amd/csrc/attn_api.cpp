@@ -18,7 +18,7 @@ attn_status check_shape(const attn_shape* s, attn::Problem* pr) {
   if (s->heads_q % s->heads_kv != 0) return ATTN_ERR_INVALID_ARG;
   if (!(isfinite(s->scale) && s->scale > 0.f)) return ATTN_ERR_INVALID_ARG;
   if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
-  if (s->causal != 1) return ATTN_ERR_UNSUPPORTED;
+  if (s->causal != 0 && s->causal != 1) return ATTN_ERR_INVALID_ARG;
   if (s->seqlens && (reinterpret_cast<uintptr_t>(s->seqlens) & 3u) != 0) return ATTN_ERR_MISALIGNED;
   // tiles are fetched through buffer resources with 32-bit byte offsets that
   // span up to 128 rows of one sequence: 128 * heads * head_dim * 2 < 2^31
@@ -30,6 +30,7 @@ attn_status check_shape(const attn_shape* s, attn::Problem* pr) {
   pr->d = s->head_dim;
   pr->scale = s->scale;
   pr->seqlens = s->seqlens;
+  pr->causal = s->causal;
   if (attn::max_grid(*pr) > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
@@ -113,7 +114,7 @@ const char* attn_status_string(attn_status status) {
   switch (status) {
     case ATTN_OK: return "ATTN_OK";
     case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: null pointer, bad size, Hq % Hkv != 0 or bad scale";
-    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: head_dim must be 64 or 128, causal must be 1";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: head_dim must be 64 or 128";
     case ATTN_ERR_MISALIGNED: return "ATTN_ERR_MISALIGNED: tensor pointers must be 16-byte aligned";
     case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace smaller than attn_bwd_workspace_bytes()";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: the HIP runtime reported a launch error";

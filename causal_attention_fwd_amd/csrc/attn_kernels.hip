@@ -38,6 +38,7 @@ struct FwdArgs {
   const int32_t* seqlens;
   int B, S, Hq, Hkv, nqb;
   float scale;
+  int causal;  // 1: keys j <= i only; 0: every key of the valid prefix
 };
 
 struct PreArgs {
@@ -62,6 +63,7 @@ struct BwdArgs {
   const int32_t* seqlens;
   int B, S, Hq, Hkv, nblk;
   float scale;
+  int causal;  // 1: keys j <= i only; 0: every key of the valid prefix
 };
 
 constexpr int kThreads = 256;  // four waves, one per SIMD
@@ -136,7 +138,8 @@ struct FwdState {
 };
 
 // One 64-key tile for one wave. MASK: keys past min(row, L-1) are excluded;
-// lim[t] = min(i, L-1) - j0 - (lane/32)*4 for the lane's row i of n-tile t.
+// lim[t] = min(i, L-1) - j0 - (lane/32)*4 for the lane's row i of n-tile t
+// (causal), L-1 - j0 - (lane/32)*4 (bidirectional).
 template <int D, int NT, bool MASK>
 __device__ __forceinline__ void fwd_tile(FwdState<D, NT>& st, const bf16* Ks, const bf16* Vs, int lane, float c,
                                          const int (&lim)[NT]) {
@@ -246,8 +249,11 @@ void fwd_kernel(FwdArgs a) {
 
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32 * NT;
-  const int ntiles = (q0 < L) ? (min(q0 + BM, L) - 1) / BN + 1 : 0;
+  // causal: key tiles up to the block's last row; bidirectional: all of them
+  const int kend = a.causal ? min(q0 + BM, L) : L;
+  const int ntiles = (q0 < L) ? (kend - 1) / BN + 1 : 0;
   const int wave_last = min(qw + 32 * NT, L) - 1;  // < qw when the wave is all padding
+  const int key_last = a.causal ? wave_last : (wave_last < qw ? -1 : L - 1);  // last key a row of the wave sees
   const float c = a.scale * kLog2e;
 
   FwdState<D, NT> st;
@@ -272,11 +278,11 @@ void fwd_kernel(FwdArgs a) {
   };
   auto compute = [&](int kt, const KVBuf& buf) {
     const int j0 = kt * BN;
-    if (j0 > wave_last) return;
-    if ((j0 + BN - 1 > qw) || (j0 + BN > L)) {
+    if (j0 > key_last) return;
+    if ((a.causal && j0 + BN - 1 > qw) || (j0 + BN > L)) {
       int lim[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) lim[t] = min(qw + t * 32 + l32, L - 1) - j0 - g * 4;
+      for (int t = 0; t < NT; ++t) lim[t] = (a.causal ? min(qw + t * 32 + l32, L - 1) : L - 1) - j0 - g * 4;
       fwd_tile<D, NT, true>(st, buf.k, buf.v, lane, c, lim);
     } else {
       const int lim[NT] = {};
@@ -497,7 +503,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
   wait_vmem();
 
-  const int qt0 = j0 / BMQ;
+  const int qt0 = a.causal ? j0 / BMQ : 0;  // first query tile with rows at or below the block
   const int nq = (j0 < L) ? (L - 1) / BMQ - qt0 + 1 : 0;  // query tiles per head
   const int iters = nq * G;                               // (head, query tile) pairs
   const int trips = (iters + GROUPS - 1) / GROUPS;        // this group does it = trip*GROUPS + grp
@@ -536,15 +542,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int i0 = qt * BMQ;
     // skip when every query row of the tile is above this wave's key rows, or
     // the wave's keys are all padding
-    if (i0 + BMQ - 1 < jw || jw >= L) return;
+    if ((a.causal && i0 + BMQ - 1 < jw) || jw >= L) return;
     const float* ls = sstat[grp][buf.idx][0];
     const float* ds = sstat[grp][buf.idx][1];
-    if ((i0 < jw + 32 * NTJ - 1) || (i0 + BMQ > L) || (jw + 32 * NTJ > L)) {
+    if ((a.causal && i0 < jw + 32 * NTJ - 1) || (i0 + BMQ > L) || (jw + 32 * NTJ > L)) {
       int lo[NTJ], hi[NTJ];
 #pragma unroll
       for (int t = 0; t < NTJ; ++t) {
         const int j = jw + t * 32 + l32;
-        lo[t] = j - i0 - g * 4;                     // i >= j
+        lo[t] = a.causal ? j - i0 - g * 4 : -(1 << 30);  // causal: i >= j
         hi[t] = (j < L) ? L - 1 - i0 - g * 4 : -1;  // i < L, and no rows when j >= L
       }
       dkdv_tile<D, NTJ, true>(st, buf.k, buf.v, ls, ds, lane, c, lo, hi);
@@ -713,8 +719,10 @@ void bwd_dq_kernel(BwdArgs a) {
 
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32 * NT;
-  const int ntiles = (q0 < L) ? (min(q0 + BM, L) - 1) / BN + 1 : 0;
+  const int kend = a.causal ? min(q0 + BM, L) : L;
+  const int ntiles = (q0 < L) ? (kend - 1) / BN + 1 : 0;
   const int wave_last = min(qw + 32 * NT, L) - 1;
+  const int key_last = a.causal ? wave_last : (wave_last < qw ? -1 : L - 1);
   const float c = a.scale * kLog2e;
 
   DqState<D, NT> st;
@@ -743,13 +751,13 @@ void bwd_dq_kernel(BwdArgs a) {
   };
   auto compute = [&](int kt, const KVBuf& buf) {
     const int j0 = kt * BN;
-    if (j0 > wave_last) return;
-    if ((j0 + BN - 1 > qw) || (j0 + BN > L) || (qw + 32 * NT > L)) {
+    if (j0 > key_last) return;
+    if ((a.causal && j0 + BN - 1 > qw) || (j0 + BN > L) || (qw + 32 * NT > L)) {
       int lim[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int i = qw + t * 32 + l32;
-        lim[t] = i < L ? min(i, L - 1) - j0 - g * 4 : -1;
+        lim[t] = i < L ? (a.causal ? i : L - 1) - j0 - g * 4 : -1;
       }
       dq_tile<D, NT, true>(st, buf.k, buf.v, lane, c, lim);
     } else {
@@ -845,7 +853,7 @@ hipError_t fwd_d(const Problem& pr, const void* q, const void* k, const void* v,
                  hipStream_t stream) {
   constexpr int NT = Tiles<D>::FWD_NT;
   FwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, pr.seqlens,
-            pr.B, pr.S, pr.Hq, pr.Hkv, cdiv(pr.S, 128 * NT), pr.scale};
+            pr.B, pr.S, pr.Hq, pr.Hkv, cdiv(pr.S, 128 * NT), pr.scale, pr.causal};
   return launch((const void*)&fwd_kernel<D, NT, Tiles<D>::FWD_OCC>, (int64_t)a.nqb * pr.B * pr.Hq, a, stream);
 }
 
@@ -863,7 +871,7 @@ hipError_t dkdv_d(const Problem& pr, const void* q, const void* k, const void* v
   constexpr int NTJ = Tiles<D>::DKDV_NTJ;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             nullptr, (bf16*)dk, (bf16*)dv, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
-            cdiv(pr.S, 128 * NTJ), pr.scale};
+            cdiv(pr.S, 128 * NTJ), pr.scale, pr.causal};
   constexpr int GR = Tiles<D>::DKDV_GROUPS;
   return launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR>, (int64_t)a.nblk * pr.B * pr.Hkv, a,
                 stream, kThreads * GR);
@@ -875,7 +883,7 @@ hipError_t dq_d(const Problem& pr, const void* q, const void* k, const void* v, 
   constexpr int NT = Tiles<D>::DQ_NT;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             (bf16*)dq, nullptr, nullptr, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
-            cdiv(pr.S, 128 * NT), pr.scale};
+            cdiv(pr.S, 128 * NT), pr.scale, pr.causal};
   return launch((const void*)&bwd_dq_kernel<D, NT, Tiles<D>::DQ_OCC>, (int64_t)a.nblk * pr.B * pr.Hq, a, stream);
 }
 

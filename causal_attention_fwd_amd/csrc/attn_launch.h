@@ -11,6 +11,7 @@ struct Problem {
   int B, S, Hq, Hkv, d;
   float scale;
   const int32_t* seqlens;  // device int32[B] or nullptr
+  int causal;              // 1: keys j <= i only; 0: every key of the valid prefix
 };
 
 hipError_t launch_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,

@@ -54,8 +54,8 @@ extern "C" {
 typedef enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, Hq % Hkv != 0,
-                                non-finite or non-positive scale */
-  ATTN_ERR_UNSUPPORTED = 2,  /* head_dim not in {64, 128}, causal == 0,
+                                non-finite or non-positive scale, causal not 0/1 */
+  ATTN_ERR_UNSUPPORTED = 2,  /* head_dim not in {64, 128},
                                 heads_q * head_dim > 2^22 (tile offsets are
                                 32-bit), or a grid beyond 2^31 - 1 blocks */
   ATTN_ERR_MISALIGNED = 3,   /* a pointer is not 16-byte aligned */
@@ -70,7 +70,8 @@ typedef struct attn_shape {
   int32_t heads_kv;    /* Hkv >= 1 */
   int32_t head_dim;    /* d: 64 or 128 */
   float scale;         /* softmax scale, finite and > 0 (typically 1/sqrt(d)) */
-  int32_t causal;      /* must be 1 (non-causal attention is not provided) */
+  int32_t causal;      /* 1: causal (query i sees keys j <= i); 0: bidirectional
+                          (every query sees every key of the valid prefix) */
   /* Optional DEVICE int32[B]: valid prefix length L_b of each sequence (right
      padding). NULL means every sequence has length S. Values are clamped into
      [0, S] on the device; positions i >= L_b take no part in any sum, may hold

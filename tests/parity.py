@@ -34,11 +34,12 @@ def to_gpu(inp):
     return t
 
 
-def run_gpu(inp, t=None):
+def run_gpu(inp, t=None, causal=True):
     """fwd -> preprocess -> bwd on the GPU; returns host fp32 numpy arrays."""
     t = t or to_gpu(inp)
-    o, lse = attn.forward(t["q"], t["k"], t["v"], inp.scale, t["seqlens"])
-    dq, dk, dv, delta = attn.backward(t["q"], t["k"], t["v"], o, t["do"], lse, inp.scale, t["seqlens"])
+    o, lse = attn.forward(t["q"], t["k"], t["v"], inp.scale, t["seqlens"], causal=causal)
+    dq, dk, dv, delta = attn.backward(t["q"], t["k"], t["v"], o, t["do"], lse, inp.scale, t["seqlens"],
+                                      causal=causal)
     torch.cuda.synchronize()
     host = lambda x: x.float().cpu().numpy()  # noqa: E731
     return {"O": host(o), "LSE": host(lse), "D": host(delta), "dQ": host(dq), "dK": host(dk), "dV": host(dv)}
@@ -50,14 +51,14 @@ def host_inputs(inp):
     return q, k, v, do, sl
 
 
-def oracle_unit(inp, b, hkv, dtype=np.float64):
+def oracle_unit(inp, b, hkv, dtype=np.float64, causal=True):
     """Oracle on one (sequence, kv head) unit: the kv head and its query-head group."""
     q, k, v, do, sl = host_inputs(inp)
     G = q.shape[2] // k.shape[2]
     hs = slice(hkv * G, (hkv + 1) * G)
     sub_sl = None if sl is None else sl[b:b + 1]
     ref = oracle.backward(q[b:b + 1, :, hs], k[b:b + 1, :, hkv:hkv + 1], v[b:b + 1, :, hkv:hkv + 1],
-                          do[b:b + 1, :, hs], inp.scale, sub_sl, dtype=dtype)
+                          do[b:b + 1, :, hs], inp.scale, sub_sl, dtype=dtype, causal=causal)
     return ref
 
 

@@ -87,7 +87,7 @@ def _pre(lib, shape, ptrs=(GOOD,) * 3):
     (dict(B=0), 1), (dict(S=0), 1), (dict(Hq=0), 1), (dict(Hkv=0), 1), (dict(S=-5), 1),
     (dict(Hq=6, Hkv=4), 1), (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
     (dict(scale=0.0), 1), (dict(scale=-0.1), 1),
-    (dict(d=32), 2), (dict(d=96), 2), (dict(d=256), 2), (dict(causal=0), 2),
+    (dict(d=32), 2), (dict(d=96), 2), (dict(d=256), 2), (dict(causal=2), 1), (dict(causal=-1), 1),
     (dict(seqlens_ptr=GOOD + 2), 3),
     (dict(B=2 ** 30, S=2 ** 20), 2), (dict(Hq=2 ** 17, Hkv=1), 2), (dict(Hq=2 ** 16, Hkv=2 ** 16, d=128), 2),
 ])
