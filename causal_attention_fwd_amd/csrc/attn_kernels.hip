@@ -1,5 +1,5 @@
-// gfx950 kernels for fused causal attention: forward, backward preprocess,
-// backward dK/dV and backward dQ.
+// gfx950 kernels for fused causal (or bidirectional) attention: forward,
+// backward preprocess, backward dK/dV and backward dQ.
 //
 // The method ("Axis", Zyora Labs page, feature list): flash attention forward
 // and backward on matrix cores in which the attention probabilities never reach
@@ -18,10 +18,11 @@
 //    P / dS feed dV^T = dO^T P and dK^T = Q^T dS as B operands directly;
 //  * the transposed A operands (V^T, K^T, dO^T, Q^T) come from row-major LDS tiles
 //    through the gfx950 transposing LDS read (ds_read_b64_tr_b16);
-//  * K/V (or Q/dO) tiles are double-buffered in LDS with a register prefetch of
-//    the next tile, one barrier per tile;
+//  * K/V (or Q/dO) tiles stream from global memory straight into LDS
+//    (buffer_load ... lds), double-buffered, one barrier per tile;
 //  * tiles entirely above the causal diagonal or past a sequence's valid length
-//    are never loaded or computed; the mask is applied only on tiles that need it;
+//    are never loaded or computed; the mask is applied only on tiles that need it
+//    (bidirectional attention, causal = 0, skips and masks only the padding);
 //  * the softmax runs in base 2 with scale*log2(e) folded into one multiply;
 //    LSE is exported as a natural log.
 #include "attn_common.h"

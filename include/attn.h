@@ -1,8 +1,9 @@
 /*
  * attn.h - C ABI of the MI355X (gfx950) fused causal attention library.
  *
- * Operation. Causal scaled-dot-product softmax attention for transformer
- * training, forward and full backward, with grouped-query heads. The pages
+ * Operation. Causal (or, with causal = 0, bidirectional) scaled-dot-product
+ * softmax attention for transformer training, forward and full backward, with
+ * grouped-query heads. The pages
  * this follows describe it as fused flash attention, forward and backward,
  * whose probabilities never reach memory, stored in bf16 and accumulated in
  * fp32 ("Axis", Zyora Labs page, feature list), with query heads sharing kv
@@ -19,6 +20,9 @@
  *   dQ_i  = scale sum_j dS_ij K_j
  *   dK_j  = scale sum_{h in group g} sum_i dS_ij Q_i
  *   dV_j  = sum_{h in group g} sum_i P_ij dO_i
+ *
+ * With causal = 0 ("Axis" Rust/cuTile page, "Sudoku as an acceptance test":
+ * bidirectional multi-head attention) every "j <= i" above reads "j < L_b".
  *
  * The S x S matrices (scores, P, dS) are never written to device memory:
  * every call needs O(B * S * H * d) memory only.
