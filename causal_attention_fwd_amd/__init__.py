@@ -250,3 +250,36 @@ def backward(q, k, v, o, d_o, lse, scale: Optional[float] = None, seqlens=None, 
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, ws, int(causal))
     return dq, dk, dv, delta
+
+
+# ------------------------------------------------------------------ graph capture
+
+def capture_step(q, k, v, d_o, o, lse, delta, dq, dk, dv, scale: float, seqlens=None, causal: bool = True,
+                 workspace=None):
+    """Capture one training step of the path -- attn_fwd, attn_bwd_preprocess,
+    attn_bwd (its dK/dV and dQ launches) -- into a HIP graph (torch.cuda.CUDAGraph)
+    and return it; ``graph.replay()`` then reruns all four kernels with one
+    launch, on the tensors given here (refill them in place between replays).
+
+    The library is capture-safe: every entry point only enqueues kernels on the
+    current stream (no allocation, no synchronisation, no memset), so the graph
+    holds exactly the four kernel nodes. Shapes, pointers, scale, seqlens and
+    causal are fixed at capture time."""
+    torch = _torch()
+    cz = int(bool(causal))
+    # one eager run on the side stream first: loads the library, and checks the
+    # arguments outside the capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        attn_fwd(q, k, v, o, lse, scale, seqlens, cz)
+        attn_bwd_preprocess(o, d_o, delta, seqlens)
+        attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, workspace, cz)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        attn_fwd(q, k, v, o, lse, scale, seqlens, cz)
+        attn_bwd_preprocess(o, d_o, delta, seqlens)
+        attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, workspace, cz)
+    return graph
