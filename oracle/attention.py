@@ -46,7 +46,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["forward", "backward", "preprocess", "probabilities", "lengths"]
+__all__ = ["forward", "backward", "preprocess", "probabilities", "lengths", "decode"]
 
 
 def lengths(B: int, S: int, seqlens):
@@ -164,3 +164,52 @@ def backward(q, k, v, do, scale: float, seqlens=None, dtype=np.float64, causal: 
             dK[b, :L, g, :] += sc * (dS.T @ qh)
             dV[b, :L, g, :] += P.T @ doh
     return {"O": O, "LSE": LSE, "D": D, "dQ": dQ, "dK": dK, "dV": dV}
+
+
+def decode(q, k_cache, v_cache, scale: float, cache_lens=None, dtype=np.float64):
+    """Attention of a few new queries against a key/value cache (inference).
+
+    "AxiomLM" (PyPI page), "Key Features" and "Zero-Overhead Inference &
+    Streaming Generation": a state-cached key/value decode engine whose step
+    touches only the cache, with grouped kv heads ("Benchmarks": 4-head GQA to
+    shrink the cache). The pages give no formula; the plain reading: sequence
+    b holds L_b cached positions, the last Sq of which belong to the Sq new
+    queries (their keys and values are already in the cache), so query t sits
+    at position p = L_b - Sq + t and attends to the cached keys j <= p (causal
+    among the new queries; with Sq = 1 the query sees the whole cache):
+      s_j = scale * <q_t, k_j>,  LSE_t = ln sum_{j <= p} exp(s_j),
+      O_t = sum_{j <= p} exp(s_j - LSE_t) v_j.
+    A query with p < 0 (L_b < Sq - t) sees no key: O_t = 0, LSE_t = -inf.
+
+    q: [B, Sq, Hq, d]; k_cache, v_cache: [B, Smax, Hkv, d]; cache_lens:
+    length-B integers (clamped into [0, Smax]) or None (= Smax).
+    Returns (O [B, Sq, Hq, d], LSE [B, Hq, Sq]) in ``dtype``."""
+    q, k_cache, v_cache = np.asarray(q), np.asarray(k_cache), np.asarray(v_cache)
+    if q.ndim != 4 or k_cache.ndim != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, Sq, Hq, d] and the caches [B, Smax, Hkv, d]")
+    B, Sq, Hq, d = q.shape
+    Bc, Smax, Hkv, dc = k_cache.shape
+    if Bc != B or dc != d or Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("cache shape does not match q")
+    G = Hq // Hkv
+    lens = lengths(B, Smax, cache_lens)
+    O = np.zeros((B, Sq, Hq, d), dtype=dtype)
+    LSE = np.full((B, Hq, Sq), -np.inf, dtype=dtype)
+    sc = dtype(scale)
+    for b in range(B):
+        L = lens[b]
+        for h in range(Hq):
+            g = h // G
+            for t in range(Sq):
+                p = L - Sq + t
+                if p < 0:
+                    continue
+                kk = np.asarray(k_cache[b, :p + 1, g, :], dtype=dtype)
+                vv = np.asarray(v_cache[b, :p + 1, g, :], dtype=dtype)
+                s_ = (kk @ np.asarray(q[b, t, h, :], dtype=dtype)) * sc
+                m = np.max(s_)
+                e = np.exp(s_ - m)
+                den = np.sum(e)
+                O[b, t, h, :] = (e / den) @ vv
+                LSE[b, h, t] = m + np.log(den)
+    return O, LSE

@@ -12,6 +12,7 @@ import pytest
 
 import test_oracle as pins
 import test_oracle_noncausal as ncpins
+import test_oracle_decode as dpins
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
 
@@ -35,6 +36,11 @@ MUTATIONS = {
                                  "if causal else np.triu(np.ones((L, L), dtype=bool))"),
     "backward_ignores_causal_flag": ("P, lse = probabilities(qh, kh, scale, dtype, causal)",
                                      "P, lse = probabilities(qh, kh, scale, dtype)"),
+    # decode
+    "decode_position_off_by_one": ("p = L - Sq + t\n", "p = L - Sq + t - 1\n"),
+    "decode_new_queries_see_everything": ("p = L - Sq + t\n", "p = L - 1\n"),
+    "decode_gqa_modulo": ("            g = h // G\n            for t in range(Sq):", "            g = h % Hkv\n            for t in range(Sq):"),
+    "decode_unscaled": ("s_ = (kk @ np.asarray(q[b, t, h, :], dtype=dtype)) * sc", "s_ = (kk @ np.asarray(q[b, t, h, :], dtype=dtype))"),
 }
 
 
@@ -59,6 +65,9 @@ def _pins(orc):
     yield lambda: ncpins.test_matches_torch_sdpa_fp64(2, 64, 6, 2, 16, [64, 41], orc)
     yield lambda: ncpins.test_uniform_scores_full_mean(orc)
     yield lambda: ncpins.test_permutation_equivariance(orc)
+    yield lambda: dpins.test_equals_last_rows_of_causal_forward(3, 4, 33, 6, 2, 16, [33, 4, 9], orc)
+    yield lambda: dpins.test_matches_torch_sdpa_with_mask(orc)
+    yield lambda: dpins.test_hand_worked_values(orc)
 
 
 def test_unmutated_copy_passes_every_pin():
