@@ -21,6 +21,16 @@ with 20260000 + index (index 1..5 in the order above); draw Q, K, V, dO as
 fp32 standard normals in [B, S, H, d] order, scale dO by its stated sigma,
 round to bf16 (round-to-nearest-even), and for the padded workload draw the
 per-sequence valid lengths last with randint(S//2, S+1).
+
+Decode workloads (attention of a few new queries against a key/value cache):
+  * decode_llama1b - the llama1b heads (32 query, 8 kv, d 64), 32 sequences,
+                     cache capacity 8192, one new query each, cache lengths
+                     uniform in [Smax/4, Smax] (a serving batch of mixed
+                     lengths; the AxiomLM pages describe a cached-state decode
+                     engine for grouped-kv-head models without sizes)
+Recipe: generator seeded with 20260100 + index; draw q [B, Sq, Hq, d], then the
+k and v caches [B, Smax, Hkv, d] as fp32 standard normals, round to bf16, then
+the cache lengths with randint(lo, hi + 1).
 """
 from __future__ import annotations
 
@@ -130,3 +140,75 @@ def algorithmic_flops(w_or_shape, seqlens=None, causal: bool = True) -> dict:
     fwd = 4.0 * d * Hq * pairs
     return {"pairs_per_head": pairs, "fwd": fwd, "bwd": 2.5 * fwd, "total": 3.5 * fwd,
             "bwd_dkdv": 2.0 * fwd, "bwd_dq": 0.5 * fwd}
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    index: int
+    B: int
+    Sq: int
+    Smax: int
+    Hq: int
+    Hkv: int
+    d: int
+    len_lo: int
+    len_hi: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def seed(self) -> int:
+        return 20260100 + self.index
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "B": self.B, "Sq": self.Sq, "Smax": self.Smax, "Hq": self.Hq,
+                "Hkv": self.Hkv, "d": self.d, "cache_len_range": [self.len_lo, self.len_hi]}
+
+
+DECODE_WORKLOADS = {
+    "decode_llama1b": DecodeWorkload("decode_llama1b", 1, B=32, Sq=1, Smax=8192, Hq=32, Hkv=8, d=64,
+                                     len_lo=2048, len_hi=8192),
+}
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    q: torch.Tensor                  # [B, Sq, Hq, d] bf16 (CPU)
+    k_cache: torch.Tensor            # [B, Smax, Hkv, d] bf16
+    v_cache: torch.Tensor            # [B, Smax, Hkv, d] bf16
+    cache_lens: Optional[torch.Tensor]  # int32 [B] or None (= Smax)
+    scale: float
+
+
+def make_decode_inputs(B: int, Sq: int, Smax: int, Hq: int, Hkv: int, d: int, seed: int,
+                       len_range: Optional[tuple] = None, scale: Optional[float] = None) -> DecodeInputs:
+    """Draw bf16-rounded N(0,1) decode inputs; ``len_range`` (lo, hi inclusive)
+    draws per-sequence cache lengths, None leaves every cache full."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    q = torch.randn(B, Sq, Hq, d, generator=gen, dtype=torch.float32)
+    k = torch.randn(B, Smax, Hkv, d, generator=gen, dtype=torch.float32)
+    v = torch.randn(B, Smax, Hkv, d, generator=gen, dtype=torch.float32)
+    lens = None
+    if len_range is not None:
+        lo, hi = len_range
+        lens = torch.randint(lo, hi + 1, (B,), generator=gen, dtype=torch.int64).to(torch.int32)
+    return DecodeInputs(q=q.to(torch.bfloat16), k_cache=k.to(torch.bfloat16), v_cache=v.to(torch.bfloat16),
+                        cache_lens=lens, scale=(1.0 / math.sqrt(d)) if scale is None else float(scale))
+
+
+def decode_workload_inputs(w: DecodeWorkload) -> DecodeInputs:
+    return make_decode_inputs(w.B, w.Sq, w.Smax, w.Hq, w.Hkv, w.d, w.seed, (w.len_lo, w.len_hi))
+
+
+def decode_bytes(B: int, Sq: int, Smax: int, Hq: int, Hkv: int, d: int, cache_lens=None) -> dict:
+    """Algorithmic HBM bytes of one decode call: every valid cached key and
+    value row read once (bf16), the queries read and the outputs written once
+    (bf16), one fp32 LSE per query row. Pure counting."""
+    lens = [Smax] * B if cache_lens is None else [min(max(int(L), 0), Smax) for L in cache_lens.tolist()]
+    cache = sum(lens) * Hkv * d * 2 * 2
+    qo = B * Sq * Hq * d * 2 * 2 + B * Sq * Hq * 4
+    return {"cache": cache, "q_o_lse": qo, "total": cache + qo}

@@ -17,6 +17,9 @@ Other modes (measurement tooling, used under rocprofv3):
     --pmc-summary DIR ...    turn rocprofv3 --pmc outputs into profiles/*_pmc.txt
     --trace-summary DIR      turn a rocprofv3 --kernel-trace --stats run into profiles/*_trace.txt
     --sq-summary DIR ...     turn rocprofv3 --pmc runs of SQ counters into profiles/*_sq.txt
+    --decode                 decode attention against a key/value cache instead
+                             (workload decode_llama1b; HBM GB/s, one step = one
+                             attn_decode call)
 """
 from __future__ import annotations
 
@@ -36,7 +39,10 @@ METRIC = "causal bf16 attention fwd+bwd TFLOP/s and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak (2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 KERNEL_SOURCES = ["causal_attention_fwd_amd/csrc/attn_kernels.hip", "causal_attention_fwd_amd/csrc/attn_common.h"]
-KERNEL_NAMES = {"fwd": "fwd_kernel", "pre": "preprocess_kernel", "dkdv": "bwd_dkdv_kernel", "dq": "bwd_dq_kernel"}
+KERNEL_NAMES = {"fwd": "fwd_kernel", "pre": "preprocess_kernel", "dkdv": "bwd_dkdv_kernel", "dq": "bwd_dq_kernel",
+                "dsplit": "decode_split_kernel", "dmerge": "decode_merge_kernel"}
+DECODE_METRIC = "decode attention over a bf16 key/value cache, HBM GB/s (algorithmic bytes) and % of 8 TB/s"
+MALL_BYTES = 256 << 20         # MI355X last-level (Infinity) cache
 
 
 def log(msg):
@@ -168,7 +174,9 @@ def sq_summary(args):
 def trace_summary(args):
     """profiles/<kernel>_<workload>_trace.txt from a rocprofv3 --kernel-trace --stats run."""
     import csv
-    from attn_workloads import WORKLOADS, algorithmic_flops, workload_inputs
+    from attn_workloads import DECODE_WORKLOADS, WORKLOADS, algorithmic_flops, workload_inputs
+    if args.workload in DECODE_WORKLOADS:
+        return decode_trace_summary(args)
     w = WORKLOADS[args.workload]
     seqlens = workload_inputs(w).seqlens if w.padded else None
     fl = algorithmic_flops(w, seqlens)
@@ -199,6 +207,36 @@ def trace_summary(args):
             else:
                 out.write(f"algorithmic_bytes_per_launch: {pre_bytes:.0f}\n")
                 out.write(f"achieved_gbs_at_average: {pre_bytes / (avg_us * 1e-6) / 1e9:.1f}\n")
+        log(f"wrote {path}: {avg_us:.1f} us")
+
+
+def decode_trace_summary(args):
+    import csv
+    from attn_workloads import DECODE_WORKLOADS, decode_bytes, decode_workload_inputs
+    w = DECODE_WORKLOADS[args.workload]
+    nb = decode_bytes(w.B, w.Sq, w.Smax, w.Hq, w.Hkv, w.d, decode_workload_inputs(w).cache_lens)
+    alg = {"decode_split_kernel": nb["cache"] + w.B * w.Sq * w.Hq * w.d * 2,
+           "decode_merge_kernel": w.B * w.Sq * w.Hq * (w.d * 2 + 4)}
+    files = glob.glob(os.path.join(args.trace_summary, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no kernel_stats.csv under {args.trace_summary}")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for row in csv.DictReader(open(files[0])):
+        kname = next((k for k in alg if k in row["Name"]), None)
+        if kname is None:
+            continue
+        avg_us = float(row["AverageNs"]) / 1e3
+        path = os.path.join(ROOT, "profiles", f"{kname}_{w.name}_trace.txt")
+        with open(path, "w") as out:
+            out.write(f"# rocprofv3 kernel-trace summary: {kname} on workload {w.name} {w.describe()}\n")
+            out.write(f"# command: {args.pmc_command}\n")
+            out.write(f"kernel: {row['Name']}\n")
+            out.write(f"kernel_source_sha256_16: {kernel_source_sha()}\n")
+            out.write(f"calls: {row['Calls']}\n")
+            out.write(f"average_us: {avg_us:.2f}\nmin_us: {float(row['MinNs']) / 1e3:.2f}\n"
+                      f"max_us: {float(row['MaxNs']) / 1e3:.2f}\n")
+            out.write(f"algorithmic_bytes_per_launch: {alg[kname]:.0f}\n")
+            out.write(f"achieved_gbs_at_average: {alg[kname] / (avg_us * 1e-6) / 1e9:.1f}\n")
         log(f"wrote {path}: {avg_us:.1f} us")
 
 
@@ -357,12 +395,111 @@ def run(args):
     print(json.dumps(result), flush=True)
 
 
+def decode_cpu_baseline(w, inp, budget_s: float):
+    """The oracle (fp32 mode, untuned) on whole sequences of the decode workload
+    until about `budget_s` seconds of CPU work have been spent; priced in the
+    same algorithmic bytes as the GPU figure."""
+    import numpy as np
+    import oracle
+    from attn_workloads import decode_bytes
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    q = inp.q.float().numpy()
+    k, v = inp.k_cache.float().numpy(), inp.v_cache.float().numpy()
+    lens = inp.cache_lens.numpy() if inp.cache_lens is not None else None
+    done, nbytes, t0 = 0, 0.0, time.perf_counter()
+    for b in range(w.B):
+        lb = None if lens is None else lens[b:b + 1]
+        oracle.decode(q[b:b + 1], k[b:b + 1], v[b:b + 1], inp.scale, lb, dtype=np.float32)
+        done += 1
+        nbytes += decode_bytes(1, w.Sq, w.Smax, w.Hq, w.Hkv, w.d, None if lb is None else inp.cache_lens[b:b + 1])["total"]
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {w.B} sequences of {w.name}, numpy fp32, {dt:.1f} s"}
+
+
+def run_decode(args):
+    """One step = one attn_decode call (split-KV partials, then their merge)
+    over the resident cache. Several copies of the inputs are rotated so that
+    a call never finds its cache in the last-level cache from the call before
+    (serving walks a different layer's cache each call)."""
+    import torch
+    import causal_attention_fwd_amd as attn
+    from attn_workloads import DECODE_WORKLOADS, decode_bytes, decode_workload_inputs
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    attn.load_library()
+    w = DECODE_WORKLOADS[args.workload]
+    inp = decode_workload_inputs(w)
+    dev = torch.device("cuda")
+    alloc = 2 * inp.k_cache.numel() * 2
+    copies = max(2, math.ceil(3 * MALL_BYTES / alloc) + 1)
+    lens = inp.cache_lens.to(dev) if inp.cache_lens is not None else None
+    sets = []
+    for _ in range(copies):
+        q, k, v = (x.to(dev).contiguous() for x in (inp.q, inp.k_cache, inp.v_cache))
+        sets.append((q, k, v, torch.empty_like(q), torch.empty(w.B, w.Hq, w.Sq, device=dev)))
+    ws = torch.empty(max(16, attn.attn_decode_workspace_bytes(w.B, w.Sq, w.Smax, w.Hq, w.Hkv, w.d)),
+                     dtype=torch.uint8, device=dev)
+    nb = decode_bytes(w.B, w.Sq, w.Smax, w.Hq, w.Hkv, w.d, inp.cache_lens)
+
+    def step(i, ev=None):
+        q, k, v, o, lse = sets[i % copies]
+        if ev is not None:
+            ev[0].record()
+        attn.attn_decode(q, k, v, o, lse, inp.scale, lens, ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_call = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    gbs = nb["total"] / (ms_step * 1e-3) / 1e9
+    achieved = nb["total"] / (ms_call * 1e-3) / 1e9
+    t_split, t_merge = read_traffic("dsplit", w.name), read_traffic("dmerge", w.name)
+    roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": (t_split + t_merge) if (t_split is not None and t_merge is not None) else None,
+            "kernel": "decode_split_kernel+decode_merge_kernel", "ms_per_launch": ms_call}
+    result = {
+        "metric": DECODE_METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": dict(w.describe(), launch="eager", input_copies_rotated=copies,
+                       algorithmic_bytes_per_step=nb["total"]),
+        "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = decode_cpu_baseline(w, inp, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama1b")
+    ap.add_argument("--workload", default=None, help="llama1b (default), or decode_llama1b with --decode")
+    ap.add_argument("--decode", action="store_true", help="decode attention against a key/value cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work in cpu_baseline")
     ap.add_argument("--graph", action="store_true",
@@ -382,6 +519,8 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path (each GPU would run its own "
               "(sequence, kv-head) units independently); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.workload is None:
+        args.workload = "decode_llama1b" if args.decode else "llama1b"
     if args.pmc_summary:
         pmc_summary(args)
     elif args.trace_summary:
@@ -390,6 +529,8 @@ def main():
         sq_summary(args)
     elif args.copy_calibration:
         copy_calibration(args)
+    elif args.decode:
+        run_decode(args)
     else:
         run(args)
 

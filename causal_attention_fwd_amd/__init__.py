@@ -12,8 +12,10 @@ Entry points (same names as the C ABI):
     attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens=None, workspace=None)
     attn_bwd_dkdv(q, k, v, d_o, lse, delta, dk, dv, scale, seqlens=None)
     attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale, seqlens=None)
+    attn_decode_workspace_bytes(B, Sq, Smax, Hq, Hkv, d)
+    attn_decode(q, k_cache, v_cache, o, lse, scale, cache_lens=None, workspace=None)
     attn_status_string(code)
-and allocating conveniences `forward(...)`, `backward(...)`.
+and allocating conveniences `forward(...)`, `backward(...)`, `decode(...)`.
 """
 from __future__ import annotations
 
@@ -23,7 +25,8 @@ import os
 from typing import Optional
 
 __all__ = ["attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
-           "attn_bwd_dkdv", "attn_bwd_dq", "attn_status_string", "forward", "backward", "AttnError", "library_path", "load_library",
+           "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode_workspace_bytes", "attn_decode", "attn_status_string",
+           "forward", "backward", "decode", "capture_step", "AttnError", "library_path", "load_library",
            "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +37,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3:
 
 # The symbols include/attn.h declares.
 EXPORTED = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_dkdv",
-            "attn_bwd_dq", "attn_status_string")
+            "attn_bwd_dq", "attn_decode_workspace_bytes", "attn_decode", "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -47,6 +50,12 @@ class AttnShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("heads_q", ctypes.c_int32),
                 ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("causal", ctypes.c_int32), ("seqlens", ctypes.c_void_p)]
+
+
+class AttnDecodeShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("cache_len", ctypes.c_int32),
+                ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("cache_lens", ctypes.c_void_p)]
 
 
 def library_path() -> str:
@@ -79,6 +88,11 @@ def load_library():
     lib.attn_bwd_dkdv.restype = i32
     lib.attn_bwd_dq.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.attn_bwd_dq.restype = i32
+    dshp = ctypes.POINTER(AttnDecodeShape)
+    lib.attn_decode_workspace_bytes.argtypes = [dshp]
+    lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_decode.argtypes = [dshp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.attn_decode.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -221,6 +235,55 @@ def attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale: float, seqlens=None, causal
     ptrs += [_check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d))]
     _call(load_library().attn_bwd_dq, "attn_bwd_dq", ctypes.byref(shape),
           *[ctypes.c_void_p(p) for p in ptrs], _stream())
+
+
+# ------------------------------------------------------------------ decode
+
+def make_decode_shape(B: int, Sq: int, Smax: int, Hq: int, Hkv: int, d: int, scale: float,
+                      cache_lens_ptr: Optional[int] = None) -> AttnDecodeShape:
+    return AttnDecodeShape(int(B), int(Sq), int(Smax), int(Hq), int(Hkv), int(d), float(scale),
+                           ctypes.c_void_p(cache_lens_ptr) if cache_lens_ptr else None)
+
+
+def attn_decode_workspace_bytes(B: int, Sq: int, Smax: int, Hq: int, Hkv: int, d: int) -> int:
+    shape = make_decode_shape(B, Sq, Smax, Hq, Hkv, d, 1.0 / math.sqrt(d))
+    return int(load_library().attn_decode_workspace_bytes(ctypes.byref(shape)))
+
+
+def attn_decode(q, k_cache, v_cache, o, lse, scale: float, cache_lens=None, workspace=None):
+    """O, LSE <- decode attention of q [B,Sq,Hq,d] against the caches [B,Smax,Hkv,d]."""
+    torch = _torch()
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q must be [B,Sq,Hq,d] and the caches [B,Smax,Hkv,d]")
+    B, Sq, Hq, d = q.shape
+    Smax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    lens = _check_gpu("cache_lens", cache_lens, torch.int32, (B,)) if cache_lens is not None else None
+    shape = make_decode_shape(B, Sq, Smax, Hq, Hkv, d, scale, lens)
+    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, Sq, Hq, d)),
+            _check_gpu("k_cache", k_cache, torch.bfloat16, (B, Smax, Hkv, d)),
+            _check_gpu("v_cache", v_cache, torch.bfloat16, (B, Smax, Hkv, d)),
+            _check_gpu("o", o, torch.bfloat16, (B, Sq, Hq, d)),
+            _check_gpu("lse", lse, torch.float32, (B, Hq, Sq))]
+    ws, nbytes = None, 0
+    if workspace is not None:
+        ws = _check_gpu("workspace", workspace, torch.uint8)
+        nbytes = workspace.numel()
+    _call(load_library().attn_decode, "attn_decode", ctypes.byref(shape), *[ctypes.c_void_p(p) for p in ptrs],
+          ctypes.c_void_p(ws), ctypes.c_size_t(nbytes), _stream())
+
+
+def decode(q, k_cache, v_cache, scale: Optional[float] = None, cache_lens=None):
+    """Returns (O, LSE) of decode attention as new tensors (allocates the workspace)."""
+    torch = _torch()
+    B, Sq, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    need = attn_decode_workspace_bytes(B, Sq, k_cache.shape[1], Hq, k_cache.shape[2], d)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    attn_decode(q, k_cache, v_cache, o, lse, scale, cache_lens, ws)
+    return o, lse
 
 
 # ------------------------------------------------------------------ allocating conveniences

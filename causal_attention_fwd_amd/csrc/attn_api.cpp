@@ -35,6 +35,32 @@ attn_status check_shape(const attn_shape* s, attn::Problem* pr) {
   return ATTN_OK;
 }
 
+attn_status check_decode_shape(const attn_decode_shape* s, attn::DecodeProblem* pr) {
+  if (!s) return ATTN_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->q_len < 1 || s->cache_len < 1 || s->heads_q < 1 || s->heads_kv < 1)
+    return ATTN_ERR_INVALID_ARG;
+  if (s->heads_q % s->heads_kv != 0) return ATTN_ERR_INVALID_ARG;
+  if (!(isfinite(s->scale) && s->scale > 0.f)) return ATTN_ERR_INVALID_ARG;
+  if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  // one 32-row block of query rows per kv head
+  if ((int64_t)s->q_len * (s->heads_q / s->heads_kv) > 32) return ATTN_ERR_UNSUPPORTED;
+  if (s->cache_lens && (reinterpret_cast<uintptr_t>(s->cache_lens) & 3u) != 0) return ATTN_ERR_MISALIGNED;
+  // 32-bit tile offsets (as for the training path) and grid size
+  if ((int64_t)s->heads_kv * s->head_dim > (int64_t)1 << 22) return ATTN_ERR_UNSUPPORTED;
+  pr->B = s->batch;
+  pr->Sq = s->q_len;
+  pr->Smax = s->cache_len;
+  pr->Hq = s->heads_q;
+  pr->Hkv = s->heads_kv;
+  pr->d = s->head_dim;
+  pr->scale = s->scale;
+  pr->cache_lens = s->cache_lens;
+  const attn::DecodePlan plan = attn::plan_decode(*pr);
+  if ((int64_t)s->batch * s->heads_kv * plan.nsplit > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  if (((int64_t)s->batch * s->heads_q * s->q_len + 3) / 4 > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
 attn_status check_ptrs(std::initializer_list<const void*> ptrs) {
   for (const void* p : ptrs)
     if (!p) return ATTN_ERR_INVALID_ARG;
@@ -110,13 +136,31 @@ attn_status attn_bwd(const attn_shape* shape, const void* q, const void* k, cons
   return from_hip(attn::launch_bwd_dq(pr, q, k, v, d_o, lse, delta, dq, stream));
 }
 
+size_t attn_decode_workspace_bytes(const attn_decode_shape* shape) {
+  attn::DecodeProblem pr;
+  if (check_decode_shape(shape, &pr) != ATTN_OK) return 0;
+  return attn::plan_decode(pr).workspace_bytes;
+}
+
+attn_status attn_decode(const attn_decode_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                        void* o, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  attn::DecodeProblem pr;
+  attn_status st = check_decode_shape(shape, &pr);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k_cache, v_cache, o, lse});
+  if (st != ATTN_OK) return st;
+  const attn::DecodePlan plan = attn::plan_decode(pr);
+  if (workspace_bytes < plan.workspace_bytes || !workspace || !aligned16(workspace)) return ATTN_ERR_WORKSPACE;
+  return from_hip(attn::launch_decode(pr, plan, q, k_cache, v_cache, o, lse, workspace, stream));
+}
+
 const char* attn_status_string(attn_status status) {
   switch (status) {
     case ATTN_OK: return "ATTN_OK";
     case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: null pointer, bad size, Hq % Hkv != 0 or bad scale";
     case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: head_dim must be 64 or 128";
     case ATTN_ERR_MISALIGNED: return "ATTN_ERR_MISALIGNED: tensor pointers must be 16-byte aligned";
-    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace smaller than attn_bwd_workspace_bytes()";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing, misaligned or smaller than required";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: the HIP runtime reported a launch error";
   }
   return "ATTN_ERR_UNKNOWN";

@@ -25,6 +25,8 @@
 //    (bidirectional attention, causal = 0, skips and masks only the padding);
 //  * the softmax runs in base 2 with scale*log2(e) folded into one multiply;
 //    LSE is exported as a natural log.
+#include <algorithm>
+
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -788,8 +790,148 @@ void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Launchers
+// Decode. Sq new queries per sequence (the last Sq cached positions) against a
+// [B, Smax, Hkv, d] key/value cache. The cache of one (sequence, kv head) is
+// cut into splits; one wave (a one-wave workgroup, no barrier partners) takes
+// one split and runs the forward's tile routine over its 64-key tiles with the
+// G*Sq query rows of the kv group as its 32-row block (row r = head r / Sq,
+// new query r % Sq; rows past G*Sq are empty). It writes the split's
+// normalised partial O (fp32) and LSE; the merge kernel combines the splits.
+// The work is bound by streaming the cache from HBM.
 // ----------------------------------------------------------------------------
+struct DecArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const int32_t* lens;
+  float* ws_o;    // [B, Hq, Sq, nsplit, D]
+  float* ws_lse;  // [B, Hq, Sq, nsplit]
+  bf16* o;        // [B, Sq, Hq, D]
+  float* lse;     // [B, Hq, Sq]
+  int B, Sq, Smax, Hq, Hkv, nsplit, chunk;
+  float scale;
+};
+
+template <int D, int OCC>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void decode_split_kernel(DecArgs a) {
+  constexpr int BN = 64;
+  constexpr int KK = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int KVT = TileLayout<D>::template elems<BN>();
+  __shared__ __attribute__((aligned(16))) bf16 sK0[KVT], sV0[KVT], sK1[KVT], sV1[KVT];
+
+  const int lane = threadIdx.x;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int s = blockIdx.x % a.nsplit;
+  const int unit = blockIdx.x / a.nsplit;  // b * Hkv + hkv
+  const int b = unit / a.Hkv;
+  const int hkv = unit - b * a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int L = valid_len(a.lens, b, a.Smax);
+  const int64_t ks = (int64_t)a.Hkv * D;
+  const bf16* Kb = a.k + ((int64_t)b * a.Smax * a.Hkv + hkv) * D;
+  const bf16* Vb = a.v + ((int64_t)b * a.Smax * a.Hkv + hkv) * D;
+
+  // the lane's query row: head hkv*G + r / Sq, new query t = r % Sq at cache
+  // position L - Sq + t, which sees keys 0 .. L - Sq + t
+  const int r = l32;
+  const bool row_ok = r < G * a.Sq;
+  const int hh = row_ok ? r / a.Sq : 0;
+  const int t = row_ok ? r - hh * a.Sq : 0;
+  const int h = hkv * G + hh;
+  const int jmax = row_ok ? L - a.Sq + t : -1;  // last visible key (< 0: none)
+
+  FwdState<D, 1> st;
+  const bf16* qrow = a.q + (((int64_t)b * a.Sq + t) * a.Hq + h) * D;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    st.qf[0][kk] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + g * 8) : zero_bf16x8();
+  st.mu[0] = kNegInf;
+  st.lsum[0] = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) st.oacc[dt][0] = zero16();
+  wait_vmem();
+
+  const float c = a.scale * kLog2e;
+  const int k0 = s * a.chunk;                          // the split's first key
+  const int kend = min(k0 + a.chunk, L);               // and one past its last
+  const int ntiles = kend > k0 ? (kend - k0 + BN - 1) / BN : 0;
+  const int first_last = L - a.Sq;                     // smallest last-visible key of the rows
+  const KVBuf b0{sK0, sV0, 0}, b1{sK1, sV1, 1};
+  auto fetch = [&](int kt, const KVBuf& buf) {
+    tile_load_lds<BN, D, 1>(Kb, ks, k0 + kt * BN, kend, buf.k, 0, lane);
+    tile_load_lds<BN, D, 1>(Vb, ks, k0 + kt * BN, kend, buf.v, 0, lane);
+  };
+  auto compute = [&](int kt, const KVBuf& buf) {
+    const int j0 = k0 + kt * BN;
+    if (j0 + BN - 1 > first_last || j0 + BN > kend) {
+      const int lim[1] = {min(jmax, kend - 1) - j0 - g * 4};
+      fwd_tile<D, 1, true>(st, buf.k, buf.v, lane, c, lim);
+    } else {
+      const int lim[1] = {};
+      fwd_tile<D, 1, false>(st, buf.k, buf.v, lane, c, lim);
+    }
+  };
+  tile_pipeline(ntiles, b0, b1, fetch, [](int, const KVBuf&) {}, compute);
+
+  // partial result of this split: O / l (fp32) and LSE = mu*scale + ln l
+  const float lt = xhalf_sum(st.lsum[0]);
+  if (row_ok) {
+    const int64_t row = ((int64_t)b * a.Hq + h) * a.Sq + t;
+    const bool any = lt > 0.f;
+    const float inv = any ? 1.f / lt : 0.f;
+    float* wo = a.ws_o + (row * a.nsplit + s) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float4 ov;
+        ov.x = st.oacc[dt][0][rr * 4 + 0] * inv;
+        ov.y = st.oacc[dt][0][rr * 4 + 1] * inv;
+        ov.z = st.oacc[dt][0][rr * 4 + 2] * inv;
+        ov.w = st.oacc[dt][0][rr * 4 + 3] * inv;
+        *reinterpret_cast<float4*>(wo + dt * 32 + rr * 8 + g * 4) = ov;
+      }
+    if (g == 0) a.ws_lse[row * a.nsplit + s] = any ? (st.mu[0] * c + __log2f(lt)) * kLn2 : kNegInf;
+  }
+}
+
+// Merge: one wave per (sequence, head, new query); LSE = ln sum_s exp(LSE_s),
+// O = sum_s exp(LSE_s - LSE) O_s, rounded to bf16; lanes run over d.
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecArgs a) {
+  constexpr int PER = D / 64;  // elements per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * Hq + h) * Sq + t
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+  if (row >= rows) return;
+  const float* wl = a.ws_lse + row * a.nsplit;
+  float m = kNegInf;
+  for (int s = 0; s < a.nsplit; ++s) m = fmaxf(m, wl[s]);
+  float acc[PER] = {};
+  float den = 0.f;
+  if (m != kNegInf) {
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float w = __expf(wl[s] - m);  // 0 for empty splits (-inf)
+      den += w;
+      const float* wo = a.ws_o + (row * a.nsplit + s) * D;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += w * wo[e * 64 + lane];
+    }
+  }
+  const int t = (int)(row % a.Sq);
+  const int64_t bh = row / a.Sq;
+  const int h = (int)(bh % a.Hq);
+  const int b = (int)(bh / a.Hq);
+  bf16* orow = a.o + (((int64_t)b * a.Sq + t) * a.Hq + h) * D;
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) orow[e * 64 + lane] = (bf16)(acc[e] * inv);
+  if (lane == 0) a.lse[bh * a.Sq + t] = den > 0.f ? m + __logf(den) : kNegInf;
+}
+
 namespace {
 
 // Per head dimension: 32-row tiles per wave (NT: query rows in the forward and
@@ -917,6 +1059,44 @@ int64_t max_grid(const Problem& pr) {
   int64_t m = nb * pr.B * pr.Hq;
   const int64_t pre = ((int64_t)pr.B * pr.S * pr.Hq + 15) / 16;
   return m > pre ? m : pre;
+}
+
+DecodePlan plan_decode(const DecodeProblem& pr) {
+  // enough waves to cover every SIMD a few times over, but no split shorter
+  // than one 64-key tile
+  const int64_t units = (int64_t)pr.B * pr.Hkv;
+  const int tiles = (pr.Smax + 63) / 64;
+  const int64_t target = 2048;
+  int nsplit = (int)std::min<int64_t>(tiles, std::max<int64_t>(1, (target + units - 1) / units));
+  const int per = (tiles + nsplit - 1) / nsplit;
+  nsplit = (tiles + per - 1) / per;
+  DecodePlan plan;
+  plan.nsplit = nsplit;
+  plan.chunk = per * 64;
+  const size_t rows = (size_t)pr.B * pr.Hq * pr.Sq;
+  const size_t o_bytes = rows * nsplit * pr.d * sizeof(float);
+  plan.workspace_bytes = o_bytes + ((rows * nsplit * sizeof(float) + 255) / 256) * 256;
+  return plan;
+}
+
+hipError_t launch_decode(const DecodeProblem& pr, const DecodePlan& plan, const void* q, const void* k_cache,
+                         const void* v_cache, void* o, float* lse, void* workspace, hipStream_t stream) {
+  const size_t rows = (size_t)pr.B * pr.Hq * pr.Sq;
+  DecArgs a{(const bf16*)q, (const bf16*)k_cache, (const bf16*)v_cache, pr.cache_lens,
+            reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ((rows * plan.nsplit * sizeof(float) + 255) / 256) * 256),
+            reinterpret_cast<float*>(workspace), (bf16*)o, lse, pr.B, pr.Sq, pr.Smax, pr.Hq, pr.Hkv,
+            plan.nsplit, plan.chunk, pr.scale};
+  const int64_t splits = (int64_t)pr.B * pr.Hkv * plan.nsplit;
+  const int64_t merge_blocks = ((int64_t)rows + 3) / 4;
+  hipError_t e;
+  if (pr.d == 64) {
+    e = launch((const void*)&decode_split_kernel<64, 2>, splits, a, stream, 64);
+    if (e == hipSuccess) e = launch((const void*)&decode_merge_kernel<64>, merge_blocks, a, stream);
+  } else {
+    e = launch((const void*)&decode_split_kernel<128, 1>, splits, a, stream, 64);
+    if (e == hipSuccess) e = launch((const void*)&decode_merge_kernel<128>, merge_blocks, a, stream);
+  }
+  return e;
 }
 
 }  // namespace attn

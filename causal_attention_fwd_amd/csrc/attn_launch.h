@@ -26,4 +26,22 @@ hipError_t launch_bwd_dq(const Problem& pr, const void* q, const void* k, const 
 // hardware's 2^31-1 workgroup limit by the API layer).
 int64_t max_grid(const Problem& pr);
 
+// Decode: Sq new queries per sequence against a [B, Smax, Hkv, d] key/value cache.
+struct DecodeProblem {
+  int B, Sq, Smax, Hq, Hkv, d;
+  float scale;
+  const int32_t* cache_lens;  // device int32[B] or nullptr (= Smax)
+};
+
+// How the cache of one (sequence, kv head) is cut into splits: nsplit chunks of
+// `chunk` positions (a multiple of 64), each handled by one wave; a merge pass
+// combines the splits' partial results by log-sum-exp.
+struct DecodePlan {
+  int nsplit, chunk;
+  size_t workspace_bytes;  // partial O (fp32) and LSE of every split
+};
+DecodePlan plan_decode(const DecodeProblem& pr);
+hipError_t launch_decode(const DecodeProblem& pr, const DecodePlan& plan, const void* q, const void* k_cache,
+                         const void* v_cache, void* o, float* lse, void* workspace, hipStream_t stream);
+
 }  // namespace attn

@@ -136,6 +136,49 @@ attn_status attn_bwd_dq(const attn_shape* shape, const void* q, const void* k, c
                         const void* d_o, const float* lse, const float* delta,
                         void* dq, hipStream_t stream);
 
+/*
+ * Decode: attention of Sq new queries per sequence against a key/value cache
+ * (inference). "AxiomLM" (PyPI page), "Key Features" and "Zero-Overhead
+ * Inference & Streaming Generation": a state-cached key/value decode engine,
+ * with grouped kv heads ("Benchmarks": 4-head GQA shrinks the cache).
+ * Sequence b holds L_b valid cache positions; the last Sq of them belong to
+ * the new queries (their keys/values are already in the cache), so query t
+ * sits at position p = L_b - Sq + t and attends to cached keys j <= p:
+ *   LSE_t = ln sum_{j <= p} exp(scale <q_t, k_j>),
+ *   O_t   = sum_{j <= p} exp(scale <q_t, k_j> - LSE_t) v_j,
+ * with O_t = 0 and LSE_t = -inf when p < 0 (the query sees no key).
+ */
+typedef struct attn_decode_shape {
+  int32_t batch;       /* B >= 1 */
+  int32_t q_len;       /* Sq >= 1 new queries per sequence; Sq * (Hq / Hkv) <= 32 */
+  int32_t cache_len;   /* Smax >= 1: cache capacity (positions) per sequence */
+  int32_t heads_q;     /* Hq >= 1, a multiple of heads_kv */
+  int32_t heads_kv;    /* Hkv >= 1 */
+  int32_t head_dim;    /* d: 64 or 128 */
+  float scale;         /* finite and > 0 */
+  /* Optional DEVICE int32[B]: valid cache length L_b of each sequence, clamped
+     into [0, Smax] on the device; NULL means L_b = Smax. Positions >= L_b may
+     hold any bits (including NaN). */
+  const int32_t* cache_lens;
+} attn_decode_shape;
+
+/*
+ * Bytes of device workspace attn_decode needs (the per-split partial outputs:
+ * B * Hq * Sq * nsplit * (d + 1) floats, nsplit <= ceil(Smax / 64)). Returns 0
+ * for a NULL or invalid shape.
+ */
+size_t attn_decode_workspace_bytes(const attn_decode_shape* shape);
+
+/*
+ * q [B,Sq,Hq,d], k_cache/v_cache [B,Smax,Hkv,d], o [B,Sq,Hq,d] bf16; lse
+ * [B,Hq,Sq] fp32; workspace: caller-owned device memory of at least
+ * attn_decode_workspace_bytes() bytes, 16-byte aligned (ATTN_ERR_WORKSPACE
+ * otherwise), overwritten by the call and free again when the stream has run
+ * it. Two launches (per-split partials, then their merge); deterministic.
+ */
+attn_status attn_decode(const attn_decode_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                        void* o, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* attn_status_string(attn_status status);
 

@@ -167,3 +167,57 @@ def test_product_path_never_uses_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+# ------------------------------------------------------------------ decode
+
+def _dshape(**kw):
+    base = dict(B=2, Sq=1, Smax=256, Hq=8, Hkv=2, d=64, scale=0.125, lens_ptr=None)
+    base.update(kw)
+    return attn.make_decode_shape(base["B"], base["Sq"], base["Smax"], base["Hq"], base["Hkv"], base["d"],
+                                  base["scale"], base["lens_ptr"])
+
+
+def _dec(lib, shape, ptrs=(GOOD,) * 5, ws=None, ws_bytes=0):
+    return lib.attn_decode(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs],
+                           P(ws), ctypes.c_size_t(ws_bytes), P(0))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 1), (dict(Sq=0), 1), (dict(Smax=0), 1), (dict(Hq=0), 1), (dict(Hkv=0), 1), (dict(Smax=-3), 1),
+    (dict(Hq=6, Hkv=4), 1), (dict(scale=float("nan")), 1), (dict(scale=0.0), 1), (dict(scale=-1.0), 1),
+    (dict(d=32), 2), (dict(d=96), 2), (dict(Sq=5, Hq=16, Hkv=2), 2), (dict(Sq=1, Hq=33, Hkv=1), 2),
+    (dict(lens_ptr=GOOD + 2), 3), (dict(Hq=2 ** 16, Hkv=2 ** 16, d=128), 2),
+])
+def test_decode_invalid_shapes_rejected(lib, kw, code):
+    shape = _dshape(**kw)
+    assert _dec(lib, shape, ws=GOOD, ws_bytes=1 << 40) == code
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(shape)) == 0
+
+
+def test_decode_pointers_and_workspace(lib):
+    assert _dec(lib, None) == 1
+    assert lib.attn_decode_workspace_bytes(None) == 0
+    shape = _dshape()
+    need = lib.attn_decode_workspace_bytes(ctypes.byref(shape))
+    assert need > 0
+    for i in range(5):
+        ptrs = [GOOD] * 5
+        ptrs[i] = 0
+        assert _dec(lib, shape, ptrs, GOOD, need) == 1
+        ptrs[i] = ODD
+        assert _dec(lib, shape, ptrs, GOOD, need) == 3
+    assert _dec(lib, shape, ws=None, ws_bytes=need) == 4
+    assert _dec(lib, shape, ws=GOOD, ws_bytes=need - 1) == 4
+    assert _dec(lib, shape, ws=ODD, ws_bytes=need) == 4
+
+
+def test_decode_workspace_bytes_grows_with_splits_not_cache(lib):
+    # one fp32 partial row (d values + LSE) per (query row, split); splits are
+    # capped, so the workspace stays bounded as the cache grows
+    small = lib.attn_decode_workspace_bytes(ctypes.byref(_dshape(B=1, Smax=64, Hq=32, Hkv=8)))
+    assert small == 32 * 64 * 4 + 256
+    for Smax in (4096, 65536, 1 << 20):
+        ws = lib.attn_decode_workspace_bytes(ctypes.byref(_dshape(B=1, Smax=Smax, Hq=32, Hkv=8)))
+        splits = -(-2048 // 8)
+        assert ws <= 32 * splits * (64 * 4 + 4) + 256
