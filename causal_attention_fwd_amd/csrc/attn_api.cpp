@@ -55,8 +55,8 @@ attn_status check_decode_shape(const attn_decode_shape* s, attn::DecodeProblem* 
   pr->d = s->head_dim;
   pr->scale = s->scale;
   pr->cache_lens = s->cache_lens;
-  const attn::DecodePlan plan = attn::plan_decode(*pr);
-  if ((int64_t)s->batch * s->heads_kv * plan.nsplit > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  // the count of valid 64-key tiles over all units is a 32-bit int on the device
+  if ((int64_t)s->batch * s->heads_kv * ((s->cache_len + 63) / 64) > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
   if (((int64_t)s->batch * s->heads_q * s->q_len + 3) / 4 > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }

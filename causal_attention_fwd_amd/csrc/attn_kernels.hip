@@ -791,44 +791,72 @@ void bwd_dq_kernel(BwdArgs a) {
 
 // ----------------------------------------------------------------------------
 // Decode. Sq new queries per sequence (the last Sq cached positions) against a
-// [B, Smax, Hkv, d] key/value cache. The cache of one (sequence, kv head) is
-// cut into splits; one wave (a one-wave workgroup, no barrier partners) takes
-// one split and runs the forward's tile routine over its 64-key tiles with the
-// G*Sq query rows of the kv group as its 32-row block (row r = head r / Sq,
-// new query r % Sq; rows past G*Sq are empty). It writes the split's
-// normalised partial O (fp32) and LSE; the merge kernel combines the splits.
-// The work is bound by streaming the cache from HBM.
+// [B, Smax, Hkv, d] key/value cache. A unit is one (sequence, kv head); its
+// R = G*Sq query rows (row r: head r / Sq of the group, new query r % Sq) form
+// one 32-row block (rows past R are empty). The valid 64-key tiles of all
+// units, laid end to end (sequence-major, then kv head), are dealt out evenly
+// to the W one-wave workgroups of the grid: wave w takes tiles
+// [floor(w*T/W), floor((w+1)*T/W)) of the T in total, so every wave streams
+// the same number of bytes whatever the mix of cache lengths. A wave's range
+// may cross units; for each unit it touches it runs the forward's tile
+// routine over its share of that unit's tiles and writes a normalised fp32
+// partial O and its LSE to slot w + u. The (wave, unit) pairs form a
+// staircase (a later wave never returns to an earlier unit), so w + u never
+// repeats and W + U - 1 slots suffice. The merge kernel combines the partials
+// of each query row by log-sum-exp. The work is bound by streaming the cache
+// from HBM.
 // ----------------------------------------------------------------------------
 struct DecArgs {
   const bf16* q;
   const bf16* k;
   const bf16* v;
   const int32_t* lens;
-  float* ws_o;    // [B, Hq, Sq, nsplit, D]
-  float* ws_lse;  // [B, Hq, Sq, nsplit]
+  int* hdr;       // hdr[0] = T, the number of valid tiles over all units
+  int2* uinfo;    // per unit: first and last wave holding a partial of it
+  float* ws_o;    // [slots, R, D]
+  float* ws_lse;  // [slots, R]
   bf16* o;        // [B, Sq, Hq, D]
   float* lse;     // [B, Hq, Sq]
-  int B, Sq, Smax, Hq, Hkv, nsplit, chunk;
+  int B, Sq, Smax, Hq, Hkv, W;
   float scale;
 };
 
-template <int D, int OCC>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
-void decode_split_kernel(DecArgs a) {
+// Valid 64-key tiles of each unit of sequence b.
+__device__ __forceinline__ int dec_tiles(const DecArgs& a, int b) {
+  return (valid_len(a.lens, b, a.Smax) + 63) >> 6;
+}
+
+// First tile of wave w (wave w owns [dec_start(w), dec_start(w + 1))).
+__device__ __forceinline__ int dec_start(int w, int T, int W) {
+  return (int)(((int64_t)w * T) / W);
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ int wave_scan_incl_i(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// One unit's share of a wave: local tiles [s0, s1) of unit (b, hkv), partial
+// result to slot `slot`.
+template <int D, int STAGES>
+__device__ __forceinline__ void decode_segment(const DecArgs& a, int b, int hkv, int s0, int s1, int64_t slot,
+                                               bf16* sK0, bf16* sV0, bf16* sK1, bf16* sV1, int lane) {
   constexpr int BN = 64;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
-  constexpr int KVT = TileLayout<D>::template elems<BN>();
-  __shared__ __attribute__((aligned(16))) bf16 sK0[KVT], sV0[KVT], sK1[KVT], sV1[KVT];
-
-  const int lane = threadIdx.x;
   const int g = lane >> 5;
-  const int l32 = lane & 31;
-  const int s = blockIdx.x % a.nsplit;
-  const int unit = blockIdx.x / a.nsplit;  // b * Hkv + hkv
-  const int b = unit / a.Hkv;
-  const int hkv = unit - b * a.Hkv;
   const int G = a.Hq / a.Hkv;
+  const int R = G * a.Sq;
   const int L = valid_len(a.lens, b, a.Smax);
   const int64_t ks = (int64_t)a.Hkv * D;
   const bf16* Kb = a.k + ((int64_t)b * a.Smax * a.Hkv + hkv) * D;
@@ -836,8 +864,8 @@ void decode_split_kernel(DecArgs a) {
 
   // the lane's query row: head hkv*G + r / Sq, new query t = r % Sq at cache
   // position L - Sq + t, which sees keys 0 .. L - Sq + t
-  const int r = l32;
-  const bool row_ok = r < G * a.Sq;
+  const int r = lane & 31;
+  const bool row_ok = r < R;
   const int hh = row_ok ? r / a.Sq : 0;
   const int t = row_ok ? r - hh * a.Sq : 0;
   const int h = hkv * G + hh;
@@ -855,10 +883,10 @@ void decode_split_kernel(DecArgs a) {
   wait_vmem();
 
   const float c = a.scale * kLog2e;
-  const int k0 = s * a.chunk;                          // the split's first key
-  const int kend = min(k0 + a.chunk, L);               // and one past its last
-  const int ntiles = kend > k0 ? (kend - k0 + BN - 1) / BN : 0;
-  const int first_last = L - a.Sq;                     // smallest last-visible key of the rows
+  const int k0 = s0 * BN;                   // the segment's first key
+  const int kend = min(s1 * BN, L);         // and one past its last
+  const int ntiles = s1 - s0;
+  const int first_last = L - a.Sq;          // smallest last-visible key of the rows
   const KVBuf b0{sK0, sV0, 0}, b1{sK1, sV1, 1};
   auto fetch = [&](int kt, const KVBuf& buf) {
     tile_load_lds<BN, D, 1>(Kb, ks, k0 + kt * BN, kend, buf.k, 0, lane);
@@ -874,15 +902,27 @@ void decode_split_kernel(DecArgs a) {
       fwd_tile<D, 1, false>(st, buf.k, buf.v, lane, c, lim);
     }
   };
-  tile_pipeline(ntiles, b0, b1, fetch, [](int, const KVBuf&) {}, compute);
+  if constexpr (STAGES == 2) {
+    tile_pipeline(ntiles, b0, b1, fetch, [](int, const KVBuf&) {}, compute);
+  } else {
+    // one stage: the wave waits for each tile; the other waves on the SIMD
+    // (twice as many fit in LDS) keep HBM busy meanwhile
+    for (int kt = 0; kt < ntiles; ++kt) {
+      fetch(kt, b0);
+      wait_vmem();
+      __syncthreads();
+      compute(kt, b0);
+      __syncthreads();
+    }
+  }
 
-  // partial result of this split: O / l (fp32) and LSE = mu*scale + ln l
+  // partial result: O / l (fp32) and LSE = mu*scale + ln l
   const float lt = xhalf_sum(st.lsum[0]);
   if (row_ok) {
-    const int64_t row = ((int64_t)b * a.Hq + h) * a.Sq + t;
+    const int64_t prow = slot * R + r;
     const bool any = lt > 0.f;
     const float inv = any ? 1.f / lt : 0.f;
-    float* wo = a.ws_o + (row * a.nsplit + s) * D;
+    float* wo = a.ws_o + prow * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -894,12 +934,74 @@ void decode_split_kernel(DecArgs a) {
         ov.w = st.oacc[dt][0][rr * 4 + 3] * inv;
         *reinterpret_cast<float4*>(wo + dt * 32 + rr * 8 + g * 4) = ov;
       }
-    if (g == 0) a.ws_lse[row * a.nsplit + s] = any ? (st.mu[0] * c + __log2f(lt)) * kLn2 : kNegInf;
+    if (g == 0) a.ws_lse[prow] = any ? (st.mu[0] * c + __log2f(lt)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, int OCC, int STAGES>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void decode_split_kernel(DecArgs a) {
+  constexpr int KVT = TileLayout<D>::template elems<64>();
+  __shared__ __attribute__((aligned(16))) bf16 sK0[KVT], sV0[KVT];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[STAGES == 2 ? KVT : 8], sV1[STAGES == 2 ? KVT : 8];
+  const int lane = threadIdx.x;
+  const int w = blockIdx.x;
+
+  // T: valid tiles over all units (every wave counts them; wave 0 publishes)
+  int part = 0;
+  for (int b = lane; b < a.B; b += 64) part += dec_tiles(a, b) * a.Hkv;
+  const int T = wave_sum_i(part);
+  if (w == 0 && lane == 0) a.hdr[0] = T;
+  int tb = dec_start(w, T, a.W);
+  const int te = dec_start(w + 1, T, a.W);
+  if (tb >= te) return;
+
+  // the sequence holding tile tb: the first whose inclusive tile prefix exceeds it
+  int b = -1, before = 0;  // before: tiles of the sequences ahead of b
+  for (int base = 0; base < a.B; base += 64) {
+    const int x = base + lane < a.B ? dec_tiles(a, base + lane) * a.Hkv : 0;
+    const int incl = wave_scan_incl_i(x, lane) + before;
+    const uint64_t hit = __ballot(incl > tb);
+    if (hit) {
+      const int f = __builtin_ctzll(hit);
+      b = base + f;
+      before = __shfl(incl - x, f, 64);
+      break;
+    }
+    before = __shfl(incl, 63, 64);
+  }
+  if (b < 0) return;  // unreachable while tb < T
+
+  int nt = dec_tiles(a, b);  // > 0: sequence b holds tile tb
+  int hkv = (tb - before) / nt;
+  int ustart = before + hkv * nt;
+  for (;;) {
+    const int64_t u = (int64_t)b * a.Hkv + hkv;
+    const int s0 = tb - ustart;
+    const int s1 = min(te, ustart + nt) - ustart;
+    decode_segment<D, STAGES>(a, b, hkv, s0, s1, w + u, sK0, sV0, sK1, sV1, lane);
+    if (lane == 0) {
+      if (s0 == 0) a.uinfo[u].x = w;
+      if (s1 == nt) a.uinfo[u].y = w;
+    }
+    tb = ustart + s1;
+    if (tb >= te) break;
+    ustart += nt;
+    if (++hkv == a.Hkv) {  // next sequence with a non-empty cache
+      hkv = 0;
+      do {
+        ++b;
+      } while (b < a.B && (nt = dec_tiles(a, b)) == 0);
+      if (b >= a.B) break;  // unreachable while tb < T
+    }
   }
 }
 
 // Merge: one wave per (sequence, head, new query); LSE = ln sum_s exp(LSE_s),
-// O = sum_s exp(LSE_s - LSE) O_s, rounded to bf16; lanes run over d.
+// O = sum_s exp(LSE_s - LSE) O_s over the unit's partials, rounded to bf16.
+// The weights are computed with lanes over partials, the sum with lanes over
+// d (eight partials' loads in flight at a time). A sequence with an empty
+// cache has no partials: O = 0, LSE = -inf.
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecArgs a) {
   constexpr int PER = D / 64;  // elements per lane
@@ -907,24 +1009,56 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecArgs a) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * Hq + h) * Sq + t
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
   if (row >= rows) return;
-  const float* wl = a.ws_lse + row * a.nsplit;
-  float m = kNegInf;
-  for (int s = 0; s < a.nsplit; ++s) m = fmaxf(m, wl[s]);
-  float acc[PER] = {};
-  float den = 0.f;
-  if (m != kNegInf) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float w = __expf(wl[s] - m);  // 0 for empty splits (-inf)
-      den += w;
-      const float* wo = a.ws_o + (row * a.nsplit + s) * D;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += w * wo[e * 64 + lane];
-    }
-  }
   const int t = (int)(row % a.Sq);
   const int64_t bh = row / a.Sq;
   const int h = (int)(bh % a.Hq);
   const int b = (int)(bh / a.Hq);
+  const int G = a.Hq / a.Hkv;
+  const int R = G * a.Sq;
+  const int hkv = h / G;
+  const int r = (h - hkv * G) * a.Sq + t;
+  const int64_t u = (int64_t)b * a.Hkv + hkv;
+  float m = kNegInf;
+  float acc[PER] = {};
+  float den = 0.f;
+  if (dec_tiles(a, b) > 0) {
+    const int T = a.hdr[0];
+    const int2 ui = a.uinfo[u];
+    const int n = ui.y - ui.x + 1;
+    // waves between the first and the last that own no tile wrote nothing
+    auto has = [&](int i) {
+      const int w = ui.x + i;
+      return i < n && dec_start(w, T, a.W) < dec_start(w + 1, T, a.W);
+    };
+    for (int i0 = 0; i0 < n; i0 += 64)
+      if (has(i0 + lane)) m = fmaxf(m, a.ws_lse[(ui.x + i0 + lane + u) * R + r]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (m != kNegInf) {
+      for (int i0 = 0; i0 < n; i0 += 64) {
+        const float wt = has(i0 + lane) ? __expf(a.ws_lse[(ui.x + i0 + lane + u) * R + r] - m) : 0.f;
+        den += wt;  // 0 for a partial that saw no key
+        const int cnt = min(64, n - i0);
+        for (int j = 0; j < cnt; j += 8) {
+          float x[8][PER], wj[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const int jx = j + jj < cnt ? j + jj : 0;
+            wj[jj] = j + jj < cnt ? __shfl(wt, jx, 64) : 0.f;
+            const float* wo = a.ws_o + ((ui.x + i0 + jx + u) * R + r) * D;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) x[jj][e] = wo[e * 64 + lane];
+          }
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += wj[jj] > 0.f ? wj[jj] * x[jj][e] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+    }
+  }
   bf16* orow = a.o + (((int64_t)b * a.Sq + t) * a.Hq + h) * D;
   const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
@@ -1061,39 +1195,52 @@ int64_t max_grid(const Problem& pr) {
   return m > pre ? m : pre;
 }
 
+#ifndef ATTN_DEC_STAGES
+#define ATTN_DEC_STAGES 2
+#endif
+#ifndef ATTN_DEC_ROUNDS
+#define ATTN_DEC_ROUNDS 1
+#endif
+
+// Workspace layout: [hdr: 256 B][uinfo: int2 per unit][partial LSE][partial O],
+// each part 256-byte aligned.
+namespace {
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
 DecodePlan plan_decode(const DecodeProblem& pr) {
-  // enough waves to cover every SIMD a few times over, but no split shorter
-  // than one 64-key tile
-  const int64_t units = (int64_t)pr.B * pr.Hkv;
-  const int tiles = (pr.Smax + 63) / 64;
-  const int64_t target = 2048;
-  int nsplit = (int)std::min<int64_t>(tiles, std::max<int64_t>(1, (target + units - 1) / units));
-  const int per = (tiles + nsplit - 1) / nsplit;
-  nsplit = (tiles + per - 1) / per;
+  // one wave per decode workgroup; as many waves as fit on the 256 CUs at
+  // once (LDS decides: two 64-key K and V tiles per stage), times ATTN_DEC_ROUNDS,
+  // but no more than there can be tiles
+  constexpr int kCUs = 256;
+  const int per_cu = (pr.d == 64 ? 8 : 4) / ATTN_DEC_STAGES;
+  const int64_t tmax = (int64_t)pr.B * pr.Hkv * ((pr.Smax + 63) / 64);
   DecodePlan plan;
-  plan.nsplit = nsplit;
-  plan.chunk = per * 64;
-  const size_t rows = (size_t)pr.B * pr.Hq * pr.Sq;
-  const size_t o_bytes = rows * nsplit * pr.d * sizeof(float);
-  plan.workspace_bytes = o_bytes + ((rows * nsplit * sizeof(float) + 255) / 256) * 256;
+  plan.waves = (int)std::min<int64_t>((int64_t)kCUs * per_cu * ATTN_DEC_ROUNDS, tmax);
+  const int64_t units = (int64_t)pr.B * pr.Hkv;
+  const int64_t slots = plan.waves + units - 1;
+  const int64_t R = (int64_t)(pr.Hq / pr.Hkv) * pr.Sq;
+  plan.off_uinfo = 256;
+  plan.off_lse = plan.off_uinfo + align256((size_t)units * 8);
+  plan.off_o = plan.off_lse + align256((size_t)(slots * R) * sizeof(float));
+  plan.workspace_bytes = plan.off_o + (size_t)(slots * R) * pr.d * sizeof(float);
   return plan;
 }
 
 hipError_t launch_decode(const DecodeProblem& pr, const DecodePlan& plan, const void* q, const void* k_cache,
                          const void* v_cache, void* o, float* lse, void* workspace, hipStream_t stream) {
-  const size_t rows = (size_t)pr.B * pr.Hq * pr.Sq;
+  char* ws = reinterpret_cast<char*>(workspace);
   DecArgs a{(const bf16*)q, (const bf16*)k_cache, (const bf16*)v_cache, pr.cache_lens,
-            reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ((rows * plan.nsplit * sizeof(float) + 255) / 256) * 256),
-            reinterpret_cast<float*>(workspace), (bf16*)o, lse, pr.B, pr.Sq, pr.Smax, pr.Hq, pr.Hkv,
-            plan.nsplit, plan.chunk, pr.scale};
-  const int64_t splits = (int64_t)pr.B * pr.Hkv * plan.nsplit;
-  const int64_t merge_blocks = ((int64_t)rows + 3) / 4;
+            reinterpret_cast<int*>(ws), reinterpret_cast<int2*>(ws + plan.off_uinfo),
+            reinterpret_cast<float*>(ws + plan.off_o), reinterpret_cast<float*>(ws + plan.off_lse),
+            (bf16*)o, lse, pr.B, pr.Sq, pr.Smax, pr.Hq, pr.Hkv, plan.waves, pr.scale};
+  const int64_t merge_blocks = ((int64_t)pr.B * pr.Hq * pr.Sq + 3) / 4;
   hipError_t e;
   if (pr.d == 64) {
-    e = launch((const void*)&decode_split_kernel<64, 2>, splits, a, stream, 64);
+    e = launch((const void*)&decode_split_kernel<64, 2, ATTN_DEC_STAGES>, plan.waves, a, stream, 64);
     if (e == hipSuccess) e = launch((const void*)&decode_merge_kernel<64>, merge_blocks, a, stream);
   } else {
-    e = launch((const void*)&decode_split_kernel<128, 1>, splits, a, stream, 64);
+    e = launch((const void*)&decode_split_kernel<128, 1, ATTN_DEC_STAGES>, plan.waves, a, stream, 64);
     if (e == hipSuccess) e = launch((const void*)&decode_merge_kernel<128>, merge_blocks, a, stream);
   }
   return e;

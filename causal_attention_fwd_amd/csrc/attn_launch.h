@@ -33,12 +33,14 @@ struct DecodeProblem {
   const int32_t* cache_lens;  // device int32[B] or nullptr (= Smax)
 };
 
-// How the cache of one (sequence, kv head) is cut into splits: nsplit chunks of
-// `chunk` positions (a multiple of 64), each handled by one wave; a merge pass
-// combines the splits' partial results by log-sum-exp.
+// How the decode work is dealt out: `waves` one-wave workgroups share the
+// valid 64-key tiles of all (sequence, kv head) units evenly; each writes one
+// partial (O, LSE) per unit it touches, and a merge pass combines them by
+// log-sum-exp. Workspace: a header, per-unit wave bounds, the partials.
 struct DecodePlan {
-  int nsplit, chunk;
-  size_t workspace_bytes;  // partial O (fp32) and LSE of every split
+  int waves;
+  size_t off_uinfo, off_lse, off_o;
+  size_t workspace_bytes;
 };
 DecodePlan plan_decode(const DecodeProblem& pr);
 hipError_t launch_decode(const DecodeProblem& pr, const DecodePlan& plan, const void* q, const void* k_cache,

@@ -163,9 +163,13 @@ typedef struct attn_decode_shape {
 } attn_decode_shape;
 
 /*
- * Bytes of device workspace attn_decode needs (the per-split partial outputs:
- * B * Hq * Sq * nsplit * (d + 1) floats, nsplit <= ceil(Smax / 64)). Returns 0
- * for a NULL or invalid shape.
+ * Bytes of device workspace attn_decode needs. The valid 64-key tiles of all
+ * (sequence, kv head) units are shared evenly by W <= 1024 waves (fewer when
+ * there are fewer tiles); each wave leaves one partial result, (d + 1) floats
+ * per query row, for each unit it touches, so the workspace holds
+ * (W + B * Hkv - 1) * (Hq / Hkv) * Sq * (d + 1) floats plus an 8-byte record
+ * per unit and a small header; it does not grow with Smax once W is capped.
+ * Returns 0 for a NULL or invalid shape.
  */
 size_t attn_decode_workspace_bytes(const attn_decode_shape* shape);
 
@@ -174,7 +178,8 @@ size_t attn_decode_workspace_bytes(const attn_decode_shape* shape);
  * [B,Hq,Sq] fp32; workspace: caller-owned device memory of at least
  * attn_decode_workspace_bytes() bytes, 16-byte aligned (ATTN_ERR_WORKSPACE
  * otherwise), overwritten by the call and free again when the stream has run
- * it. Two launches (per-split partials, then their merge); deterministic.
+ * it. Two launches (partials, then their merge); deterministic for a given
+ * shape and cache lengths.
  */
 attn_status attn_decode(const attn_decode_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                         void* o, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);

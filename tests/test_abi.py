@@ -212,12 +212,16 @@ def test_decode_pointers_and_workspace(lib):
     assert _dec(lib, shape, ws=ODD, ws_bytes=need) == 4
 
 
-def test_decode_workspace_bytes_grows_with_splits_not_cache(lib):
-    # one fp32 partial row (d values + LSE) per (query row, split); splits are
-    # capped, so the workspace stays bounded as the cache grows
-    small = lib.attn_decode_workspace_bytes(ctypes.byref(_dshape(B=1, Smax=64, Hq=32, Hkv=8)))
-    assert small == 32 * 64 * 4 + 256
-    for Smax in (4096, 65536, 1 << 20):
-        ws = lib.attn_decode_workspace_bytes(ctypes.byref(_dshape(B=1, Smax=Smax, Hq=32, Hkv=8)))
-        splits = -(-2048 // 8)
-        assert ws <= 32 * splits * (64 * 4 + 4) + 256
+def test_decode_workspace_bytes_bounded_by_waves_and_units(lib):
+    # one fp32 partial (d values + LSE) per query row and (wave, unit) slot;
+    # the wave count is capped, so the workspace does not grow with the cache
+    def ws(**kw):
+        return lib.attn_decode_workspace_bytes(ctypes.byref(_dshape(**kw)))
+    B, Hq, Hkv, d = 4, 32, 8, 64
+    R, U = Hq // Hkv, B * Hkv
+    big = [ws(B=B, Smax=Smax, Hq=Hq, Hkv=Hkv, d=d) for Smax in (1 << 14, 1 << 16, 1 << 20)]
+    assert big[0] == big[1] == big[2]
+    assert big[0] <= 256 + 256 + U * 8 + 256 + (4096 + U) * R * (d + 1) * 4
+    # a one-tile cache needs one wave per unit at most
+    small = ws(B=B, Smax=64, Hq=Hq, Hkv=Hkv, d=d)
+    assert small <= 256 + 256 + U * 8 + 256 + (2 * U) * R * (d + 1) * 4

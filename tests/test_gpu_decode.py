@@ -68,6 +68,9 @@ CASES = [
     (2, 2, 4096, 4, 4, 128, None),
     (3, 1, 5000, 12, 4, 128, (64, 5000)),
     (5, 16, 129, 4, 2, 128, (10, 129)),
+    # one unit shared by every wave (over a thousand partials to merge)
+    (1, 1, 131072, 8, 1, 64, None),
+    (2, 1, 70000, 16, 2, 128, (30000, 70000)),
 ]
 
 
