@@ -89,3 +89,60 @@ def test_pins_catch_mutation(name):
         except Exception:  # assertion failures, and crashes caused by the mutant
             caught += 1
     assert caught > 0, f"no pin caught mutation {name}"
+
+
+# ------------------------------------------------------------------ rotary position embedding
+
+import test_oracle_rope as rpins  # noqa: E402
+
+ROPE_SRC = os.path.join(os.path.dirname(SRC), "rope.py")
+
+ROPE_MUTATIONS = {
+    "rope_sin_sign": ("out[..., 0::2] = even * c - odd * s", "out[..., 0::2] = even * c + odd * s"),
+    "rope_exponent_without_two": ("-2.0 * i / d", "-1.0 * i / d"),
+    "rope_positions_from_one": ("np.arange(S, dtype=np.float64) if positions", "np.arange(1, S + 1, dtype=np.float64) if positions"),
+    "rope_half_split_pairs": ("even, odd = x[..., 0::2], x[..., 1::2]", "even, odd = x[..., :d // 2], x[..., d // 2:]"),
+    "rope_backward_rotates_forward": ('ref["dQ"] = rotate(ref["dQ"], base, inverse=True', 'ref["dQ"] = rotate(ref["dQ"], base, inverse=False'),
+    "rope_dK_not_taken_back": ('    ref["dK"] = rotate(ref["dK"], base, inverse=True, dtype=dtype)\n', ""),
+    "rope_values_rotated": ("kr = rotate(k, base, dtype=dtype)\n    ref = attention.backward(qr, kr, v,",
+                            "kr = rotate(k, base, dtype=dtype)\n    ref = attention.backward(qr, kr, rotate(v, base),"),
+}
+
+
+def _rope_module(src):
+    mod = types.ModuleType("oracle_rope_copy")
+    exec(compile(src.replace("from . import attention", "from oracle import attention"), "oracle_rope_copy", "exec"),
+         mod.__dict__)
+    return mod
+
+
+def _rope_pins(rp):
+    yield lambda: rpins.test_position_zero_is_identity(rp)
+    yield lambda: rpins.test_head_size_two_is_plane_rotation_by_the_position(rp)
+    yield lambda: rpins.test_frequencies_are_powers_of_ten_for_head_size_eight(rp)
+    yield lambda: rpins.test_matches_complex_multiplication(rp)
+    yield lambda: rpins.test_orthogonal_and_inverse(rp)
+    yield lambda: rpins.test_scores_depend_only_on_relative_position(rp)
+    yield lambda: rpins.test_central_differences_through_rope(1, 5, 2, 1, 4, None, True, rp)
+    yield lambda: rpins.test_matches_torch_complex_rope_and_sdpa(True, rp)
+
+
+def test_unmutated_rope_copy_passes_every_pin():
+    mod = _rope_module(open(ROPE_SRC).read())
+    for pin in _rope_pins(mod):
+        pin()
+
+
+@pytest.mark.parametrize("name", sorted(ROPE_MUTATIONS))
+def test_rope_pins_catch_mutation(name):
+    old, new = ROPE_MUTATIONS[name]
+    src = open(ROPE_SRC).read()
+    assert old in src, old
+    mod = _rope_module(src.replace(old, new))
+    caught = 0
+    for pin in _rope_pins(mod):
+        try:
+            pin()
+        except Exception:
+            caught += 1
+    assert caught > 0, f"no pin caught mutation {name}"
