@@ -6,6 +6,7 @@ memory and the current stream. There is no CPU fallback: if the library is not
 built, or a tensor is not on a GPU, the call raises.
 
 Entry points (same names as the C ABI):
+    attn_rope(q, k, q_rot, k_rot, rope_base=10000.0, seqlens=None)
     attn_fwd(q, k, v, o, lse, scale, seqlens=None)
     attn_bwd_preprocess(o, d_o, delta, seqlens=None)
     attn_bwd_workspace_bytes(B, S, Hq, Hkv, d)
@@ -15,7 +16,7 @@ Entry points (same names as the C ABI):
     attn_decode_workspace_bytes(B, Sq, Smax, Hq, Hkv, d)
     attn_decode(q, k_cache, v_cache, o, lse, scale, cache_lens=None, workspace=None)
     attn_status_string(code)
-and allocating conveniences `forward(...)`, `backward(...)`, `decode(...)`.
+and allocating conveniences `rope(...)`, `forward(...)`, `backward(...)`, `decode(...)`.
 """
 from __future__ import annotations
 
@@ -24,7 +25,7 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
+__all__ = ["attn_rope", "rope", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode_workspace_bytes", "attn_decode", "attn_status_string",
            "forward", "backward", "decode", "capture_step", "AttnError", "library_path", "load_library",
            "STATUS"]
@@ -36,7 +37,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3:
           4: "ATTN_ERR_WORKSPACE", 5: "ATTN_ERR_HIP"}
 
 # The symbols include/attn.h declares.
-EXPORTED = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_dkdv",
+EXPORTED = ("attn_rope", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_dkdv",
             "attn_bwd_dq", "attn_decode_workspace_bytes", "attn_decode", "attn_status_string")
 
 
@@ -49,7 +50,7 @@ class AttnError(RuntimeError):
 class AttnShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("heads_q", ctypes.c_int32),
                 ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("causal", ctypes.c_int32), ("seqlens", ctypes.c_void_p)]
+                ("causal", ctypes.c_int32), ("seqlens", ctypes.c_void_p), ("rope_base", ctypes.c_float)]
 
 
 class AttnDecodeShape(ctypes.Structure):
@@ -93,6 +94,8 @@ def load_library():
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode.argtypes = [dshp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_decode.restype = i32
+    lib.attn_rope.argtypes = [shp, vp, vp, vp, vp, vp]
+    lib.attn_rope.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -104,9 +107,9 @@ def attn_status_string(code: int) -> str:
 
 
 def make_shape(B: int, S: int, Hq: int, Hkv: int, d: int, scale: float, seqlens_ptr: Optional[int] = None,
-               causal: int = 1) -> AttnShape:
+               causal: int = 1, rope_base: float = 0.0) -> AttnShape:
     return AttnShape(int(B), int(S), int(Hq), int(Hkv), int(d), float(scale), int(causal),
-                     ctypes.c_void_p(seqlens_ptr) if seqlens_ptr else None)
+                     ctypes.c_void_p(seqlens_ptr) if seqlens_ptr else None, float(rope_base or 0.0))
 
 
 # ------------------------------------------------------------------ torch marshalling
@@ -131,7 +134,7 @@ def _check_gpu(name, t, dtype, shape=None):
     return t.data_ptr()
 
 
-def _shape_from(q, k, scale, seqlens, causal=1):
+def _shape_from(q, k, scale, seqlens, causal=1, rope_base=0.0):
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q must be [B,S,Hq,d] and k [B,S,Hkv,d]")
@@ -140,7 +143,7 @@ def _shape_from(q, k, scale, seqlens, causal=1):
     sl = None
     if seqlens is not None:
         sl = _check_gpu("seqlens", seqlens, torch.int32, (B,))
-    return make_shape(B, S, Hq, Hkv, d, scale, sl, causal), (B, S, Hq, Hkv, d)
+    return make_shape(B, S, Hq, Hkv, d, scale, sl, causal, rope_base), (B, S, Hq, Hkv, d)
 
 
 def _stream():
@@ -151,6 +154,18 @@ def _call(fn, where, *args):
     code = fn(*args)
     if code != 0:
         raise AttnError(code, where)
+
+
+def attn_rope(q, k, q_rot, k_rot, rope_base: float = 10000.0, seqlens=None):
+    """q_rot, k_rot <- q and k rotated by the rotary position embedding."""
+    torch = _torch()
+    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, 1.0, seqlens, 1, rope_base)
+    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d)),
+            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d)),
+            _check_gpu("q_rot", q_rot, torch.bfloat16, (B, S, Hq, d)),
+            _check_gpu("k_rot", k_rot, torch.bfloat16, (B, S, Hkv, d))]
+    _call(load_library().attn_rope, "attn_rope", ctypes.byref(shape), *[ctypes.c_void_p(p) for p in ptrs],
+          _stream())
 
 
 def attn_fwd(q, k, v, o, lse, scale: float, seqlens=None, causal: int = 1):
@@ -185,10 +200,13 @@ def attn_bwd_workspace_bytes(B: int, S: int, Hq: int, Hkv: int, d: int) -> int:
     return int(load_library().attn_bwd_workspace_bytes(ctypes.byref(shape)))
 
 
-def attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale: float, seqlens=None, workspace=None, causal: int = 1):
-    """dQ, dK, dV <- attention backward (writes into `dq`, `dk`, `dv`)."""
+def attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale: float, seqlens=None, workspace=None, causal: int = 1,
+             rope_base: float = 0.0):
+    """dQ, dK, dV <- attention backward (writes into `dq`, `dk`, `dv`). With
+    rope_base > 0, q and k are the rotated tensors and dq, dk come back with
+    respect to the unrotated ones."""
     torch = _torch()
-    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal)
+    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal, rope_base)
     ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d)),
             _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d)),
             _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d)),
@@ -206,9 +224,9 @@ def attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale: float, seqlens=None, w
           ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), _stream())
 
 
-def _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal):
+def _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal, rope_base):
     torch = _torch()
-    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal)
+    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal, rope_base)
     ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d)),
             _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d)),
             _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d)),
@@ -218,20 +236,22 @@ def _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal):
     return shape, (B, S, Hq, Hkv, d), ptrs
 
 
-def attn_bwd_dkdv(q, k, v, d_o, lse, delta, dk, dv, scale: float, seqlens=None, causal: int = 1):
+def attn_bwd_dkdv(q, k, v, d_o, lse, delta, dk, dv, scale: float, seqlens=None, causal: int = 1,
+                  rope_base: float = 0.0):
     """dK, dV <- the key-block pass of the backward (writes into `dk`, `dv`)."""
     torch = _torch()
-    shape, (B, S, Hq, Hkv, d), ptrs = _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal)
+    shape, (B, S, Hq, Hkv, d), ptrs = _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal, rope_base)
     ptrs += [_check_gpu("dk", dk, torch.bfloat16, (B, S, Hkv, d)),
              _check_gpu("dv", dv, torch.bfloat16, (B, S, Hkv, d))]
     _call(load_library().attn_bwd_dkdv, "attn_bwd_dkdv", ctypes.byref(shape),
           *[ctypes.c_void_p(p) for p in ptrs], _stream())
 
 
-def attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale: float, seqlens=None, causal: int = 1):
+def attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale: float, seqlens=None, causal: int = 1,
+                rope_base: float = 0.0):
     """dQ <- the query-block pass of the backward (writes into `dq`)."""
     torch = _torch()
-    shape, (B, S, Hq, Hkv, d), ptrs = _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal)
+    shape, (B, S, Hq, Hkv, d), ptrs = _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal, rope_base)
     ptrs += [_check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d))]
     _call(load_library().attn_bwd_dq, "attn_bwd_dq", ctypes.byref(shape),
           *[ctypes.c_void_p(p) for p in ptrs], _stream())
@@ -300,8 +320,18 @@ def forward(q, k, v, scale: Optional[float] = None, seqlens=None, causal: bool =
     return o, lse
 
 
-def backward(q, k, v, o, d_o, lse, scale: Optional[float] = None, seqlens=None, causal: bool = True):
-    """Returns (dQ, dK, dV, D) as new tensors (runs the preprocess, then the backward)."""
+def rope(q, k, rope_base: float = 10000.0):
+    """Returns (q_rot, k_rot) as new tensors."""
+    q_rot, k_rot = _torch().empty_like(q), _torch().empty_like(k)
+    attn_rope(q, k, q_rot, k_rot, rope_base)
+    return q_rot, k_rot
+
+
+def backward(q, k, v, o, d_o, lse, scale: Optional[float] = None, seqlens=None, causal: bool = True,
+             rope_base: float = 0.0):
+    """Returns (dQ, dK, dV, D) as new tensors (runs the preprocess, then the
+    backward). With rope_base > 0, q and k are the rotated tensors from rope()
+    and dQ, dK are the gradients with respect to the unrotated ones."""
     torch = _torch()
     B, S, Hq, d = q.shape
     if scale is None:
@@ -311,7 +341,7 @@ def backward(q, k, v, o, d_o, lse, scale: Optional[float] = None, seqlens=None, 
     need = attn_bwd_workspace_bytes(B, S, Hq, k.shape[2], d)
     ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, ws, int(causal))
+    attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, ws, int(causal), rope_base)
     return dq, dk, dv, delta
 
 

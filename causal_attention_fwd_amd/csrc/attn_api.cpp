@@ -19,6 +19,7 @@ attn_status check_shape(const attn_shape* s, attn::Problem* pr) {
   if (!(isfinite(s->scale) && s->scale > 0.f)) return ATTN_ERR_INVALID_ARG;
   if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   if (s->causal != 0 && s->causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (!(isfinite(s->rope_base) && s->rope_base >= 0.f)) return ATTN_ERR_INVALID_ARG;
   if (s->seqlens && (reinterpret_cast<uintptr_t>(s->seqlens) & 3u) != 0) return ATTN_ERR_MISALIGNED;
   // tiles are fetched through buffer resources with 32-bit byte offsets that
   // span up to 128 rows of one sequence: 128 * heads * head_dim * 2 < 2^31
@@ -31,6 +32,7 @@ attn_status check_shape(const attn_shape* s, attn::Problem* pr) {
   pr->scale = s->scale;
   pr->seqlens = s->seqlens;
   pr->causal = s->causal;
+  pr->rope_base = s->rope_base;
   if (attn::max_grid(*pr) > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
@@ -93,6 +95,17 @@ attn_status attn_bwd_preprocess(const attn_shape* shape, const void* o, const vo
   st = check_ptrs({o, d_o, delta});
   if (st != ATTN_OK) return st;
   return from_hip(attn::launch_preprocess(pr, o, d_o, delta, stream));
+}
+
+attn_status attn_rope(const attn_shape* shape, const void* q, const void* k, void* q_rot, void* k_rot,
+                      hipStream_t stream) {
+  attn::Problem pr;
+  attn_status st = check_shape(shape, &pr);
+  if (st != ATTN_OK) return st;
+  if (!(pr.rope_base > 0.f)) return ATTN_ERR_INVALID_ARG;
+  st = check_ptrs({q, k, q_rot, k_rot});
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_rope(pr, q, k, q_rot, k_rot, stream));
 }
 
 size_t attn_bwd_workspace_bytes(const attn_shape* shape) {

@@ -26,6 +26,7 @@
 //  * the softmax runs in base 2 with scale*log2(e) folded into one multiply;
 //    LSE is exported as a natural log.
 #include <algorithm>
+#include <cmath>
 
 #include "attn_common.h"
 #include "attn_launch.h"
@@ -53,6 +54,38 @@ struct PreArgs {
   int64_t rows;  // B * Hq * S
 };
 
+// Rotary position embedding ("AxiomLM" PyPI page, "Key Features" and "8.
+// Standalone Modern Architectural Modules"): pair (2i, 2i+1) of a query or key
+// at position p is rotated by the angle p * theta_i, theta_i = base^(-2i/d).
+// phi_i = theta_i / (2 pi) (revolutions per position) comes from the host in
+// fp64, so the angle is reduced to [0, 1) revolutions exactly enough for any
+// position before the hardware sine and cosine (which take revolutions).
+struct RopeFreq {
+  double phi[64];  // i < d/2
+};
+
+__device__ __forceinline__ void rope_cos_sin(double phi, int p, float& cs, float& sn) {
+  const double x = (double)p * phi;
+  const float rev = (float)(x - __builtin_floor(x));
+  cs = __builtin_amdgcn_cosf(rev);
+  sn = __builtin_amdgcn_sinf(rev);
+}
+
+// The adjoint rotation (by -p*theta) of four consecutive elements of one row,
+// d = d0 + 4g .. d0 + 4g + 3 (d0 a multiple of 8, the same for every lane;
+// g = 0 or 1 per lane): pairs (d, d+1) and (d+2, d+3).
+__device__ __forceinline__ void rope_adjoint4(const RopeFreq& rf, int d0, int g, int p, float (&x)[4]) {
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr) {
+    float cs, sn;
+    const double phi = g ? rf.phi[d0 / 2 + 2 + pr] : rf.phi[d0 / 2 + pr];
+    rope_cos_sin(phi, p, cs, sn);
+    const float x0 = x[2 * pr], x1 = x[2 * pr + 1];
+    x[2 * pr] = x0 * cs + x1 * sn;
+    x[2 * pr + 1] = x1 * cs - x0 * sn;
+  }
+}
+
 struct BwdArgs {
   const bf16* q;
   const bf16* k;
@@ -67,6 +100,8 @@ struct BwdArgs {
   int B, S, Hq, Hkv, nblk;
   float scale;
   int causal;  // 1: keys j <= i only; 0: every key of the valid prefix
+  int rope;    // 1: q and k are rotated; dQ and dK leave through the adjoint
+  RopeFreq rf;
 };
 
 constexpr int kThreads = 256;  // four waves, one per SIMD
@@ -609,9 +644,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           bf16x4 kv4, vv4;
+          float kx[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kx[e] = st.dk[ct][t][rr * 4 + e] * a.scale;
+          if (a.rope) rope_adjoint4(a.rf, ct * 32 + rr * 8, g, j, kx);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            kv4[e] = (bf16)(valid ? st.dk[ct][t][rr * 4 + e] * a.scale : 0.f);
+            kv4[e] = (bf16)(valid ? kx[e] : 0.f);
             vv4[e] = (bf16)(valid ? st.dv[ct][t][rr * 4 + e] : 0.f);
           }
           const int64_t off = (int64_t)j * ks + ct * 32 + rr * 8 + g * 4;
@@ -780,13 +819,64 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           bf16x4 ov;
+          float qx[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = (bf16)(valid ? st.acc[dt][t][rr * 4 + e] * a.scale : 0.f);
+          for (int e = 0; e < 4; ++e) qx[e] = st.acc[dt][t][rr * 4 + e] * a.scale;
+          if (a.rope) rope_adjoint4(a.rf, dt * 32 + rr * 8, g, i, qx);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (bf16)(valid ? qx[e] : 0.f);
           *reinterpret_cast<bf16x4*>(dQb + (int64_t)i * qs + dt * 32 + rr * 8 + g * 4) = ov;
         }
     }
   }
   ATTN_TRACE_END(3);
+}
+
+// ----------------------------------------------------------------------------
+// RoPE pre-pass: q_rot, k_rot = the rotated q and k, once per step (HBM-bound:
+// every element read and written once). The forward and both backward passes
+// then read the rotated tensors; the backward passes take dQ and dK back
+// through the adjoint in their epilogues. One thread per 8 consecutive
+// elements (16 bytes, four pairs) of a row; rows of q first, then rows of k.
+// ----------------------------------------------------------------------------
+struct RopeArgs {
+  const bf16* q;
+  const bf16* k;
+  bf16* qr;
+  bf16* kr;
+  int64_t nq, nk;  // 8-element chunks of q and of k
+  int S, Hq, Hkv;
+  RopeFreq rf;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a) {
+  int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bf16* src = a.q;
+  bf16* dst = a.qr;
+  int H = a.Hq;
+  if (idx >= a.nq) {
+    idx -= a.nq;
+    if (idx >= a.nk) return;
+    src = a.k;
+    dst = a.kr;
+    H = a.Hkv;
+  }
+  constexpr int CPR = D / 8;  // chunks per row
+  const int64_t row = idx / CPR;
+  const int c = (int)(idx - row * CPR);
+  const int p = (int)((row / H) % a.S);
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + idx * 8);
+  bf16x8 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float cs, sn;
+    rope_cos_sin(a.rf.phi[c * 4 + e], p, cs, sn);
+    const float x0 = (float)x[2 * e], x1 = (float)x[2 * e + 1];
+    y[2 * e] = (bf16)(x0 * cs - x1 * sn);
+    y[2 * e + 1] = (bf16)(x0 * sn + x1 * cs);
+  }
+  *reinterpret_cast<bf16x8*>(dst + idx * 8) = y;
 }
 
 // ----------------------------------------------------------------------------
@@ -1125,6 +1215,15 @@ hipError_t launch(const void* fn, int64_t grid, Args args, hipStream_t stream, i
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(threads), kargs, 0, stream);
 }
 
+// phi_i = base^(-2i/d) / (2 pi), in fp64 (zeros when RoPE is off)
+RopeFreq rope_freq(const Problem& pr) {
+  RopeFreq rf{};
+  if (pr.rope_base > 0.f)
+    for (int i = 0; i < pr.d / 2; ++i)
+      rf.phi[i] = std::pow((double)pr.rope_base, -2.0 * i / pr.d) / (2.0 * 3.14159265358979323846);
+  return rf;
+}
+
 template <int D>
 hipError_t fwd_d(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,
                  hipStream_t stream) {
@@ -1148,7 +1247,7 @@ hipError_t dkdv_d(const Problem& pr, const void* q, const void* k, const void* v
   constexpr int NTJ = Tiles<D>::DKDV_NTJ;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             nullptr, (bf16*)dk, (bf16*)dv, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
-            cdiv(pr.S, 128 * NTJ), pr.scale, pr.causal};
+            cdiv(pr.S, 128 * NTJ), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr)};
   constexpr int GR = Tiles<D>::DKDV_GROUPS;
   return launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR>, (int64_t)a.nblk * pr.B * pr.Hkv, a,
                 stream, kThreads * GR);
@@ -1160,11 +1259,24 @@ hipError_t dq_d(const Problem& pr, const void* q, const void* k, const void* v, 
   constexpr int NT = Tiles<D>::DQ_NT;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             (bf16*)dq, nullptr, nullptr, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
-            cdiv(pr.S, 128 * NT), pr.scale, pr.causal};
+            cdiv(pr.S, 128 * NT), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr)};
   return launch((const void*)&bwd_dq_kernel<D, NT, Tiles<D>::DQ_OCC>, (int64_t)a.nblk * pr.B * pr.Hq, a, stream);
 }
 
+template <int D>
+hipError_t rope_d(const Problem& pr, const void* q, const void* k, void* qr, void* kr, hipStream_t stream) {
+  RopeArgs a{(const bf16*)q, (const bf16*)k, (bf16*)qr, (bf16*)kr,
+             (int64_t)pr.B * pr.S * pr.Hq * (D / 8), (int64_t)pr.B * pr.S * pr.Hkv * (D / 8),
+             pr.S, pr.Hq, pr.Hkv, rope_freq(pr)};
+  return launch((const void*)&rope_kernel<D>, (a.nq + a.nk + kThreads - 1) / kThreads, a, stream);
+}
+
 }  // namespace
+
+hipError_t launch_rope(const Problem& pr, const void* q, const void* k, void* q_rot, void* k_rot,
+                       hipStream_t stream) {
+  return pr.d == 64 ? rope_d<64>(pr, q, k, q_rot, k_rot, stream) : rope_d<128>(pr, q, k, q_rot, k_rot, stream);
+}
 
 hipError_t launch_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,
                       hipStream_t stream) {
@@ -1192,7 +1304,10 @@ int64_t max_grid(const Problem& pr) {
   const int64_t nb = (pr.S + 127) / 128;
   int64_t m = nb * pr.B * pr.Hq;
   const int64_t pre = ((int64_t)pr.B * pr.S * pr.Hq + 15) / 16;
-  return m > pre ? m : pre;
+  // RoPE pre-pass: one thread per 8 elements of q and k
+  const int64_t rope = ((int64_t)pr.B * pr.S * (pr.Hq + pr.Hkv) * (pr.d / 8) + kThreads - 1) / kThreads;
+  m = m > pre ? m : pre;
+  return m > rope ? m : rope;
 }
 
 #ifndef ATTN_DEC_STAGES

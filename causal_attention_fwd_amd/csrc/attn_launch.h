@@ -12,10 +12,13 @@ struct Problem {
   float scale;
   const int32_t* seqlens;  // device int32[B] or nullptr
   int causal;              // 1: keys j <= i only; 0: every key of the valid prefix
+  float rope_base;         // > 0: rotary embedding base (q, k rotated); 0: none
 };
 
 hipError_t launch_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,
                       hipStream_t stream);
+hipError_t launch_rope(const Problem& pr, const void* q, const void* k, void* q_rot, void* k_rot,
+                       hipStream_t stream);
 hipError_t launch_preprocess(const Problem& pr, const void* o, const void* d_o, float* delta, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
                            const float* lse, const float* delta, void* dk, void* dv, hipStream_t stream);

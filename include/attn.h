@@ -58,7 +58,8 @@ extern "C" {
 typedef enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, Hq % Hkv != 0,
-                                non-finite or non-positive scale, causal not 0/1 */
+                                non-finite or non-positive scale, causal not 0/1,
+                                negative or non-finite rope_base */
   ATTN_ERR_UNSUPPORTED = 2,  /* head_dim not in {64, 128},
                                 heads_q * head_dim > 2^22 (tile offsets are
                                 32-bit), or a grid beyond 2^31 - 1 blocks */
@@ -81,7 +82,30 @@ typedef struct attn_shape {
      [0, S] on the device; positions i >= L_b take no part in any sum, may hold
      any bits (including NaN), and receive zero outputs/gradients. */
   const int32_t* seqlens;
+  /* Rotary position embedding base, or 0 for none (finite and >= 0, else
+     ATTN_ERR_INVALID_ARG). When > 0, the q and k handed to attn_fwd and the
+     backward entry points are the ROTATED tensors written by attn_rope, and
+     the backward entry points return dq and dk with respect to the unrotated
+     q and k (the rotation's adjoint is applied as they are written).
+     attn_fwd and attn_bwd_preprocess do not depend on it. */
+  float rope_base;
 } attn_shape;
+
+/*
+ * Rotary position embedding ("AxiomLM" PyPI page, "Key Features": RoPE in its
+ * modern architecture suite; "8. Standalone Modern Architectural Modules":
+ * frequencies precomputed for the head size, applied to q [B,S,Hq,d] and k
+ * [B,S,Hkv,d] ahead of attention). Pair (2i, 2i+1) of every head at token
+ * position p (0 .. S-1) is rotated by a = p * theta_i, theta_i =
+ * rope_base^(-2i/d):
+ *   r_2i = x_2i cos a - x_2i+1 sin a,   r_2i+1 = x_2i sin a + x_2i+1 cos a.
+ * q_rot [B,S,Hq,d] and k_rot [B,S,Hkv,d] bf16 (rounded once from fp32). The
+ * caller keeps them for the backward pass (they replace q and k there).
+ * Requires shape->rope_base > 0 (ATTN_ERR_INVALID_ARG otherwise). Padded
+ * positions are rotated too; no attention pass reads them.
+ */
+attn_status attn_rope(const attn_shape* shape, const void* q, const void* k, void* q_rot, void* k_rot,
+                      hipStream_t stream);
 
 /*
  * Forward: O = softmax(scale * Q K^T + causal/padding mask) V, and the fp32

@@ -22,6 +22,12 @@ of the rotated q and k) is the rotation by -a.
 
 Gradients: with q_r = R q and k_r = R k, attention's dQ_r and dK_r map back to
 dQ = R^T dQ_r and dK = R^T dK_r; dV is unchanged.
+
+Storage. In a bf16 pipeline ("Axis", Zyora Labs page, feature list: bf16
+storage, fp32 accumulation) the rotated q and k are tensors like any other and
+are stored in bf16 before attention reads them. ``bf16_storage=True`` rounds
+them to the nearest bf16 value (ties to even) at that point; the rest stays in
+the oracle's precision.
 """
 from __future__ import annotations
 
@@ -29,7 +35,7 @@ import numpy as np
 
 from . import attention
 
-__all__ = ["ROPE_BASE", "frequencies", "rotate", "forward", "backward"]
+__all__ = ["ROPE_BASE", "frequencies", "rotate", "round_bf16", "forward", "backward"]
 
 ROPE_BASE = 10000.0
 
@@ -62,21 +68,36 @@ def rotate(x, base: float = ROPE_BASE, positions=None, inverse: bool = False, dt
     return out
 
 
-def forward(q, k, v, scale: float, seqlens=None, base: float = ROPE_BASE, dtype=np.float64, causal: bool = True):
+def round_bf16(x):
+    """Nearest bf16 value (8 significant bits, ties to even) of each finite
+    normal-range element, kept in x's dtype."""
+    x = np.asarray(x)
+    m, e = np.frexp(x)                     # x = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e).astype(x.dtype)
+
+
+def _rotated(q, k, base, dtype, bf16_storage):
+    qr, kr = rotate(q, base, dtype=dtype), rotate(k, base, dtype=dtype)
+    if bf16_storage:
+        qr, kr = round_bf16(qr), round_bf16(kr)
+    return qr, kr
+
+
+def forward(q, k, v, scale: float, seqlens=None, base: float = ROPE_BASE, dtype=np.float64, causal: bool = True,
+            bf16_storage: bool = False):
     """Attention of the rotated q and k (oracle/attention.py's forward)."""
-    return attention.forward(rotate(q, base, dtype=dtype), rotate(k, base, dtype=dtype), v, scale, seqlens,
-                             dtype=dtype, causal=causal)
+    qr, kr = _rotated(q, k, base, dtype, bf16_storage)
+    return attention.forward(qr, kr, v, scale, seqlens, dtype=dtype, causal=causal)
 
 
 def backward(q, k, v, do, scale: float, seqlens=None, base: float = ROPE_BASE, dtype=np.float64,
-             causal: bool = True):
+             causal: bool = True, bf16_storage: bool = False):
     """Forward and backward of attention(rope(q), rope(k), v).
 
     Returns oracle/attention.py's backward dict with dQ and dK taken back
     through the rotation's adjoint (gradients with respect to the unrotated
     q and k), plus the rotated inputs as "Qrot" and "Krot"."""
-    qr = rotate(q, base, dtype=dtype)
-    kr = rotate(k, base, dtype=dtype)
+    qr, kr = _rotated(q, k, base, dtype, bf16_storage)
     ref = attention.backward(qr, kr, v, do, scale, seqlens, dtype=dtype, causal=causal)
     ref["dQ"] = rotate(ref["dQ"], base, inverse=True, dtype=dtype)
     ref["dK"] = rotate(ref["dK"], base, inverse=True, dtype=dtype)

@@ -51,10 +51,10 @@ def test_status_strings(lib):
 
 
 def _shape(**kw):
-    base = dict(B=2, S=128, Hq=4, Hkv=2, d=64, scale=0.125, seqlens_ptr=None, causal=1)
+    base = dict(B=2, S=128, Hq=4, Hkv=2, d=64, scale=0.125, seqlens_ptr=None, causal=1, rope_base=0.0)
     base.update(kw)
     return attn.make_shape(base["B"], base["S"], base["Hq"], base["Hkv"], base["d"], base["scale"],
-                           base["seqlens_ptr"], base["causal"])
+                           base["seqlens_ptr"], base["causal"], base["rope_base"])
 
 
 P = ctypes.c_void_p
@@ -79,6 +79,10 @@ def _dq(lib, shape, ptrs=(GOOD,) * 7):
     return lib.attn_bwd_dq(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], P(0))
 
 
+def _rope(lib, shape, ptrs=(GOOD,) * 4):
+    return lib.attn_rope(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], P(0))
+
+
 def _pre(lib, shape, ptrs=(GOOD,) * 3):
     return lib.attn_bwd_preprocess(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], P(0))
 
@@ -89,10 +93,12 @@ def _pre(lib, shape, ptrs=(GOOD,) * 3):
     (dict(scale=0.0), 1), (dict(scale=-0.1), 1),
     (dict(d=32), 2), (dict(d=96), 2), (dict(d=256), 2), (dict(causal=2), 1), (dict(causal=-1), 1),
     (dict(seqlens_ptr=GOOD + 2), 3),
+    (dict(rope_base=-1.0), 1), (dict(rope_base=float("nan")), 1), (dict(rope_base=float("inf")), 1),
     (dict(B=2 ** 30, S=2 ** 20), 2), (dict(Hq=2 ** 17, Hkv=1), 2), (dict(Hq=2 ** 16, Hkv=2 ** 16, d=128), 2),
 ])
 def test_invalid_shapes_rejected(lib, kw, code):
     shape = _shape(**kw)
+    assert _rope(lib, shape) == code
     assert _fwd(lib, shape) == code
     assert _pre(lib, shape) == code
     assert _bwd(lib, shape) == code
@@ -225,3 +231,17 @@ def test_decode_workspace_bytes_bounded_by_waves_and_units(lib):
     # a one-tile cache needs one wave per unit at most
     small = ws(B=B, Smax=64, Hq=Hq, Hkv=Hkv, d=d)
     assert small <= 256 + 256 + U * 8 + 256 + (2 * U) * R * (d + 1) * 4
+
+
+def test_rope_requires_a_base_and_valid_pointers(lib):
+    assert _rope(lib, None) == 1
+    assert _rope(lib, _shape()) == 1                      # rope_base = 0: nothing to rotate with
+    shape = _shape(rope_base=10000.0)
+    for i in range(4):
+        ptrs = [GOOD] * 4
+        ptrs[i] = 0
+        assert _rope(lib, shape, ptrs) == 1
+        ptrs[i] = ODD
+        assert _rope(lib, shape, ptrs) == 3
+    # a rope base is accepted by every attention entry point (validation only)
+    assert _fwd(lib, _shape(rope_base=10000.0, d=96)) == 2

@@ -158,3 +158,26 @@ def test_matches_torch_complex_rope_and_sdpa(causal, rp=oracle_rope):
     o, dq, dk, dv = _torch_rope_attention(q, k, v, do, scale, causal)
     for key, ref in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
         np.testing.assert_allclose(out[key], ref, atol=1e-10, rtol=0, err_msg=key)
+
+
+def test_bf16_rounding_matches_torch_conversion(rp=oracle_rope):
+    # values exactly representable in fp32, so torch's fp32 -> bf16 conversion
+    # (round to nearest, ties to even) rounds the same number once
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 3.0 * (1 + 2.0 ** -8)], np.float32)
+    x = np.concatenate([x, ties])
+    want = torch.tensor(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = rp.round_bf16(x.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(rp.round_bf16(np.array([1.0 + 2.0 ** -8])), [1.0])       # tie to even
+    np.testing.assert_array_equal(rp.round_bf16(np.array([1.0 + 3 * 2.0 ** -8])), [1.0 + 2.0 ** -6])
+
+
+def test_bf16_storage_rounds_only_the_rotated_inputs(rp=oracle_rope):
+    q, k, v, do = rand_inputs(1, 20, 2, 1, 8, seed=12)
+    exact = rp.backward(q, k, v, do, 0.3)
+    stored = rp.backward(q, k, v, do, 0.3, bf16_storage=True)
+    np.testing.assert_array_equal(stored["Qrot"], rp.round_bf16(exact["Qrot"]))
+    np.testing.assert_array_equal(stored["Krot"], rp.round_bf16(exact["Krot"]))
+    assert 0 < np.max(np.abs(stored["O"] - exact["O"])) < 1e-2
