@@ -104,8 +104,7 @@ ROPE_MUTATIONS = {
     "rope_half_split_pairs": ("even, odd = x[..., 0::2], x[..., 1::2]", "even, odd = x[..., :d // 2], x[..., d // 2:]"),
     "rope_backward_rotates_forward": ('ref["dQ"] = rotate(ref["dQ"], base, inverse=True', 'ref["dQ"] = rotate(ref["dQ"], base, inverse=False'),
     "rope_dK_not_taken_back": ('    ref["dK"] = rotate(ref["dK"], base, inverse=True, dtype=dtype)\n', ""),
-    "rope_values_rotated": ("kr = rotate(k, base, dtype=dtype)\n    ref = attention.backward(qr, kr, v,",
-                            "kr = rotate(k, base, dtype=dtype)\n    ref = attention.backward(qr, kr, rotate(v, base),"),
+    "rope_values_rotated": ("ref = attention.backward(qr, kr, v,", "ref = attention.backward(qr, kr, rotate(v, base),"),
 }
 
 
