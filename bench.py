@@ -255,7 +255,7 @@ def copy_calibration(args):
 
 # ----------------------------------------------------------------------------- the benchmark
 
-def cpu_baseline(w, inp, budget_s: float, causal: bool = True):
+def cpu_baseline(w, inp, budget_s: float, causal: bool = True, rope_base: float = 0.0):
     """The oracle (fp32 mode, untuned) on whole (sequence, kv head) units of the
     same workload until about `budget_s` seconds of CPU work have been spent."""
     import numpy as np
@@ -273,8 +273,12 @@ def cpu_baseline(w, inp, budget_s: float, causal: bool = True):
     done, flops, t0 = 0, 0.0, time.perf_counter()
     for b, g in units:
         hs = slice(g * G, (g + 1) * G)
-        oracle.backward(q[b:b + 1, :, hs], k[b:b + 1, :, g:g + 1], v[b:b + 1, :, g:g + 1], do[b:b + 1, :, hs],
-                        inp.scale, None if sl is None else sl[b:b + 1], dtype=np.float32, causal=causal)
+        args = (q[b:b + 1, :, hs], k[b:b + 1, :, g:g + 1], v[b:b + 1, :, g:g + 1], do[b:b + 1, :, hs],
+                inp.scale, None if sl is None else sl[b:b + 1])
+        if rope_base:
+            oracle.rope.backward(*args, base=rope_base, dtype=np.float32, causal=causal)
+        else:
+            oracle.backward(*args, dtype=np.float32, causal=causal)
         done += 1
         pairs = valid_pairs(w.S, 1, None if sl is None else sl[b:b + 1], causal)
         flops += 3.5 * 4.0 * w.d * G * pairs
@@ -309,27 +313,36 @@ def run(args):
     causal = not args.non_causal
     fl = algorithmic_flops(w, inp.seqlens, causal)
     cz = int(causal)
+    rb = args.rope_base if args.rope else 0.0
+    qa, ka = q, k
+    if args.rope:
+        # the rotated copies the forward and backward read (kept like saved activations)
+        qa, ka = torch.empty_like(q), torch.empty_like(k)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        attn.attn_fwd(q, k, v, o, lse, scale, sl, cz)
+        if args.rope:
+            attn.attn_rope(q, k, qa, ka, rb)
+        if ev is not None:
+            ev[5].record()
+        attn.attn_fwd(qa, ka, v, o, lse, scale, sl, cz)
         if ev is not None:
             ev[1].record()
         attn.attn_bwd_preprocess(o, do, delta, sl)
         if ev is not None:
             ev[2].record()
-        attn.attn_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, scale, sl, cz)
+        attn.attn_bwd_dkdv(qa, ka, v, do, lse, delta, dk, dv, scale, sl, cz, rb)
         if ev is not None:
             ev[3].record()
-        attn.attn_bwd_dq(q, k, v, do, lse, delta, dq, scale, sl, cz)
+        attn.attn_bwd_dq(qa, ka, v, do, lse, delta, dq, scale, sl, cz, rb)
         if ev is not None:
             ev[4].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
@@ -337,15 +350,21 @@ def run(args):
     wall = time.perf_counter() - t0
     names = ["fwd", "pre", "dkdv", "dq"]
     per = {n: 0.0 for n in names}
+    rope_ms = 0.0
     for ev in events:
-        for j, n in enumerate(names):
+        per["fwd"] += ev[5].elapsed_time(ev[1])
+        for j, n in enumerate(names[1:], start=1):
             per[n] += ev[j].elapsed_time(ev[j + 1])
+        rope_ms += ev[0].elapsed_time(ev[5])
     per = {n: per[n] / args.steps for n in names}           # ms per launch
+    rope_ms /= args.steps
     ms_step = wall * 1e3 / args.steps
     launch = "eager"
     if args.graph:
         # the same four launches captured in one HIP graph, replayed; the
         # per-kernel times above stay those of the eager launches
+        if args.rope:
+            sys.exit("--graph and --rope together are not supported")
         graph = attn.capture_step(q, k, v, do, o, lse, delta, dq, dk, dv, scale, sl, causal)
         for _ in range(args.warmup):
             graph.replay()
@@ -373,23 +392,25 @@ def run(args):
                 "frac": achieved / PEAK_BF16_TFLOPS}
     roof["kernel"] = KERNEL_NAMES[dom]
     roof["ms_per_launch"] = per[dom]
-    roof["traffic"] = read_traffic(dom, w.name) if causal else None
+    roof["traffic"] = read_traffic(dom, w.name) if (causal and not args.rope) else None
 
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": dict(w.describe(), causal=causal, launch=launch, valid_pairs_per_head=fl["pairs_per_head"],
-                       algorithmic_gflop_per_step=round(fl["total"] / 1e9, 3)),
+                       algorithmic_gflop_per_step=round(fl["total"] / 1e9, 3),
+                       rope_base=rb if args.rope else None),
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "kernel_ms": {KERNEL_NAMES[n]: round(per[n], 4) for n in names},
+        "kernel_ms": dict({KERNEL_NAMES[n]: round(per[n], 4) for n in names},
+                          **({"rope_kernel": round(rope_ms, 4)} if args.rope else {})),
         "kernel_tflops": {KERNEL_NAMES[n]: round(s / (per[n] * 1e-3) / 1e12, 1)
                           for n, s in (("fwd", fl["fwd"]), ("dkdv", fl["bwd_dkdv"]), ("dq", fl["bwd_dq"]))},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, causal)
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, causal, rb)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
@@ -506,6 +527,9 @@ def main():
                     help="time the step as one captured HIP graph (fwd, preprocess, dK/dV, dQ) replayed")
     ap.add_argument("--non-causal", action="store_true",
                     help="bidirectional attention (causal = 0): every key of the valid prefix, all pairs priced")
+    ap.add_argument("--rope", action="store_true",
+                    help="rotary position embedding: attn_rope pre-pass, backward with the fused adjoint")
+    ap.add_argument("--rope-base", type=float, default=10000.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--copy-bytes", type=float, default=1 << 30)
     ap.add_argument("--copy-kernel", default="copy")
