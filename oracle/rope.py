@@ -35,7 +35,7 @@ import numpy as np
 
 from . import attention
 
-__all__ = ["ROPE_BASE", "frequencies", "rotate", "round_bf16", "forward", "backward"]
+__all__ = ["ROPE_BASE", "frequencies", "rotate", "round_bf16", "forward", "backward", "decode"]
 
 ROPE_BASE = 10000.0
 
@@ -103,3 +103,22 @@ def backward(q, k, v, do, scale: float, seqlens=None, base: float = ROPE_BASE, d
     ref["dK"] = rotate(ref["dK"], base, inverse=True, dtype=dtype)
     ref["Qrot"], ref["Krot"] = qr, kr
     return ref
+
+
+def decode(q, k_cache, v_cache, scale: float, cache_lens=None, base: float = ROPE_BASE, dtype=np.float64,
+           bf16_storage: bool = False):
+    """Decode attention (oracle/attention.py's decode) with the new queries
+    rotated at their positions: query t of sequence b sits at position
+    p = L_b - Sq + t, the position its key was rotated at when it entered the
+    cache, so the cache holds keys already rotated and is used as it is.
+    ``bf16_storage`` rounds the rotated queries to bf16 (see the header)."""
+    q = np.asarray(q, dtype=dtype)
+    B, Sq, Hq, d = q.shape
+    lens = attention.lengths(B, np.asarray(k_cache).shape[1], cache_lens)
+    qr = np.empty_like(q)
+    for b in range(B):
+        pos = lens[b] - Sq + np.arange(Sq)
+        qr[b:b + 1] = rotate(q[b:b + 1], base, positions=pos, dtype=dtype)
+    if bf16_storage:
+        qr = round_bf16(qr)
+    return attention.decode(qr, k_cache, v_cache, scale, cache_lens, dtype=dtype)

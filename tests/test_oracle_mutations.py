@@ -104,6 +104,7 @@ ROPE_MUTATIONS = {
     "rope_half_split_pairs": ("even, odd = x[..., 0::2], x[..., 1::2]", "even, odd = x[..., :d // 2], x[..., d // 2:]"),
     "rope_backward_rotates_forward": ('ref["dQ"] = rotate(ref["dQ"], base, inverse=True', 'ref["dQ"] = rotate(ref["dQ"], base, inverse=False'),
     "rope_dK_not_taken_back": ('    ref["dK"] = rotate(ref["dK"], base, inverse=True, dtype=dtype)\n', ""),
+    "rope_decode_position_off_by_one": ("pos = lens[b] - Sq + np.arange(Sq)", "pos = lens[b] - Sq + 1 + np.arange(Sq)"),
     "rope_values_rotated": ("ref = attention.backward(qr, kr, v,", "ref = attention.backward(qr, kr, rotate(v, base),"),
 }
 
@@ -124,6 +125,7 @@ def _rope_pins(rp):
     yield lambda: rpins.test_scores_depend_only_on_relative_position(rp)
     yield lambda: rpins.test_central_differences_through_rope(1, 5, 2, 1, 4, None, True, rp)
     yield lambda: rpins.test_matches_torch_complex_rope_and_sdpa(True, rp)
+    yield lambda: rpins.test_decode_equals_last_rows_of_rope_forward(3, 4, 33, 6, 2, 16, [33, 4, 9], rp)
 
 
 def test_unmutated_rope_copy_passes_every_pin():

@@ -181,3 +181,43 @@ def test_bf16_storage_rounds_only_the_rotated_inputs(rp=oracle_rope):
     np.testing.assert_array_equal(stored["Qrot"], rp.round_bf16(exact["Qrot"]))
     np.testing.assert_array_equal(stored["Krot"], rp.round_bf16(exact["Krot"]))
     assert 0 < np.max(np.abs(stored["O"] - exact["O"])) < 1e-2
+
+
+@pytest.mark.parametrize("B,Sq,S,Hq,Hkv,d,lens", [
+    (2, 1, 40, 4, 2, 8, [40, 17]),
+    (3, 4, 33, 6, 2, 16, [33, 4, 9]),
+    (1, 3, 70, 2, 1, 32, [70]),
+])
+def test_decode_equals_last_rows_of_rope_forward(B, Sq, S, Hq, Hkv, d, lens, rp=oracle_rope):
+    # a cache holding keys rotated at their positions, queried by the last Sq
+    # queries of each sequence, gives the last Sq rows of the causal rope
+    # forward over the whole valid prefix
+    q, k, v, _ = rand_inputs(B, S, Hq, Hkv, d, seed=S + Sq)
+    scale = 1.0 / math.sqrt(d)
+    cache = rp.rotate(k)
+    qn = np.zeros((B, Sq, Hq, d))
+    for b, L in enumerate(lens):
+        for t in range(Sq):
+            if L - Sq + t >= 0:
+                qn[b, t] = q[b, L - Sq + t]
+    O, LSE = rp.decode(qn, cache, v, scale, lens)
+    for b, L in enumerate(lens):
+        Of, LSEf = rp.forward(q[b:b + 1, :L], k[b:b + 1, :L], v[b:b + 1, :L], scale)
+        for t in range(Sq):
+            p = L - Sq + t
+            if p < 0:
+                assert np.all(O[b, t] == 0) and np.all(np.isneginf(LSE[b, :, t]))
+                continue
+            np.testing.assert_allclose(O[b, t], Of[0, p], atol=1e-12, rtol=0)
+            np.testing.assert_allclose(LSE[b, :, t], LSEf[0, :, p], atol=1e-12, rtol=0)
+
+
+def test_decode_at_position_zero_is_plain_decode(rp=oracle_rope):
+    import oracle
+    q, k, v, _ = rand_inputs(3, 1, 4, 2, 16, seed=5)
+    kc = np.random.default_rng(6).standard_normal((3, 9, 2, 16))
+    vc = np.random.default_rng(7).standard_normal((3, 9, 2, 16))
+    O, LSE = rp.decode(q, kc, vc, 0.25, [1, 1, 1])
+    O2, LSE2 = oracle.decode(q, kc, vc, 0.25, [1, 1, 1])
+    np.testing.assert_array_equal(O, O2)
+    np.testing.assert_array_equal(LSE, LSE2)
