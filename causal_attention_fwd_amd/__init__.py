@@ -56,7 +56,7 @@ class AttnShape(ctypes.Structure):
 class AttnDecodeShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("cache_len", ctypes.c_int32),
                 ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("cache_lens", ctypes.c_void_p)]
+                ("scale", ctypes.c_float), ("cache_lens", ctypes.c_void_p), ("rope_base", ctypes.c_float)]
 
 
 def library_path() -> str:
@@ -260,9 +260,9 @@ def attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale: float, seqlens=None, causal
 # ------------------------------------------------------------------ decode
 
 def make_decode_shape(B: int, Sq: int, Smax: int, Hq: int, Hkv: int, d: int, scale: float,
-                      cache_lens_ptr: Optional[int] = None) -> AttnDecodeShape:
+                      cache_lens_ptr: Optional[int] = None, rope_base: float = 0.0) -> AttnDecodeShape:
     return AttnDecodeShape(int(B), int(Sq), int(Smax), int(Hq), int(Hkv), int(d), float(scale),
-                           ctypes.c_void_p(cache_lens_ptr) if cache_lens_ptr else None)
+                           ctypes.c_void_p(cache_lens_ptr) if cache_lens_ptr else None, float(rope_base or 0.0))
 
 
 def attn_decode_workspace_bytes(B: int, Sq: int, Smax: int, Hq: int, Hkv: int, d: int) -> int:
@@ -270,15 +270,17 @@ def attn_decode_workspace_bytes(B: int, Sq: int, Smax: int, Hq: int, Hkv: int, d
     return int(load_library().attn_decode_workspace_bytes(ctypes.byref(shape)))
 
 
-def attn_decode(q, k_cache, v_cache, o, lse, scale: float, cache_lens=None, workspace=None):
-    """O, LSE <- decode attention of q [B,Sq,Hq,d] against the caches [B,Smax,Hkv,d]."""
+def attn_decode(q, k_cache, v_cache, o, lse, scale: float, cache_lens=None, workspace=None, rope_base: float = 0.0):
+    """O, LSE <- decode attention of q [B,Sq,Hq,d] against the caches [B,Smax,Hkv,d]
+    (with rope_base > 0 the queries are rotated at their positions; the cache
+    holds rotated keys)."""
     torch = _torch()
     if q.dim() != 4 or k_cache.dim() != 4:
         raise ValueError("q must be [B,Sq,Hq,d] and the caches [B,Smax,Hkv,d]")
     B, Sq, Hq, d = q.shape
     Smax, Hkv = k_cache.shape[1], k_cache.shape[2]
     lens = _check_gpu("cache_lens", cache_lens, torch.int32, (B,)) if cache_lens is not None else None
-    shape = make_decode_shape(B, Sq, Smax, Hq, Hkv, d, scale, lens)
+    shape = make_decode_shape(B, Sq, Smax, Hq, Hkv, d, scale, lens, rope_base)
     ptrs = [_check_gpu("q", q, torch.bfloat16, (B, Sq, Hq, d)),
             _check_gpu("k_cache", k_cache, torch.bfloat16, (B, Smax, Hkv, d)),
             _check_gpu("v_cache", v_cache, torch.bfloat16, (B, Smax, Hkv, d)),
@@ -292,7 +294,7 @@ def attn_decode(q, k_cache, v_cache, o, lse, scale: float, cache_lens=None, work
           ctypes.c_void_p(ws), ctypes.c_size_t(nbytes), _stream())
 
 
-def decode(q, k_cache, v_cache, scale: Optional[float] = None, cache_lens=None):
+def decode(q, k_cache, v_cache, scale: Optional[float] = None, cache_lens=None, rope_base: float = 0.0):
     """Returns (O, LSE) of decode attention as new tensors (allocates the workspace)."""
     torch = _torch()
     B, Sq, Hq, d = q.shape
@@ -302,7 +304,7 @@ def decode(q, k_cache, v_cache, scale: Optional[float] = None, cache_lens=None):
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     need = attn_decode_workspace_bytes(B, Sq, k_cache.shape[1], Hq, k_cache.shape[2], d)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    attn_decode(q, k_cache, v_cache, o, lse, scale, cache_lens, ws)
+    attn_decode(q, k_cache, v_cache, o, lse, scale, cache_lens, ws, rope_base)
     return o, lse
 
 

@@ -44,8 +44,7 @@ attn_status check_decode_shape(const attn_decode_shape* s, attn::DecodeProblem* 
   if (s->heads_q % s->heads_kv != 0) return ATTN_ERR_INVALID_ARG;
   if (!(isfinite(s->scale) && s->scale > 0.f)) return ATTN_ERR_INVALID_ARG;
   if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
-  // one 32-row block of query rows per kv head
-  if ((int64_t)s->q_len * (s->heads_q / s->heads_kv) > 32) return ATTN_ERR_UNSUPPORTED;
+  if (!(isfinite(s->rope_base) && s->rope_base >= 0.f)) return ATTN_ERR_INVALID_ARG;
   if (s->cache_lens && (reinterpret_cast<uintptr_t>(s->cache_lens) & 3u) != 0) return ATTN_ERR_MISALIGNED;
   // 32-bit tile offsets (as for the training path) and grid size
   if ((int64_t)s->heads_kv * s->head_dim > (int64_t)1 << 22) return ATTN_ERR_UNSUPPORTED;
@@ -57,8 +56,12 @@ attn_status check_decode_shape(const attn_decode_shape* s, attn::DecodeProblem* 
   pr->d = s->head_dim;
   pr->scale = s->scale;
   pr->cache_lens = s->cache_lens;
-  // the count of valid 64-key tiles over all units is a 32-bit int on the device
-  if ((int64_t)s->batch * s->heads_kv * ((s->cache_len + 63) / 64) > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  pr->rope_base = s->rope_base;
+  // the count of valid 64-key tiles over all units (one per kv head and
+  // 32-row block of its query rows) is a 32-bit int on the device
+  const int64_t row_blocks = ((int64_t)s->q_len * (s->heads_q / s->heads_kv) + 31) / 32;
+  if ((int64_t)s->batch * s->heads_kv * row_blocks * ((s->cache_len + 63) / 64) > 0x7fffffffLL)
+    return ATTN_ERR_UNSUPPORTED;
   if (((int64_t)s->batch * s->heads_q * s->q_len + 3) / 4 > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }

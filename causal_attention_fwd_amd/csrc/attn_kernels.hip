@@ -881,10 +881,11 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a) {
 
 // ----------------------------------------------------------------------------
 // Decode. Sq new queries per sequence (the last Sq cached positions) against a
-// [B, Smax, Hkv, d] key/value cache. A unit is one (sequence, kv head); its
-// R = G*Sq query rows (row r: head r / Sq of the group, new query r % Sq) form
-// one 32-row block (rows past R are empty). The valid 64-key tiles of all
-// units, laid end to end (sequence-major, then kv head), are dealt out evenly
+// [B, Smax, Hkv, d] key/value cache. The R = G*Sq query rows of a kv head (row
+// r: head r / Sq of the group, new query r % Sq) are cut into RB blocks of 32
+// MFMA rows; a unit is one (sequence, kv head, row block). The valid 64-key
+// tiles of all units, laid end to end (sequence-major, then kv head, then row
+// block), are dealt out evenly
 // to the W one-wave workgroups of the grid: wave w takes tiles
 // [floor(w*T/W), floor((w+1)*T/W)) of the T in total, so every wave streams
 // the same number of bytes whatever the mix of cache lengths. A wave's range
@@ -903,12 +904,15 @@ struct DecArgs {
   const int32_t* lens;
   int* hdr;       // hdr[0] = T, the number of valid tiles over all units
   int2* uinfo;    // per unit: first and last wave holding a partial of it
-  float* ws_o;    // [slots, R, D]
-  float* ws_lse;  // [slots, R]
+  float* ws_o;    // [slots, RU, D]
+  float* ws_lse;  // [slots, RU]
   bf16* o;        // [B, Sq, Hq, D]
   float* lse;     // [B, Hq, Sq]
   int B, Sq, Smax, Hq, Hkv, W;
+  int RB, RU;     // row blocks per kv head; partial rows per slot (R if RB = 1, else 32)
   float scale;
+  int rope;       // 1: query t is rotated at position L - Sq + t before use
+  RopeFreq rf;
 };
 
 // Valid 64-key tiles of each unit of sequence b.
@@ -936,11 +940,12 @@ __device__ __forceinline__ int wave_scan_incl_i(int x, int lane) {
   return x;
 }
 
-// One unit's share of a wave: local tiles [s0, s1) of unit (b, hkv), partial
-// result to slot `slot`.
+// One unit's share of a wave: local tiles [s0, s1) of unit (b, hkv, rb),
+// partial result to slot `slot`.
 template <int D, int STAGES>
-__device__ __forceinline__ void decode_segment(const DecArgs& a, int b, int hkv, int s0, int s1, int64_t slot,
-                                               bf16* sK0, bf16* sV0, bf16* sK1, bf16* sV1, int lane) {
+__device__ __forceinline__ void decode_segment(const DecArgs& a, int b, int hkv, int rb, int s0, int s1,
+                                               int64_t slot, bf16* sK0, bf16* sV0, bf16* sK1, bf16* sV1,
+                                               int lane) {
   constexpr int BN = 64;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
@@ -952,20 +957,35 @@ __device__ __forceinline__ void decode_segment(const DecArgs& a, int b, int hkv,
   const bf16* Kb = a.k + ((int64_t)b * a.Smax * a.Hkv + hkv) * D;
   const bf16* Vb = a.v + ((int64_t)b * a.Smax * a.Hkv + hkv) * D;
 
-  // the lane's query row: head hkv*G + r / Sq, new query t = r % Sq at cache
-  // position L - Sq + t, which sees keys 0 .. L - Sq + t
+  // the lane's query row rr = 32*rb + r: head hkv*G + rr / Sq, new query
+  // t = rr % Sq at cache position L - Sq + t, which sees keys 0 .. L - Sq + t
   const int r = lane & 31;
-  const bool row_ok = r < R;
-  const int hh = row_ok ? r / a.Sq : 0;
-  const int t = row_ok ? r - hh * a.Sq : 0;
+  const int rr = rb * 32 + r;
+  const bool row_ok = rr < R;
+  const int hh = row_ok ? rr / a.Sq : 0;
+  const int t = row_ok ? rr - hh * a.Sq : 0;
   const int h = hkv * G + hh;
   const int jmax = row_ok ? L - a.Sq + t : -1;  // last visible key (< 0: none)
 
   FwdState<D, 1> st;
   const bf16* qrow = a.q + (((int64_t)b * a.Sq + t) * a.Hq + h) * D;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    st.qf[0][kk] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + g * 8) : zero_bf16x8();
+  for (int kk = 0; kk < KK; ++kk) {
+    bf16x8 qv = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + g * 8) : zero_bf16x8();
+    if (a.rope) {
+      // pairs kk*8 + 4g + e of the lane's 8 elements, rotated at the query's
+      // position and stored back in bf16 (the rotated query is a bf16 tensor)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float cs, sn;
+        rope_cos_sin(g ? a.rf.phi[kk * 8 + 4 + e] : a.rf.phi[kk * 8 + e], L - a.Sq + t, cs, sn);
+        const float x0 = (float)qv[2 * e], x1 = (float)qv[2 * e + 1];
+        qv[2 * e] = (bf16)(x0 * cs - x1 * sn);
+        qv[2 * e + 1] = (bf16)(x0 * sn + x1 * cs);
+      }
+    }
+    st.qf[0][kk] = qv;
+  }
   st.mu[0] = kNegInf;
   st.lsum[0] = 0.f;
 #pragma unroll
@@ -1009,7 +1029,7 @@ __device__ __forceinline__ void decode_segment(const DecArgs& a, int b, int hkv,
   // partial result: O / l (fp32) and LSE = mu*scale + ln l
   const float lt = xhalf_sum(st.lsum[0]);
   if (row_ok) {
-    const int64_t prow = slot * R + r;
+    const int64_t prow = slot * a.RU + r;
     const bool any = lt > 0.f;
     const float inv = any ? 1.f / lt : 0.f;
     float* wo = a.ws_o + prow * D;
@@ -1037,9 +1057,10 @@ void decode_split_kernel(DecArgs a) {
   const int lane = threadIdx.x;
   const int w = blockIdx.x;
 
+  const int HU = a.Hkv * a.RB;  // units per sequence
   // T: valid tiles over all units (every wave counts them; wave 0 publishes)
   int part = 0;
-  for (int b = lane; b < a.B; b += 64) part += dec_tiles(a, b) * a.Hkv;
+  for (int b = lane; b < a.B; b += 64) part += dec_tiles(a, b) * HU;
   const int T = wave_sum_i(part);
   if (w == 0 && lane == 0) a.hdr[0] = T;
   int tb = dec_start(w, T, a.W);
@@ -1049,7 +1070,7 @@ void decode_split_kernel(DecArgs a) {
   // the sequence holding tile tb: the first whose inclusive tile prefix exceeds it
   int b = -1, before = 0;  // before: tiles of the sequences ahead of b
   for (int base = 0; base < a.B; base += 64) {
-    const int x = base + lane < a.B ? dec_tiles(a, base + lane) * a.Hkv : 0;
+    const int x = base + lane < a.B ? dec_tiles(a, base + lane) * HU : 0;
     const int incl = wave_scan_incl_i(x, lane) + before;
     const uint64_t hit = __ballot(incl > tb);
     if (hit) {
@@ -1063,13 +1084,13 @@ void decode_split_kernel(DecArgs a) {
   if (b < 0) return;  // unreachable while tb < T
 
   int nt = dec_tiles(a, b);  // > 0: sequence b holds tile tb
-  int hkv = (tb - before) / nt;
-  int ustart = before + hkv * nt;
+  int hu = (tb - before) / nt;  // unit of the sequence: kv head hu / RB, row block hu % RB
+  int ustart = before + hu * nt;
   for (;;) {
-    const int64_t u = (int64_t)b * a.Hkv + hkv;
+    const int64_t u = (int64_t)b * HU + hu;
     const int s0 = tb - ustart;
     const int s1 = min(te, ustart + nt) - ustart;
-    decode_segment<D, STAGES>(a, b, hkv, s0, s1, w + u, sK0, sV0, sK1, sV1, lane);
+    decode_segment<D, STAGES>(a, b, hu / a.RB, hu % a.RB, s0, s1, w + u, sK0, sV0, sK1, sV1, lane);
     if (lane == 0) {
       if (s0 == 0) a.uinfo[u].x = w;
       if (s1 == nt) a.uinfo[u].y = w;
@@ -1077,8 +1098,8 @@ void decode_split_kernel(DecArgs a) {
     tb = ustart + s1;
     if (tb >= te) break;
     ustart += nt;
-    if (++hkv == a.Hkv) {  // next sequence with a non-empty cache
-      hkv = 0;
+    if (++hu == HU) {  // next sequence with a non-empty cache
+      hu = 0;
       do {
         ++b;
       } while (b < a.B && (nt = dec_tiles(a, b)) == 0);
@@ -1104,10 +1125,11 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecArgs a) {
   const int h = (int)(bh % a.Hq);
   const int b = (int)(bh / a.Hq);
   const int G = a.Hq / a.Hkv;
-  const int R = G * a.Sq;
   const int hkv = h / G;
-  const int r = (h - hkv * G) * a.Sq + t;
-  const int64_t u = (int64_t)b * a.Hkv + hkv;
+  const int rr = (h - hkv * G) * a.Sq + t;  // row within the kv head's rows
+  const int r = rr & 31;
+  const int64_t u = ((int64_t)b * a.Hkv + hkv) * a.RB + (rr >> 5);
+  const int R = a.RU;  // partial rows per slot
   float m = kNegInf;
   float acc[PER] = {};
   float den = 0.f;
@@ -1208,6 +1230,14 @@ template <> struct Tiles<128> {
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// phi_i = base^(-2i/d) / (2 pi) in fp64; zeros when base is 0 (no rotation)
+RopeFreq rope_freq_d(float base, int d) {
+  RopeFreq rf{};
+  if (base > 0.f)
+    for (int i = 0; i < d / 2; ++i) rf.phi[i] = std::pow((double)base, -2.0 * i / d) / (2.0 * 3.14159265358979323846);
+  return rf;
+}
+
 template <typename Args>
 hipError_t launch(const void* fn, int64_t grid, Args args, hipStream_t stream, int threads = kThreads) {
   if (grid <= 0) return hipSuccess;
@@ -1216,13 +1246,7 @@ hipError_t launch(const void* fn, int64_t grid, Args args, hipStream_t stream, i
 }
 
 // phi_i = base^(-2i/d) / (2 pi), in fp64 (zeros when RoPE is off)
-RopeFreq rope_freq(const Problem& pr) {
-  RopeFreq rf{};
-  if (pr.rope_base > 0.f)
-    for (int i = 0; i < pr.d / 2; ++i)
-      rf.phi[i] = std::pow((double)pr.rope_base, -2.0 * i / pr.d) / (2.0 * 3.14159265358979323846);
-  return rf;
-}
+RopeFreq rope_freq(const Problem& pr) { return rope_freq_d(pr.rope_base, pr.d); }
 
 template <int D>
 hipError_t fwd_d(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -1329,12 +1353,15 @@ DecodePlan plan_decode(const DecodeProblem& pr) {
   // but no more than there can be tiles
   constexpr int kCUs = 256;
   const int per_cu = (pr.d == 64 ? 8 : 4) / ATTN_DEC_STAGES;
-  const int64_t tmax = (int64_t)pr.B * pr.Hkv * ((pr.Smax + 63) / 64);
+  const int64_t rows = (int64_t)(pr.Hq / pr.Hkv) * pr.Sq;  // query rows per kv head
   DecodePlan plan;
+  plan.rb = (int)((rows + 31) / 32);
+  plan.ru = plan.rb == 1 ? (int)rows : 32;
+  const int64_t units = (int64_t)pr.B * pr.Hkv * plan.rb;
+  const int64_t tmax = units * ((pr.Smax + 63) / 64);
   plan.waves = (int)std::min<int64_t>((int64_t)kCUs * per_cu * ATTN_DEC_ROUNDS, tmax);
-  const int64_t units = (int64_t)pr.B * pr.Hkv;
   const int64_t slots = plan.waves + units - 1;
-  const int64_t R = (int64_t)(pr.Hq / pr.Hkv) * pr.Sq;
+  const int64_t R = plan.ru;
   plan.off_uinfo = 256;
   plan.off_lse = plan.off_uinfo + align256((size_t)units * 8);
   plan.off_o = plan.off_lse + align256((size_t)(slots * R) * sizeof(float));
@@ -1348,7 +1375,8 @@ hipError_t launch_decode(const DecodeProblem& pr, const DecodePlan& plan, const 
   DecArgs a{(const bf16*)q, (const bf16*)k_cache, (const bf16*)v_cache, pr.cache_lens,
             reinterpret_cast<int*>(ws), reinterpret_cast<int2*>(ws + plan.off_uinfo),
             reinterpret_cast<float*>(ws + plan.off_o), reinterpret_cast<float*>(ws + plan.off_lse),
-            (bf16*)o, lse, pr.B, pr.Sq, pr.Smax, pr.Hq, pr.Hkv, plan.waves, pr.scale};
+            (bf16*)o, lse, pr.B, pr.Sq, pr.Smax, pr.Hq, pr.Hkv, plan.waves, plan.rb, plan.ru, pr.scale,
+            pr.rope_base > 0.f, rope_freq_d(pr.rope_base, pr.d)};
   const int64_t merge_blocks = ((int64_t)pr.B * pr.Hq * pr.Sq + 3) / 4;
   hipError_t e;
   if (pr.d == 64) {

@@ -34,6 +34,7 @@ struct DecodeProblem {
   int B, Sq, Smax, Hq, Hkv, d;
   float scale;
   const int32_t* cache_lens;  // device int32[B] or nullptr (= Smax)
+  float rope_base;            // > 0: new queries rotated at their positions; 0: none
 };
 
 // How the decode work is dealt out: `waves` one-wave workgroups share the
@@ -42,6 +43,7 @@ struct DecodeProblem {
 // log-sum-exp. Workspace: a header, per-unit wave bounds, the partials.
 struct DecodePlan {
   int waves;
+  int rb, ru;  // 32-row blocks per kv head; partial rows per slot
   size_t off_uinfo, off_lse, off_o;
   size_t workspace_bytes;
 };

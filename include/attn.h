@@ -171,10 +171,14 @@ attn_status attn_bwd_dq(const attn_shape* shape, const void* q, const void* k, c
  *   LSE_t = ln sum_{j <= p} exp(scale <q_t, k_j>),
  *   O_t   = sum_{j <= p} exp(scale <q_t, k_j> - LSE_t) v_j,
  * with O_t = 0 and LSE_t = -inf when p < 0 (the query sees no key).
+ * With rope_base > 0 the cache holds keys already rotated at their positions
+ * (see attn_rope) and each new query is rotated at its position p before use
+ * (the rotated query is rounded to bf16, like any stored tensor).
  */
 typedef struct attn_decode_shape {
   int32_t batch;       /* B >= 1 */
-  int32_t q_len;       /* Sq >= 1 new queries per sequence; Sq * (Hq / Hkv) <= 32 */
+  int32_t q_len;       /* Sq >= 1 new queries per sequence (the Sq * Hq / Hkv
+                          query rows of a kv head run in blocks of 32) */
   int32_t cache_len;   /* Smax >= 1: cache capacity (positions) per sequence */
   int32_t heads_q;     /* Hq >= 1, a multiple of heads_kv */
   int32_t heads_kv;    /* Hkv >= 1 */
@@ -184,15 +188,20 @@ typedef struct attn_decode_shape {
      into [0, Smax] on the device; NULL means L_b = Smax. Positions >= L_b may
      hold any bits (including NaN). */
   const int32_t* cache_lens;
+  /* Rotary embedding base for the new queries, or 0 for none (finite and
+     >= 0, else ATTN_ERR_INVALID_ARG). */
+  float rope_base;
 } attn_decode_shape;
 
 /*
- * Bytes of device workspace attn_decode needs. The valid 64-key tiles of all
- * (sequence, kv head) units are shared evenly by W <= 1024 waves (fewer when
- * there are fewer tiles); each wave leaves one partial result, (d + 1) floats
- * per query row, for each unit it touches, so the workspace holds
- * (W + B * Hkv - 1) * (Hq / Hkv) * Sq * (d + 1) floats plus an 8-byte record
- * per unit and a small header; it does not grow with Smax once W is capped.
+ * Bytes of device workspace attn_decode needs. A unit is one (sequence, kv
+ * head, block of up to 32 of the kv head's R = Sq * Hq / Hkv query rows);
+ * U = B * Hkv * ceil(R / 32). The valid 64-key tiles of all units are shared
+ * evenly by W <= 1024 waves (fewer when there are fewer tiles); each wave
+ * leaves one partial result, (d + 1) floats per row, for each unit it
+ * touches, so the workspace holds (W + U - 1) * min(R, 32) * (d + 1) floats
+ * plus an 8-byte record per unit and a small header; it does not grow with
+ * Smax once W is capped.
  * Returns 0 for a NULL or invalid shape.
  */
 size_t attn_decode_workspace_bytes(const attn_decode_shape* shape);

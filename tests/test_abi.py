@@ -178,10 +178,10 @@ def test_product_path_never_uses_the_oracle():
 # ------------------------------------------------------------------ decode
 
 def _dshape(**kw):
-    base = dict(B=2, Sq=1, Smax=256, Hq=8, Hkv=2, d=64, scale=0.125, lens_ptr=None)
+    base = dict(B=2, Sq=1, Smax=256, Hq=8, Hkv=2, d=64, scale=0.125, lens_ptr=None, rope_base=0.0)
     base.update(kw)
     return attn.make_decode_shape(base["B"], base["Sq"], base["Smax"], base["Hq"], base["Hkv"], base["d"],
-                                  base["scale"], base["lens_ptr"])
+                                  base["scale"], base["lens_ptr"], base["rope_base"])
 
 
 def _dec(lib, shape, ptrs=(GOOD,) * 5, ws=None, ws_bytes=0):
@@ -192,8 +192,9 @@ def _dec(lib, shape, ptrs=(GOOD,) * 5, ws=None, ws_bytes=0):
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), 1), (dict(Sq=0), 1), (dict(Smax=0), 1), (dict(Hq=0), 1), (dict(Hkv=0), 1), (dict(Smax=-3), 1),
     (dict(Hq=6, Hkv=4), 1), (dict(scale=float("nan")), 1), (dict(scale=0.0), 1), (dict(scale=-1.0), 1),
-    (dict(d=32), 2), (dict(d=96), 2), (dict(Sq=5, Hq=16, Hkv=2), 2), (dict(Sq=1, Hq=33, Hkv=1), 2),
+    (dict(d=32), 2), (dict(d=96), 2), (dict(rope_base=-1.0), 1), (dict(rope_base=float("nan")), 1),
     (dict(lens_ptr=GOOD + 2), 3), (dict(Hq=2 ** 16, Hkv=2 ** 16, d=128), 2),
+    (dict(B=2 ** 20, Sq=64, Hq=64, Hkv=8, Smax=2 ** 16), 2),
 ])
 def test_decode_invalid_shapes_rejected(lib, kw, code):
     shape = _dshape(**kw)
@@ -223,14 +224,16 @@ def test_decode_workspace_bytes_bounded_by_waves_and_units(lib):
     # the wave count is capped, so the workspace does not grow with the cache
     def ws(**kw):
         return lib.attn_decode_workspace_bytes(ctypes.byref(_dshape(**kw)))
-    B, Hq, Hkv, d = 4, 32, 8, 64
-    R, U = Hq // Hkv, B * Hkv
-    big = [ws(B=B, Smax=Smax, Hq=Hq, Hkv=Hkv, d=d) for Smax in (1 << 14, 1 << 16, 1 << 20)]
-    assert big[0] == big[1] == big[2]
-    assert big[0] <= 256 + 256 + U * 8 + 256 + (4096 + U) * R * (d + 1) * 4
-    # a one-tile cache needs one wave per unit at most
-    small = ws(B=B, Smax=64, Hq=Hq, Hkv=Hkv, d=d)
-    assert small <= 256 + 256 + U * 8 + 256 + (2 * U) * R * (d + 1) * 4
+    for B, Sq, Hq, Hkv, d in ((4, 1, 32, 8, 64), (3, 8, 32, 4, 128), (2, 5, 20, 2, 64)):
+        R = Sq * Hq // Hkv
+        RB = -(-R // 32)
+        RU, U = (R if RB == 1 else 32), B * Hkv * RB
+        big = [ws(B=B, Sq=Sq, Smax=Smax, Hq=Hq, Hkv=Hkv, d=d) for Smax in (1 << 14, 1 << 16, 1 << 20)]
+        assert big[0] == big[1] == big[2]
+        assert big[0] <= 256 + 256 + U * 8 + 256 + (1024 + U) * RU * (d + 1) * 4
+        # a one-tile cache needs one wave per unit at most
+        small = ws(B=B, Sq=Sq, Smax=64, Hq=Hq, Hkv=Hkv, d=d)
+        assert small <= 256 + 256 + U * 8 + 256 + (2 * U) * RU * (d + 1) * 4
 
 
 def test_rope_requires_a_base_and_valid_pointers(lib):

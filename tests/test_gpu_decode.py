@@ -17,25 +17,29 @@ from attn_workloads import DECODE_WORKLOADS, decode_workload_inputs, make_decode
 from parity import TOL_LSE, TOL_MAX_ABS, TOL_REL_FRO, metrics, say
 
 import oracle
+from oracle import rope as oracle_rope
 
 pytestmark = pytest.mark.gpu
 
 
-def run_decode(inp, ws_extra=0):
+def run_decode(inp, rope_base=0.0):
     dev = torch.device("cuda")
     q = inp.q.to(dev).contiguous()
     k = inp.k_cache.to(dev).contiguous()
     v = inp.v_cache.to(dev).contiguous()
     lens = inp.cache_lens.to(dev) if inp.cache_lens is not None else None
-    o, lse = attn.decode(q, k, v, inp.scale, lens)
+    o, lse = attn.decode(q, k, v, inp.scale, lens, rope_base)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), lse.float().cpu().numpy()
 
 
-def ref_decode(inp):
+def ref_decode(inp, rope_base=0.0):
     lens = inp.cache_lens.numpy() if inp.cache_lens is not None else None
-    return oracle.decode(inp.q.float().numpy(), inp.k_cache.float().numpy(), inp.v_cache.float().numpy(),
-                         inp.scale, lens)
+    args = (inp.q.float().numpy(), inp.k_cache.float().numpy(), inp.v_cache.float().numpy(), inp.scale, lens)
+    if rope_base:
+        # the rotated queries are bf16 tensors in the pipeline
+        return oracle_rope.decode(*args, base=rope_base, bf16_storage=True)
+    return oracle.decode(*args)
 
 
 def check(got, ref, label):
@@ -71,6 +75,11 @@ CASES = [
     # one unit shared by every wave (over a thousand partials to merge)
     (1, 1, 131072, 8, 1, 64, None),
     (2, 1, 70000, 16, 2, 128, (30000, 70000)),
+    # more than 32 query rows per kv head: several 32-row blocks per head
+    (2, 33, 300, 1, 1, 64, (20, 300)),
+    (3, 8, 700, 32, 4, 64, (0, 700)),
+    (2, 16, 1000, 8, 1, 128, (5, 1000)),
+    (1, 100, 257, 4, 2, 64, None),
 ]
 
 
@@ -145,3 +154,40 @@ def test_decode_deterministic_and_workspace_reuse():
         attn.attn_decode(q, k, v, o, lse, small.scale, small.cache_lens.to(dev), ws)
         torch.cuda.synchronize()
         check((o.float().cpu().numpy(), lse.cpu().numpy()), ref_decode(small), f"decode-reuse B={B}")
+
+
+ROPE_CASES = [
+    (2, 1, 500, 8, 2, 64, (1, 500)),
+    (3, 4, 300, 16, 4, 128, (0, 300)),
+    (2, 2, 70000, 16, 8, 64, (60000, 70000)),
+    (1, 40, 128, 4, 1, 64, None),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=lambda c: "B{}_Sq{}_S{}_H{}-{}_d{}".format(*c[:6]))
+def test_decode_with_rope_every_element(case):
+    B, Sq, Smax, Hq, Hkv, d, rng = case
+    seed = 7700 + B + Sq + Smax + d
+    say(f"decode rope case B={B} Sq={Sq} Smax={Smax} Hq={Hq} Hkv={Hkv} d={d} lens={rng} seed={seed}")
+    inp = make_decode_inputs(B, Sq, Smax, Hq, Hkv, d, seed, rng)
+    check(run_decode(inp, 10000.0), ref_decode(inp, 10000.0), f"decode-rope{case}")
+
+
+def test_decode_rope_matches_rotated_queries_without_rope():
+    # the kernel's own rotation equals rotating the queries (attn_rope at the
+    # same positions) and decoding without it: here every sequence is full,
+    # so query t sits at position Smax - Sq + t
+    B, Sq, Smax, Hq, Hkv, d = 2, 3, 200, 8, 2, 64
+    inp = make_decode_inputs(B, Sq, Smax, Hq, Hkv, d, 7799, None)
+    dev = torch.device("cuda")
+    q = inp.q.to(dev)
+    padded = torch.zeros(B, Smax, Hq, d, dtype=torch.bfloat16, device=dev)
+    padded[:, Smax - Sq:] = q
+    kdummy = torch.zeros(B, Smax, Hkv, d, dtype=torch.bfloat16, device=dev)
+    q_rot, _ = attn.rope(padded, kdummy, 10000.0)
+    inp_rot = make_decode_inputs(B, Sq, Smax, Hq, Hkv, d, 7799, None)
+    inp_rot.q = q_rot[:, Smax - Sq:].contiguous().cpu()
+    a = run_decode(inp, 10000.0)
+    b = run_decode(inp_rot, 0.0)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
