@@ -50,7 +50,8 @@ class AttnError(RuntimeError):
 class AttnShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("heads_q", ctypes.c_int32),
                 ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("causal", ctypes.c_int32), ("seqlens", ctypes.c_void_p), ("rope_base", ctypes.c_float)]
+                ("causal", ctypes.c_int32), ("seqlens", ctypes.c_void_p), ("rope_base", ctypes.c_float),
+                ("q_stride", ctypes.c_int64 * 3), ("kv_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3)]
 
 
 class AttnDecodeShape(ctypes.Structure):
@@ -107,9 +108,12 @@ def attn_status_string(code: int) -> str:
 
 
 def make_shape(B: int, S: int, Hq: int, Hkv: int, d: int, scale: float, seqlens_ptr: Optional[int] = None,
-               causal: int = 1, rope_base: float = 0.0) -> AttnShape:
+               causal: int = 1, rope_base: float = 0.0, q_stride=None, kv_stride=None, o_stride=None) -> AttnShape:
+    """Stride triples are (sequence, position, head) in elements; None means dense."""
+    tri = lambda x: (ctypes.c_int64 * 3)(*(x if x is not None else (0, 0, 0)))  # noqa: E731
     return AttnShape(int(B), int(S), int(Hq), int(Hkv), int(d), float(scale), int(causal),
-                     ctypes.c_void_p(seqlens_ptr) if seqlens_ptr else None, float(rope_base or 0.0))
+                     ctypes.c_void_p(seqlens_ptr) if seqlens_ptr else None, float(rope_base or 0.0),
+                     tri(q_stride), tri(kv_stride), tri(o_stride))
 
 
 # ------------------------------------------------------------------ torch marshalling
@@ -119,7 +123,7 @@ def _torch():
     return torch
 
 
-def _check_gpu(name, t, dtype, shape=None):
+def _check_gpu(name, t, dtype, shape=None, strided=False):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -127,14 +131,31 @@ def _check_gpu(name, t, dtype, shape=None):
         raise ValueError(f"{name} must be a GPU tensor (got {t.device}); there is no CPU path")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
-    if not t.is_contiguous():
+    if strided:
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{name} must be 4-D with its last dimension contiguous")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return t.data_ptr()
 
 
-def _shape_from(q, k, scale, seqlens, causal=1, rope_base=0.0):
+def _strides(group, tensors):
+    """The (sequence, position, head) element strides the tensors of one stride
+    group share (the C ABI takes one triple per group); size-1 dimensions
+    count as stride 0."""
+    got = None
+    for name, t in tensors:
+        st = tuple(0 if t.shape[i] == 1 else int(t.stride(i)) for i in range(3))
+        if got is None:
+            got = st
+        elif st != got:
+            raise ValueError(f"{name} must have the same strides as the other {group} tensors")
+    return got
+
+
+def _shape_from(q, k, scale, seqlens, causal=1, rope_base=0.0, qg=(), kvg=(), og=()):
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q must be [B,S,Hq,d] and k [B,S,Hkv,d]")
@@ -143,7 +164,10 @@ def _shape_from(q, k, scale, seqlens, causal=1, rope_base=0.0):
     sl = None
     if seqlens is not None:
         sl = _check_gpu("seqlens", seqlens, torch.int32, (B,))
-    return make_shape(B, S, Hq, Hkv, d, scale, sl, causal, rope_base), (B, S, Hq, Hkv, d)
+    qs = _strides("q", qg) if qg else None
+    ks = _strides("k/v", kvg) if kvg else None
+    os_ = _strides("o", og) if og else None
+    return make_shape(B, S, Hq, Hkv, d, scale, sl, causal, rope_base, qs, ks, os_), (B, S, Hq, Hkv, d)
 
 
 def _stream():
@@ -159,11 +183,12 @@ def _call(fn, where, *args):
 def attn_rope(q, k, q_rot, k_rot, rope_base: float = 10000.0, seqlens=None):
     """q_rot, k_rot <- q and k rotated by the rotary position embedding."""
     torch = _torch()
-    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, 1.0, seqlens, 1, rope_base)
-    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d)),
-            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d)),
-            _check_gpu("q_rot", q_rot, torch.bfloat16, (B, S, Hq, d)),
-            _check_gpu("k_rot", k_rot, torch.bfloat16, (B, S, Hkv, d))]
+    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, 1.0, seqlens, 1, rope_base,
+                                            qg=[("q", q), ("q_rot", q_rot)], kvg=[("k", k), ("k_rot", k_rot)])
+    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("q_rot", q_rot, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("k_rot", k_rot, torch.bfloat16, (B, S, Hkv, d), True)]
     _call(load_library().attn_rope, "attn_rope", ctypes.byref(shape), *[ctypes.c_void_p(p) for p in ptrs],
           _stream())
 
@@ -171,11 +196,12 @@ def attn_rope(q, k, q_rot, k_rot, rope_base: float = 10000.0, seqlens=None):
 def attn_fwd(q, k, v, o, lse, scale: float, seqlens=None, causal: int = 1):
     """O, LSE <- attention forward (writes into `o` and `lse`)."""
     torch = _torch()
-    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal)
-    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d)),
-            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d)),
-            _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d)),
-            _check_gpu("o", o, torch.bfloat16, (B, S, Hq, d)),
+    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal, 0.0, qg=[("q", q)],
+                                            kvg=[("k", k), ("v", v)], og=[("o", o)])
+    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("o", o, torch.bfloat16, (B, S, Hq, d), True),
             _check_gpu("lse", lse, torch.float32, (B, Hq, S))]
     _call(load_library().attn_fwd, "attn_fwd", ctypes.byref(shape), *[ctypes.c_void_p(p) for p in ptrs], _stream())
 
@@ -187,9 +213,9 @@ def attn_bwd_preprocess(o, d_o, delta, seqlens=None):
         raise ValueError("o must be [B,S,Hq,d]")
     B, S, Hq, d = o.shape
     sl = _check_gpu("seqlens", seqlens, torch.int32, (B,)) if seqlens is not None else None
-    shape = make_shape(B, S, Hq, Hq, d, 1.0, sl)
-    ptrs = [_check_gpu("o", o, torch.bfloat16, (B, S, Hq, d)),
-            _check_gpu("d_o", d_o, torch.bfloat16, (B, S, Hq, d)),
+    shape = make_shape(B, S, Hq, Hq, d, 1.0, sl, o_stride=_strides("o", [("o", o), ("d_o", d_o)]))
+    ptrs = [_check_gpu("o", o, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("d_o", d_o, torch.bfloat16, (B, S, Hq, d), True),
             _check_gpu("delta", delta, torch.float32, (B, Hq, S))]
     _call(load_library().attn_bwd_preprocess, "attn_bwd_preprocess", ctypes.byref(shape),
           *[ctypes.c_void_p(p) for p in ptrs], _stream())
@@ -206,16 +232,18 @@ def attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale: float, seqlens=None, w
     rope_base > 0, q and k are the rotated tensors and dq, dk come back with
     respect to the unrotated ones."""
     torch = _torch()
-    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal, rope_base)
-    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d)),
-            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d)),
-            _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d)),
-            _check_gpu("d_o", d_o, torch.bfloat16, (B, S, Hq, d)),
+    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal, rope_base, qg=[("q", q)],
+                                            kvg=[("k", k), ("v", v), ("dk", dk), ("dv", dv)],
+                                            og=[("d_o", d_o), ("dq", dq)])
+    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("d_o", d_o, torch.bfloat16, (B, S, Hq, d), True),
             _check_gpu("lse", lse, torch.float32, (B, Hq, S)),
             _check_gpu("delta", delta, torch.float32, (B, Hq, S)),
-            _check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d)),
-            _check_gpu("dk", dk, torch.bfloat16, (B, S, Hkv, d)),
-            _check_gpu("dv", dv, torch.bfloat16, (B, S, Hkv, d))]
+            _check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("dk", dk, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("dv", dv, torch.bfloat16, (B, S, Hkv, d), True)]
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr = _check_gpu("workspace", workspace, workspace.dtype)
@@ -224,13 +252,15 @@ def attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale: float, seqlens=None, w
           ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), _stream())
 
 
-def _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal, rope_base):
+def _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal, rope_base, kv_out=(), o_out=()):
     torch = _torch()
-    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal, rope_base)
-    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d)),
-            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d)),
-            _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d)),
-            _check_gpu("d_o", d_o, torch.bfloat16, (B, S, Hq, d)),
+    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal, rope_base, qg=[("q", q)],
+                                            kvg=[("k", k), ("v", v)] + list(kv_out),
+                                            og=[("d_o", d_o)] + list(o_out))
+    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("d_o", d_o, torch.bfloat16, (B, S, Hq, d), True),
             _check_gpu("lse", lse, torch.float32, (B, Hq, S)),
             _check_gpu("delta", delta, torch.float32, (B, Hq, S))]
     return shape, (B, S, Hq, Hkv, d), ptrs
@@ -240,9 +270,10 @@ def attn_bwd_dkdv(q, k, v, d_o, lse, delta, dk, dv, scale: float, seqlens=None, 
                   rope_base: float = 0.0):
     """dK, dV <- the key-block pass of the backward (writes into `dk`, `dv`)."""
     torch = _torch()
-    shape, (B, S, Hq, Hkv, d), ptrs = _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal, rope_base)
-    ptrs += [_check_gpu("dk", dk, torch.bfloat16, (B, S, Hkv, d)),
-             _check_gpu("dv", dv, torch.bfloat16, (B, S, Hkv, d))]
+    shape, (B, S, Hq, Hkv, d), ptrs = _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal, rope_base,
+                                                  kv_out=[("dk", dk), ("dv", dv)])
+    ptrs += [_check_gpu("dk", dk, torch.bfloat16, (B, S, Hkv, d), True),
+             _check_gpu("dv", dv, torch.bfloat16, (B, S, Hkv, d), True)]
     _call(load_library().attn_bwd_dkdv, "attn_bwd_dkdv", ctypes.byref(shape),
           *[ctypes.c_void_p(p) for p in ptrs], _stream())
 
@@ -251,8 +282,9 @@ def attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale: float, seqlens=None, causal
                 rope_base: float = 0.0):
     """dQ <- the query-block pass of the backward (writes into `dq`)."""
     torch = _torch()
-    shape, (B, S, Hq, Hkv, d), ptrs = _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal, rope_base)
-    ptrs += [_check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d))]
+    shape, (B, S, Hq, Hkv, d), ptrs = _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal, rope_base,
+                                                  o_out=[("dq", dq)])
+    ptrs += [_check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d), True)]
     _call(load_library().attn_bwd_dq, "attn_bwd_dq", ctypes.byref(shape),
           *[ctypes.c_void_p(p) for p in ptrs], _stream())
 
@@ -316,7 +348,7 @@ def forward(q, k, v, scale: Optional[float] = None, seqlens=None, causal: bool =
     B, S, Hq, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     attn_fwd(q, k, v, o, lse, scale, seqlens, int(causal))
     return o, lse
@@ -324,7 +356,10 @@ def forward(q, k, v, scale: Optional[float] = None, seqlens=None, causal: bool =
 
 def rope(q, k, rope_base: float = 10000.0):
     """Returns (q_rot, k_rot) as new tensors."""
-    q_rot, k_rot = _torch().empty_like(q), _torch().empty_like(k)
+    torch = _torch()
+    # q_rot shares q's strides and k_rot k's (one stride triple per group)
+    q_rot = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    k_rot = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
     attn_rope(q, k, q_rot, k_rot, rope_base)
     return q_rot, k_rot
 
@@ -342,7 +377,10 @@ def backward(q, k, v, o, d_o, lse, scale: Optional[float] = None, seqlens=None, 
     attn_bwd_preprocess(o, d_o, delta, seqlens)
     need = attn_bwd_workspace_bytes(B, S, Hq, k.shape[2], d)
     ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    # dQ shares dO's strides and dK, dV share K's (one stride triple per group)
+    dq = torch.empty_strided(d_o.shape, d_o.stride(), dtype=q.dtype, device=q.device)
+    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+    dv = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
     attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, ws, int(causal), rope_base)
     return dq, dk, dv, delta
 

@@ -12,6 +12,20 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A stride triple (sequence, position, head) in elements; all zero means the
+// dense [B, S, H, d] layout. Returns false for a negative stride or one that
+// is not a multiple of 8 elements (rows must stay 16-byte aligned).
+bool resolve_strides(const int64_t (&in)[3], int S, int H, int d, attn::Strides* out) {
+  if (in[0] == 0 && in[1] == 0 && in[2] == 0) {
+    *out = attn::Strides{(int64_t)S * H * d, (int64_t)H * d, d};
+    return true;
+  }
+  for (int i = 0; i < 3; ++i)
+    if (in[i] < 0 || (in[i] & 7) != 0) return false;
+  *out = attn::Strides{in[0], in[1], in[2]};
+  return true;
+}
+
 attn_status check_shape(const attn_shape* s, attn::Problem* pr) {
   if (!s) return ATTN_ERR_INVALID_ARG;
   if (s->batch < 1 || s->seqlen < 1 || s->heads_q < 1 || s->heads_kv < 1) return ATTN_ERR_INVALID_ARG;
@@ -21,9 +35,17 @@ attn_status check_shape(const attn_shape* s, attn::Problem* pr) {
   if (s->causal != 0 && s->causal != 1) return ATTN_ERR_INVALID_ARG;
   if (!(isfinite(s->rope_base) && s->rope_base >= 0.f)) return ATTN_ERR_INVALID_ARG;
   if (s->seqlens && (reinterpret_cast<uintptr_t>(s->seqlens) & 3u) != 0) return ATTN_ERR_MISALIGNED;
+  attn::Strides sq, skv, so;
+  if (!resolve_strides(s->q_stride, s->seqlen, s->heads_q, s->head_dim, &sq) ||
+      !resolve_strides(s->kv_stride, s->seqlen, s->heads_kv, s->head_dim, &skv) ||
+      !resolve_strides(s->o_stride, s->seqlen, s->heads_q, s->head_dim, &so))
+    return ATTN_ERR_MISALIGNED;
   // tiles are fetched through buffer resources with 32-bit byte offsets that
-  // span up to 128 rows of one sequence: 128 * heads * head_dim * 2 < 2^31
-  if ((int64_t)s->heads_q * s->head_dim > (int64_t)1 << 22) return ATTN_ERR_UNSUPPORTED;
+  // span up to 128 rows of one sequence: 128 * position stride * 2 < 2^31
+  constexpr int64_t kMaxRowStride = (int64_t)1 << 22;
+  if ((int64_t)s->heads_q * s->head_dim > kMaxRowStride || sq.s > kMaxRowStride || skv.s > kMaxRowStride ||
+      so.s > kMaxRowStride)
+    return ATTN_ERR_UNSUPPORTED;
   pr->B = s->batch;
   pr->S = s->seqlen;
   pr->Hq = s->heads_q;
@@ -33,6 +55,9 @@ attn_status check_shape(const attn_shape* s, attn::Problem* pr) {
   pr->seqlens = s->seqlens;
   pr->causal = s->causal;
   pr->rope_base = s->rope_base;
+  pr->sq = sq;
+  pr->skv = skv;
+  pr->so = so;
   if (attn::max_grid(*pr) > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }

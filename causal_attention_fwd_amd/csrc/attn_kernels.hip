@@ -43,6 +43,7 @@ struct FwdArgs {
   int B, S, Hq, Hkv, nqb;
   float scale;
   int causal;  // 1: keys j <= i only; 0: every key of the valid prefix
+  Strides sq, skv, so;  // Q; K and V; O (elements per sequence, position, head)
 };
 
 struct PreArgs {
@@ -52,6 +53,7 @@ struct PreArgs {
   const int32_t* seqlens;
   int B, S, Hq;
   int64_t rows;  // B * Hq * S
+  Strides so;    // O and dO
 };
 
 // Rotary position embedding ("AxiomLM" PyPI page, "Key Features" and "8.
@@ -102,6 +104,7 @@ struct BwdArgs {
   int causal;  // 1: keys j <= i only; 0: every key of the valid prefix
   int rope;    // 1: q and k are rotated; dQ and dK leave through the adjoint
   RopeFreq rf;
+  Strides sq, skv, so;  // Q; K, V, dK, dV; O, dO, dQ
 };
 
 constexpr int kThreads = 256;  // four waves, one per SIMD
@@ -277,12 +280,13 @@ void fwd_kernel(FwdArgs a) {
   const int S = a.S;
   const int L = valid_len(a.seqlens, b, S);
   const int hkv = h / (a.Hq / a.Hkv);
-  const int64_t qs = (int64_t)a.Hq * D;   // elements between consecutive positions
-  const int64_t ks = (int64_t)a.Hkv * D;
-  const bf16* Qb = a.q + ((int64_t)b * S * a.Hq + h) * D;
-  const bf16* Kb = a.k + ((int64_t)b * S * a.Hkv + hkv) * D;
-  const bf16* Vb = a.v + ((int64_t)b * S * a.Hkv + hkv) * D;
-  bf16* Ob = a.o + ((int64_t)b * S * a.Hq + h) * D;
+  const int64_t qs = a.sq.s;   // elements between consecutive positions
+  const int64_t ks = a.skv.s;
+  const int64_t os = a.so.s;
+  const bf16* Qb = a.q + b * a.sq.b + h * a.sq.h;
+  const bf16* Kb = a.k + b * a.skv.b + hkv * a.skv.h;
+  const bf16* Vb = a.v + b * a.skv.b + hkv * a.skv.h;
+  bf16* Ob = a.o + b * a.so.b + h * a.so.h;
   float* LSEb = a.lse + ((int64_t)b * a.Hq + h) * S;
 
   const int q0 = qb * BM;
@@ -344,7 +348,7 @@ void fwd_kernel(FwdArgs a) {
           bf16x4 ov;
 #pragma unroll
           for (int e = 0; e < 4; ++e) ov[e] = (bf16)(st.oacc[dt][t][rr * 4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(Ob + (int64_t)i * qs + dt * 32 + rr * 8 + g * 4) = ov;
+          *reinterpret_cast<bf16x4*>(Ob + (int64_t)i * os + dt * 32 + rr * 8 + g * 4) = ov;
         }
       if (g == 0) LSEb[i] = valid ? (st.mu[t] * c + __log2f(lt)) * kLn2 : kNegInf;
     }
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
     const int64_t bh = r / a.S;
     const int h = (int)(bh % a.Hq);
     b = (int)(bh / a.Hq);
-    const int64_t off = (((int64_t)b * a.S + s) * a.Hq + h) * D + part * 8;
+    const int64_t off = b * a.so.b + s * a.so.s + h * a.so.h + part * 8;
     const bf16x8 o = *reinterpret_cast<const bf16x8*>(a.o + off);
     const bf16x8 d = *reinterpret_cast<const bf16x8*>(a.d_o + off);
 #pragma unroll
@@ -514,10 +518,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int S = a.S;
   const int L = valid_len(a.seqlens, b, S);
   const int G = a.Hq / a.Hkv;
-  const int64_t qs = (int64_t)a.Hq * D;
-  const int64_t ks = (int64_t)a.Hkv * D;
-  const bf16* Kb = a.k + ((int64_t)b * S * a.Hkv + hkv) * D;
-  const bf16* Vb = a.v + ((int64_t)b * S * a.Hkv + hkv) * D;
+  const int64_t qs = a.sq.s;
+  const int64_t os = a.so.s;
+  const int64_t ks = a.skv.s;
+  const bf16* Kb = a.k + b * a.skv.b + hkv * a.skv.h;
+  const bf16* Vb = a.v + b * a.skv.b + hkv * a.skv.h;
 
   const int j0 = kb * BN;
   const int jw = j0 + wave * 32 * NTJ;
@@ -563,10 +568,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
       st_reg = 0.f;
       if (i < L) st_reg = src[((int64_t)b * a.Hq + h) * S + i];
     }
-    const bf16* Qb = a.q + ((int64_t)b * S * a.Hq + h) * D;
-    const bf16* dOb = a.d_o + ((int64_t)b * S * a.Hq + h) * D;
+    const bf16* Qb = a.q + b * a.sq.b + h * a.sq.h;
+    const bf16* dOb = a.d_o + b * a.so.b + h * a.so.h;
     tile_load_lds<BMQ, D, 4>(Qb, qs, qt * BMQ, L, buf.k, wave, lane);
-    tile_load_lds<BMQ, D, 4>(dOb, qs, qt * BMQ, L, buf.v, wave, lane);
+    tile_load_lds<BMQ, D, 4>(dOb, os, qt * BMQ, L, buf.v, wave, lane);
   };
   auto land = [&](int trip, const KVBuf& buf) {
     if (trip * GROUPS + grp < iters && gtid < 2 * BMQ)
@@ -632,8 +637,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // Epilogue: dK = scale * dK^T, dV = dV^T transposed back; lane owns key row j.
-  bf16* dKb = a.dk + ((int64_t)b * S * a.Hkv + hkv) * D;
-  bf16* dVb = a.dv + ((int64_t)b * S * a.Hkv + hkv) * D;
+  bf16* dKb = a.dk + b * a.skv.b + hkv * a.skv.h;
+  bf16* dVb = a.dv + b * a.skv.b + hkv * a.skv.h;
 #pragma unroll
   for (int t = 0; t < NTJ; ++t) {
     const int j = jw + t * 32 + l32;
@@ -749,15 +754,16 @@ void bwd_dq_kernel(BwdArgs a) {
   const int S = a.S;
   const int L = valid_len(a.seqlens, b, S);
   const int hkv = h / (a.Hq / a.Hkv);
-  const int64_t qs = (int64_t)a.Hq * D;
-  const int64_t ks = (int64_t)a.Hkv * D;
-  const bf16* Qb = a.q + ((int64_t)b * S * a.Hq + h) * D;
-  const bf16* dOb = a.d_o + ((int64_t)b * S * a.Hq + h) * D;
-  const bf16* Kb = a.k + ((int64_t)b * S * a.Hkv + hkv) * D;
-  const bf16* Vb = a.v + ((int64_t)b * S * a.Hkv + hkv) * D;
+  const int64_t qs = a.sq.s;
+  const int64_t os = a.so.s;
+  const int64_t ks = a.skv.s;
+  const bf16* Qb = a.q + b * a.sq.b + h * a.sq.h;
+  const bf16* dOb = a.d_o + b * a.so.b + h * a.so.h;
+  const bf16* Kb = a.k + b * a.skv.b + hkv * a.skv.h;
+  const bf16* Vb = a.v + b * a.skv.b + hkv * a.skv.h;
   const float* LSEb = a.lse + ((int64_t)b * a.Hq + h) * S;
   const float* Db = a.delta + ((int64_t)b * a.Hq + h) * S;
-  bf16* dQb = a.dq + ((int64_t)b * S * a.Hq + h) * D;
+  bf16* dQb = a.dq + b * a.so.b + h * a.so.h;
 
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32 * NT;
@@ -774,9 +780,9 @@ void bwd_dq_kernel(BwdArgs a) {
     const bool valid = row < L;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const int64_t off = (int64_t)row * qs + kk * 16 + g * 8;
-      st.qf[t][kk] = valid ? *reinterpret_cast<const bf16x8*>(Qb + off) : zero_bf16x8();
-      st.df[t][kk] = valid ? *reinterpret_cast<const bf16x8*>(dOb + off) : zero_bf16x8();
+      const int64_t col = kk * 16 + g * 8;
+      st.qf[t][kk] = valid ? *reinterpret_cast<const bf16x8*>(Qb + (int64_t)row * qs + col) : zero_bf16x8();
+      st.df[t][kk] = valid ? *reinterpret_cast<const bf16x8*>(dOb + (int64_t)row * os + col) : zero_bf16x8();
     }
     st.l2[t] = valid ? LSEb[row] * kLog2e : 0.f;
     st.dd[t] = valid ? Db[row] : 0.f;
@@ -825,7 +831,7 @@ void bwd_dq_kernel(BwdArgs a) {
           if (a.rope) rope_adjoint4(a.rf, dt * 32 + rr * 8, g, i, qx);
 #pragma unroll
           for (int e = 0; e < 4; ++e) ov[e] = (bf16)(valid ? qx[e] : 0.f);
-          *reinterpret_cast<bf16x4*>(dQb + (int64_t)i * qs + dt * 32 + rr * 8 + g * 4) = ov;
+          *reinterpret_cast<bf16x4*>(dQb + (int64_t)i * os + dt * 32 + rr * 8 + g * 4) = ov;
         }
     }
   }
@@ -847,6 +853,7 @@ struct RopeArgs {
   int64_t nq, nk;  // 8-element chunks of q and of k
   int S, Hq, Hkv;
   RopeFreq rf;
+  Strides sq, skv;  // q and q_rot; k and k_rot
 };
 
 template <int D>
@@ -855,18 +862,23 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a) {
   const bf16* src = a.q;
   bf16* dst = a.qr;
   int H = a.Hq;
+  Strides st = a.sq;
   if (idx >= a.nq) {
     idx -= a.nq;
     if (idx >= a.nk) return;
     src = a.k;
     dst = a.kr;
     H = a.Hkv;
+    st = a.skv;
   }
   constexpr int CPR = D / 8;  // chunks per row
-  const int64_t row = idx / CPR;
+  const int64_t row = idx / CPR;  // (b * S + p) * H + h
   const int c = (int)(idx - row * CPR);
-  const int p = (int)((row / H) % a.S);
-  const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + idx * 8);
+  const int h = (int)(row % H);
+  const int64_t bp = row / H;
+  const int p = (int)(bp % a.S);
+  const int64_t off = (bp / a.S) * st.b + (int64_t)p * st.s + (int64_t)h * st.h + c * 8;
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + off);
   bf16x8 y;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -876,7 +888,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a) {
     y[2 * e] = (bf16)(x0 * cs - x1 * sn);
     y[2 * e + 1] = (bf16)(x0 * sn + x1 * cs);
   }
-  *reinterpret_cast<bf16x8*>(dst + idx * 8) = y;
+  *reinterpret_cast<bf16x8*>(dst + off) = y;
 }
 
 // ----------------------------------------------------------------------------
@@ -1253,14 +1265,14 @@ hipError_t fwd_d(const Problem& pr, const void* q, const void* k, const void* v,
                  hipStream_t stream) {
   constexpr int NT = Tiles<D>::FWD_NT;
   FwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, pr.seqlens,
-            pr.B, pr.S, pr.Hq, pr.Hkv, cdiv(pr.S, 128 * NT), pr.scale, pr.causal};
+            pr.B, pr.S, pr.Hq, pr.Hkv, cdiv(pr.S, 128 * NT), pr.scale, pr.causal, pr.sq, pr.skv, pr.so};
   return launch((const void*)&fwd_kernel<D, NT, Tiles<D>::FWD_OCC>, (int64_t)a.nqb * pr.B * pr.Hq, a, stream);
 }
 
 template <int D>
 hipError_t pre_d(const Problem& pr, const void* o, const void* d_o, float* delta, hipStream_t stream) {
   PreArgs a{(const bf16*)o, (const bf16*)d_o, delta, pr.seqlens, pr.B, pr.S, pr.Hq,
-            (int64_t)pr.B * pr.S * pr.Hq};
+            (int64_t)pr.B * pr.S * pr.Hq, pr.so};
   constexpr int rows_per_block = kThreads / (D / 8);
   return launch((const void*)&preprocess_kernel<D>, (a.rows + rows_per_block - 1) / rows_per_block, a, stream);
 }
@@ -1271,7 +1283,7 @@ hipError_t dkdv_d(const Problem& pr, const void* q, const void* k, const void* v
   constexpr int NTJ = Tiles<D>::DKDV_NTJ;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             nullptr, (bf16*)dk, (bf16*)dv, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
-            cdiv(pr.S, 128 * NTJ), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr)};
+            cdiv(pr.S, 128 * NTJ), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so};
   constexpr int GR = Tiles<D>::DKDV_GROUPS;
   return launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR>, (int64_t)a.nblk * pr.B * pr.Hkv, a,
                 stream, kThreads * GR);
@@ -1283,7 +1295,7 @@ hipError_t dq_d(const Problem& pr, const void* q, const void* k, const void* v, 
   constexpr int NT = Tiles<D>::DQ_NT;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             (bf16*)dq, nullptr, nullptr, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
-            cdiv(pr.S, 128 * NT), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr)};
+            cdiv(pr.S, 128 * NT), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so};
   return launch((const void*)&bwd_dq_kernel<D, NT, Tiles<D>::DQ_OCC>, (int64_t)a.nblk * pr.B * pr.Hq, a, stream);
 }
 
@@ -1291,7 +1303,7 @@ template <int D>
 hipError_t rope_d(const Problem& pr, const void* q, const void* k, void* qr, void* kr, hipStream_t stream) {
   RopeArgs a{(const bf16*)q, (const bf16*)k, (bf16*)qr, (bf16*)kr,
              (int64_t)pr.B * pr.S * pr.Hq * (D / 8), (int64_t)pr.B * pr.S * pr.Hkv * (D / 8),
-             pr.S, pr.Hq, pr.Hkv, rope_freq(pr)};
+             pr.S, pr.Hq, pr.Hkv, rope_freq(pr), pr.sq, pr.skv};
   return launch((const void*)&rope_kernel<D>, (a.nq + a.nk + kThreads - 1) / kThreads, a, stream);
 }
 

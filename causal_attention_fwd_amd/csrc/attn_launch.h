@@ -7,12 +7,18 @@
 
 namespace attn {
 
+// Element strides of a [B, S, H, d] tensor (d contiguous).
+struct Strides {
+  int64_t b, s, h;
+};
+
 struct Problem {
   int B, S, Hq, Hkv, d;
   float scale;
   const int32_t* seqlens;  // device int32[B] or nullptr
   int causal;              // 1: keys j <= i only; 0: every key of the valid prefix
   float rope_base;         // > 0: rotary embedding base (q, k rotated); 0: none
+  Strides sq, skv, so;     // Q (and q_rot); K, V, dK, dV (and k_rot); O, dO, dQ
 };
 
 hipError_t launch_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,

@@ -32,9 +32,9 @@
  *    never allocates, frees or synchronises; work is enqueued on `stream` (0 =
  *    the null stream) in call order. Buffers must stay alive until the stream
  *    has run the work.
- *  - Layouts are dense row-major: Q, O, dO, dQ are [B, S, Hq, d]; K, V, dK, dV
- *    are [B, S, Hkv, d]; all bf16 (bfloat16 bit patterns). LSE and D are fp32
- *    [B, Hq, S].
+ *  - Layouts are row-major: Q, O, dO, dQ are [B, S, Hq, d]; K, V, dK, dV
+ *    are [B, S, Hkv, d]; all bf16 (bfloat16 bit patterns), dense unless the
+ *    shape gives strides. LSE and D are fp32 [B, Hq, S], always dense.
  *  - Outputs are fully overwritten, including padded rows (zeros, LSE = -inf);
  *    gradients are not accumulated into existing contents.
  *  - Every tensor pointer must be 16-byte aligned (seqlens: 4-byte aligned).
@@ -63,7 +63,8 @@ typedef enum attn_status {
   ATTN_ERR_UNSUPPORTED = 2,  /* head_dim not in {64, 128},
                                 heads_q * head_dim > 2^22 (tile offsets are
                                 32-bit), or a grid beyond 2^31 - 1 blocks */
-  ATTN_ERR_MISALIGNED = 3,   /* a pointer is not 16-byte aligned */
+  ATTN_ERR_MISALIGNED = 3,   /* a pointer is not 16-byte aligned, or a stride is
+                                negative or not a multiple of 8 elements */
   ATTN_ERR_WORKSPACE = 4,    /* workspace smaller than attn_bwd_workspace_bytes() */
   ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
 } attn_status;
@@ -89,6 +90,18 @@ typedef struct attn_shape {
      q and k (the rotation's adjoint is applied as they are written).
      attn_fwd and attn_bwd_preprocess do not depend on it. */
   float rope_base;
+  /* Optional strides, in elements, of the (sequence, position, head)
+     dimensions; the head dimension d is always contiguous. All three zero
+     means the dense layout above. q_stride: Q (and q_rot in attn_rope);
+     kv_stride: K, V, dK, dV (and k_rot); o_stride: O, dO, dQ. Each must be a
+     non-negative multiple of 8 (ATTN_ERR_MISALIGNED otherwise) and the
+     position stride at most 2^22 (ATTN_ERR_UNSUPPORTED). They let Q, K, V be
+     views into one fused projection output, for instance. Outputs written
+     through strides that make rows overlap race; the caller keeps them
+     disjoint. */
+  int64_t q_stride[3];
+  int64_t kv_stride[3];
+  int64_t o_stride[3];
 } attn_shape;
 
 /*

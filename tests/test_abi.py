@@ -51,10 +51,12 @@ def test_status_strings(lib):
 
 
 def _shape(**kw):
-    base = dict(B=2, S=128, Hq=4, Hkv=2, d=64, scale=0.125, seqlens_ptr=None, causal=1, rope_base=0.0)
+    base = dict(B=2, S=128, Hq=4, Hkv=2, d=64, scale=0.125, seqlens_ptr=None, causal=1, rope_base=0.0,
+                q_stride=None, kv_stride=None, o_stride=None)
     base.update(kw)
     return attn.make_shape(base["B"], base["S"], base["Hq"], base["Hkv"], base["d"], base["scale"],
-                           base["seqlens_ptr"], base["causal"], base["rope_base"])
+                           base["seqlens_ptr"], base["causal"], base["rope_base"], base["q_stride"],
+                           base["kv_stride"], base["o_stride"])
 
 
 P = ctypes.c_void_p
@@ -94,6 +96,9 @@ def _pre(lib, shape, ptrs=(GOOD,) * 3):
     (dict(d=32), 2), (dict(d=96), 2), (dict(d=256), 2), (dict(causal=2), 1), (dict(causal=-1), 1),
     (dict(seqlens_ptr=GOOD + 2), 3),
     (dict(rope_base=-1.0), 1), (dict(rope_base=float("nan")), 1), (dict(rope_base=float("inf")), 1),
+    (dict(q_stride=(128 * 4 * 64, 4 * 64, 60)), 3), (dict(kv_stride=(-8, 128, 64)), 3),
+    (dict(o_stride=(8, 8, 4)), 3), (dict(q_stride=(1 << 40, (1 << 22) + 8, 64)), 2),
+    (dict(kv_stride=(0, (1 << 22) + 64, 64)), 2),
     (dict(B=2 ** 30, S=2 ** 20), 2), (dict(Hq=2 ** 17, Hkv=1), 2), (dict(Hq=2 ** 16, Hkv=2 ** 16, d=128), 2),
 ])
 def test_invalid_shapes_rejected(lib, kw, code):
@@ -248,3 +253,16 @@ def test_rope_requires_a_base_and_valid_pointers(lib):
         assert _rope(lib, shape, ptrs) == 3
     # a rope base is accepted by every attention entry point (validation only)
     assert _fwd(lib, _shape(rope_base=10000.0, d=96)) == 2
+
+
+def test_strides_accepted_when_valid(lib):
+    # a fused QKV projection output [B, S, Hq + 2 Hkv, d]: q, k, v are views
+    B, S, Hq, Hkv, d = 2, 128, 4, 2, 64
+    W = (Hq + 2 * Hkv) * d
+    shape = _shape(B=B, S=S, Hq=Hq, Hkv=Hkv, d=d, q_stride=(S * W, W, d), kv_stride=(S * W, W, d),
+                   o_stride=(S * Hq * d, Hq * d, d))
+    # validation passes; a null pointer then stops the call before any launch
+    assert _fwd(lib, shape, (0, GOOD, GOOD, GOOD, GOOD)) == 1
+    # the same layout with one stride off the 8-element grid is refused
+    bad = _shape(B=B, S=S, Hq=Hq, Hkv=Hkv, d=d, q_stride=(S * W, W + 4, d))
+    assert _fwd(lib, bad) == 3
