@@ -358,6 +358,10 @@ def run(args):
         rope_ms += ev[0].elapsed_time(ev[5])
     per = {n: per[n] / args.steps for n in names}           # ms per launch
     rope_ms /= args.steps
+    # per-step event times (first to last launch of the step): median, min, p90
+    step_ev = sorted(ev[0].elapsed_time(ev[4]) for ev in events)
+    step_stats = {"median": round(step_ev[len(step_ev) // 2], 4), "min": round(step_ev[0], 4),
+                  "p90": round(step_ev[min(len(step_ev) - 1, (9 * len(step_ev)) // 10)], 4)}
     ms_step = wall * 1e3 / args.steps
     launch = "eager"
     if args.graph:
@@ -402,6 +406,7 @@ def run(args):
                        algorithmic_gflop_per_step=round(fl["total"] / 1e9, 3),
                        rope_base=rb if args.rope else None),
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "step_event_ms": step_stats,
         "kernel_ms": dict({KERNEL_NAMES[n]: round(per[n], 4) for n in names},
                           **({"rope_kernel": round(rope_ms, 4)} if args.rope else {})),
         "kernel_tflops": {KERNEL_NAMES[n]: round(s / (per[n] * 1e-3) / 1e12, 1)
