@@ -329,15 +329,24 @@ def run(args):
         attn.attn_fwd(qa, ka, v, o, lse, scale, sl, cz)
         if ev is not None:
             ev[1].record()
-        attn.attn_bwd_preprocess(o, do, delta, sl)
-        if ev is not None:
-            ev[2].record()
-        attn.attn_bwd_dkdv(qa, ka, v, do, lse, delta, dk, dv, scale, sl, cz, rb)
-        if ev is not None:
-            ev[3].record()
-        attn.attn_bwd_dq(qa, ka, v, do, lse, delta, dq, scale, sl, cz, rb)
-        if ev is not None:
-            ev[4].record()
+        if args.fused_bwd:
+            # preprocess folded into dQ, which runs first; events 2 and 3 bracket dQ + D
+            if ev is not None:
+                ev[2].record()
+            attn.attn_bwd_fused(qa, ka, v, o, do, lse, delta, dq, dk, dv, scale, sl, None, cz, rb)
+            if ev is not None:
+                ev[3].record()
+                ev[4].record()
+        else:
+            attn.attn_bwd_preprocess(o, do, delta, sl)
+            if ev is not None:
+                ev[2].record()
+            attn.attn_bwd_dkdv(qa, ka, v, do, lse, delta, dk, dv, scale, sl, cz, rb)
+            if ev is not None:
+                ev[3].record()
+            attn.attn_bwd_dq(qa, ka, v, do, lse, delta, dq, scale, sl, cz, rb)
+            if ev is not None:
+                ev[4].record()
 
     for _ in range(args.warmup):
         step()
@@ -384,7 +393,14 @@ def run(args):
 
     # roofline of the dominant kernel
     dom = max(per, key=per.get)
-    if dom == "pre":
+    if args.fused_bwd:
+        # one call launches dQ (+D) and dK/dV back to back: priced together
+        # against the backward's algorithmic flops
+        achieved = fl["bwd"] / (per["dkdv"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "kernel": "bwd_dq_kernel+bwd_dkdv_kernel (attn_bwd_fused)",
+                "ms_per_launch": per["dkdv"], "traffic": None}
+    elif dom == "pre":
         alg_bytes = 2.0 * B * S * Hq * d * 2 + B * Hq * S * 4.0
         achieved = alg_bytes / (per[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -394,23 +410,30 @@ def run(args):
         achieved = share / (per[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS}
-    roof["kernel"] = KERNEL_NAMES[dom]
-    roof["ms_per_launch"] = per[dom]
-    roof["traffic"] = read_traffic(dom, w.name) if (causal and not args.rope) else None
+    if not args.fused_bwd:
+        roof["kernel"] = KERNEL_NAMES[dom]
+        roof["ms_per_launch"] = per[dom]
+        roof["traffic"] = read_traffic(dom, w.name) if (causal and not args.rope) else None
 
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": dict(w.describe(), causal=causal, launch=launch, valid_pairs_per_head=fl["pairs_per_head"],
+        "config": dict(w.describe(), causal=causal, launch=launch, fused_bwd=bool(args.fused_bwd),
+                       valid_pairs_per_head=fl["pairs_per_head"],
                        algorithmic_gflop_per_step=round(fl["total"] / 1e9, 3),
                        rope_base=rb if args.rope else None),
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "step_event_ms": step_stats,
-        "kernel_ms": dict({KERNEL_NAMES[n]: round(per[n], 4) for n in names},
+        "kernel_ms": dict({KERNEL_NAMES[n]: round(per[n], 4) for n in names} if not args.fused_bwd else
+                          {"fwd_kernel": round(per["fwd"], 4),
+                           "attn_bwd_fused (bwd_dq_kernel + bwd_dkdv_kernel)": round(per["dkdv"], 4)},
                           **({"rope_kernel": round(rope_ms, 4)} if args.rope else {})),
-        "kernel_tflops": {KERNEL_NAMES[n]: round(s / (per[n] * 1e-3) / 1e12, 1)
-                          for n, s in (("fwd", fl["fwd"]), ("dkdv", fl["bwd_dkdv"]), ("dq", fl["bwd_dq"]))},
+        "kernel_tflops": ({KERNEL_NAMES[n]: round(s / (per[n] * 1e-3) / 1e12, 1)
+                           for n, s in (("fwd", fl["fwd"]), ("dkdv", fl["bwd_dkdv"]), ("dq", fl["bwd_dq"]))}
+                          if not args.fused_bwd else
+                          {"fwd_kernel": round(fl["fwd"] / (per["fwd"] * 1e-3) / 1e12, 1),
+                           "attn_bwd_fused": round(fl["bwd"] / (per["dkdv"] * 1e-3) / 1e12, 1)}),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
@@ -532,6 +555,8 @@ def main():
                     help="time the step as one captured HIP graph (fwd, preprocess, dK/dV, dQ) replayed")
     ap.add_argument("--non-causal", action="store_true",
                     help="bidirectional attention (causal = 0): every key of the valid prefix, all pairs priced")
+    ap.add_argument("--fused-bwd", action="store_true",
+                    help="attn_bwd_fused: the preprocess folded into the dQ pass (3 launches per step)")
     ap.add_argument("--rope", action="store_true",
                     help="rotary position embedding: attn_rope pre-pass, backward with the fused adjoint")
     ap.add_argument("--rope-base", type=float, default=10000.0)

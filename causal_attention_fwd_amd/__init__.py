@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
     attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens=None, workspace=None)
     attn_bwd_dkdv(q, k, v, d_o, lse, delta, dk, dv, scale, seqlens=None)
     attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale, seqlens=None)
+    attn_bwd_fused(q, k, v, o, d_o, lse, delta, dq, dk, dv, scale, seqlens=None, workspace=None)
     attn_decode_workspace_bytes(B, Sq, Smax, Hq, Hkv, d)
     attn_decode(q, k_cache, v_cache, o, lse, scale, cache_lens=None, workspace=None)
     attn_status_string(code)
@@ -25,7 +26,7 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["attn_rope", "rope", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
+__all__ = ["attn_rope", "rope", "attn_bwd_fused", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode_workspace_bytes", "attn_decode", "attn_status_string",
            "forward", "backward", "decode", "capture_step", "AttnError", "library_path", "load_library",
            "STATUS"]
@@ -38,7 +39,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3:
 
 # The symbols include/attn.h declares.
 EXPORTED = ("attn_rope", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_dkdv",
-            "attn_bwd_dq", "attn_decode_workspace_bytes", "attn_decode", "attn_status_string")
+            "attn_bwd_dq", "attn_bwd_fused", "attn_decode_workspace_bytes", "attn_decode", "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -95,6 +96,8 @@ def load_library():
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode.argtypes = [dshp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_decode.restype = i32
+    lib.attn_bwd_fused.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.attn_bwd_fused.restype = i32
     lib.attn_rope.argtypes = [shp, vp, vp, vp, vp, vp]
     lib.attn_rope.restype = i32
     lib.attn_status_string.argtypes = [i32]
@@ -287,6 +290,32 @@ def attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale: float, seqlens=None, causal
     ptrs += [_check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d), True)]
     _call(load_library().attn_bwd_dq, "attn_bwd_dq", ctypes.byref(shape),
           *[ctypes.c_void_p(p) for p in ptrs], _stream())
+
+
+def attn_bwd_fused(q, k, v, o, d_o, lse, delta, dq, dk, dv, scale: float, seqlens=None, workspace=None,
+                   causal: int = 1, rope_base: float = 0.0):
+    """D, dQ, dK, dV <- the backward with the preprocess folded into the dQ
+    pass (writes `delta` as well as the gradients)."""
+    torch = _torch()
+    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal, rope_base, qg=[("q", q)],
+                                            kvg=[("k", k), ("v", v), ("dk", dk), ("dv", dv)],
+                                            og=[("o", o), ("d_o", d_o), ("dq", dq)])
+    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("o", o, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("d_o", d_o, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("lse", lse, torch.float32, (B, Hq, S)),
+            _check_gpu("delta", delta, torch.float32, (B, Hq, S)),
+            _check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("dk", dk, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("dv", dv, torch.bfloat16, (B, S, Hkv, d), True)]
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _check_gpu("workspace", workspace, workspace.dtype)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _call(load_library().attn_bwd_fused, "attn_bwd_fused", ctypes.byref(shape), *[ctypes.c_void_p(p) for p in ptrs],
+          ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), _stream())
 
 
 # ------------------------------------------------------------------ decode

@@ -177,6 +177,23 @@ attn_status attn_bwd(const attn_shape* shape, const void* q, const void* k, cons
   return from_hip(attn::launch_bwd_dq(pr, q, k, v, d_o, lse, delta, dq, stream));
 }
 
+attn_status attn_bwd_fused(const attn_shape* shape, const void* q, const void* k, const void* v, const void* o,
+                           const void* d_o, const float* lse, float* delta, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  attn::Problem pr;
+  attn_status st = check_shape(shape, &pr);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k, v, o, d_o, lse, delta, dq, dk, dv});
+  if (st != ATTN_OK) return st;
+  const size_t need = attn_bwd_workspace_bytes(shape);
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return ATTN_ERR_WORKSPACE;
+  // dQ first: it computes D, which the dK/dV pass then reads
+  st = from_hip(attn::launch_bwd_dq_with_delta(pr, q, k, v, o, d_o, lse, delta, dq, stream));
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, stream));
+}
+
 size_t attn_decode_workspace_bytes(const attn_decode_shape* shape) {
   attn::DecodeProblem pr;
   if (check_decode_shape(shape, &pr) != ATTN_OK) return 0;

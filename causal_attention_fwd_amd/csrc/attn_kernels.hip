@@ -105,6 +105,11 @@ struct BwdArgs {
   int rope;    // 1: q and k are rotated; dQ and dK leave through the adjoint
   RopeFreq rf;
   Strides sq, skv, so;  // Q; K, V, dK, dV; O, dO, dQ
+  // dQ pass only: when o is set, D = rowsum(dO * O) is computed from O and
+  // the dO rows the pass loads anyway, used, and written to delta_out (the
+  // preprocess folded in); delta is then not read
+  const bf16* o;
+  float* delta_out;
 };
 
 constexpr int kThreads = 256;  // four waves, one per SIMD
@@ -785,7 +790,23 @@ void bwd_dq_kernel(BwdArgs a) {
       st.df[t][kk] = valid ? *reinterpret_cast<const bf16x8*>(dOb + (int64_t)row * os + col) : zero_bf16x8();
     }
     st.l2[t] = valid ? LSEb[row] * kLog2e : 0.f;
-    st.dd[t] = valid ? Db[row] : 0.f;
+    if (a.o) {
+      // D from the bf16 O and dO rows: this lane holds half of each row's
+      // elements (16-element chunks split over the lane halves)
+      const bf16* Orow = a.o + b * a.so.b + h * a.so.h + (int64_t)row * os;
+      float part = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const bf16x8 ov = valid ? *reinterpret_cast<const bf16x8*>(Orow + kk * 16 + g * 8) : zero_bf16x8();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += (float)ov[e] * (float)st.df[t][kk][e];
+      }
+      const float dsum = xhalf_sum(part);
+      st.dd[t] = valid ? dsum : 0.f;
+      if (g == 0 && row < S) a.delta_out[((int64_t)b * a.Hq + h) * S + row] = valid ? dsum : 0.f;
+    } else {
+      st.dd[t] = valid ? Db[row] : 0.f;
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.acc[dt][t] = zero16();
   }
@@ -1283,7 +1304,8 @@ hipError_t dkdv_d(const Problem& pr, const void* q, const void* k, const void* v
   constexpr int NTJ = Tiles<D>::DKDV_NTJ;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             nullptr, (bf16*)dk, (bf16*)dv, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
-            cdiv(pr.S, 128 * NTJ), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so};
+            cdiv(pr.S, 128 * NTJ), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so,
+            nullptr, nullptr};
   constexpr int GR = Tiles<D>::DKDV_GROUPS;
   return launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR>, (int64_t)a.nblk * pr.B * pr.Hkv, a,
                 stream, kThreads * GR);
@@ -1291,11 +1313,13 @@ hipError_t dkdv_d(const Problem& pr, const void* q, const void* k, const void* v
 
 template <int D>
 hipError_t dq_d(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
-                const float* lse, const float* delta, void* dq, hipStream_t stream) {
+                const float* lse, const float* delta, void* dq, const void* o, float* delta_out,
+                hipStream_t stream) {
   constexpr int NT = Tiles<D>::DQ_NT;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             (bf16*)dq, nullptr, nullptr, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
-            cdiv(pr.S, 128 * NT), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so};
+            cdiv(pr.S, 128 * NT), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so,
+            (const bf16*)o, delta_out};
   return launch((const void*)&bwd_dq_kernel<D, NT, Tiles<D>::DQ_OCC>, (int64_t)a.nblk * pr.B * pr.Hq, a, stream);
 }
 
@@ -1331,8 +1355,15 @@ hipError_t launch_bwd_dkdv(const Problem& pr, const void* q, const void* k, cons
 
 hipError_t launch_bwd_dq(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
                          const float* lse, const float* delta, void* dq, hipStream_t stream) {
-  return pr.d == 64 ? dq_d<64>(pr, q, k, v, d_o, lse, delta, dq, stream)
-                    : dq_d<128>(pr, q, k, v, d_o, lse, delta, dq, stream);
+  return pr.d == 64 ? dq_d<64>(pr, q, k, v, d_o, lse, delta, dq, nullptr, nullptr, stream)
+                    : dq_d<128>(pr, q, k, v, d_o, lse, delta, dq, nullptr, nullptr, stream);
+}
+
+hipError_t launch_bwd_dq_with_delta(const Problem& pr, const void* q, const void* k, const void* v,
+                                    const void* o, const void* d_o, const float* lse, float* delta, void* dq,
+                                    hipStream_t stream) {
+  return pr.d == 64 ? dq_d<64>(pr, q, k, v, d_o, lse, nullptr, dq, o, delta, stream)
+                    : dq_d<128>(pr, q, k, v, d_o, lse, nullptr, dq, o, delta, stream);
 }
 
 int64_t max_grid(const Problem& pr) {

@@ -30,6 +30,11 @@ hipError_t launch_bwd_dkdv(const Problem& pr, const void* q, const void* k, cons
                            const float* lse, const float* delta, void* dk, void* dv, hipStream_t stream);
 hipError_t launch_bwd_dq(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
                          const float* lse, const float* delta, void* dq, hipStream_t stream);
+// The dQ pass computing D = rowsum(dO * O) itself (written to delta) instead
+// of reading it: the backward preprocess folded into the dQ pass.
+hipError_t launch_bwd_dq_with_delta(const Problem& pr, const void* q, const void* k, const void* v,
+                                    const void* o, const void* d_o, const float* lse, float* delta, void* dq,
+                                    hipStream_t stream);
 
 // Largest grid any launch for this problem would use (checked against the
 // hardware's 2^31-1 workgroup limit by the API layer).

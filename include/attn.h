@@ -174,6 +174,19 @@ attn_status attn_bwd_dq(const attn_shape* shape, const void* q, const void* k, c
                         void* dq, hipStream_t stream);
 
 /*
+ * Backward with the preprocess folded in: the dQ pass computes D = rowsum(dO * O)
+ * from the O and dO rows it loads (fp32 from the bf16 inputs, 0 on padded
+ * rows), writes it to `delta` [B,Hq,S] fp32 (an output here) and uses it; the
+ * dK/dV pass then reads it. Same results as attn_bwd_preprocess followed by
+ * attn_bwd up to the fp32 summation order of D, one launch fewer and one pass
+ * over O and dO fewer. O shares the o_stride triple with dO and dQ. Same
+ * validation, workspace rule and error codes as attn_bwd. Deterministic.
+ */
+attn_status attn_bwd_fused(const attn_shape* shape, const void* q, const void* k, const void* v, const void* o,
+                           const void* d_o, const float* lse, float* delta, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Decode: attention of Sq new queries per sequence against a key/value cache
  * (inference). "AxiomLM" (PyPI page), "Key Features" and "Zero-Overhead
  * Inference & Streaming Generation": a state-cached key/value decode engine,

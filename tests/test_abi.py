@@ -85,6 +85,11 @@ def _rope(lib, shape, ptrs=(GOOD,) * 4):
     return lib.attn_rope(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], P(0))
 
 
+def _fused(lib, shape, ptrs=(GOOD,) * 10, ws=None, ws_bytes=0):
+    return lib.attn_bwd_fused(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs],
+                              P(ws), ctypes.c_size_t(ws_bytes), P(0))
+
+
 def _pre(lib, shape, ptrs=(GOOD,) * 3):
     return lib.attn_bwd_preprocess(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], P(0))
 
@@ -104,6 +109,7 @@ def _pre(lib, shape, ptrs=(GOOD,) * 3):
 def test_invalid_shapes_rejected(lib, kw, code):
     shape = _shape(**kw)
     assert _rope(lib, shape) == code
+    assert _fused(lib, shape) == code
     assert _fwd(lib, shape) == code
     assert _pre(lib, shape) == code
     assert _bwd(lib, shape) == code
@@ -266,3 +272,13 @@ def test_strides_accepted_when_valid(lib):
     # the same layout with one stride off the 8-element grid is refused
     bad = _shape(B=B, S=S, Hq=Hq, Hkv=Hkv, d=d, q_stride=(S * W, W + 4, d))
     assert _fwd(lib, bad) == 3
+
+
+def test_fused_backward_pointers(lib):
+    assert _fused(lib, None) == 1
+    for i in range(10):
+        ptrs = [GOOD] * 10
+        ptrs[i] = 0
+        assert _fused(lib, _shape(), ptrs) == 1
+        ptrs[i] = ODD
+        assert _fused(lib, _shape(), ptrs) == 3
