@@ -1,5 +1,8 @@
 // gfx950 kernels for fused causal (or bidirectional) attention: forward,
-// backward preprocess, backward dK/dV and backward dQ.
+// backward preprocess, backward dK/dV and backward dQ (optionally computing the
+// preprocess's D itself), the rotary-embedding pre-pass, and decode attention
+// against a key/value cache (split over waves, then merged). Every kernel
+// addresses tensor rows through (sequence, position, head) strides.
 //
 // The method ("Axis", Zyora Labs page, feature list): flash attention forward
 // and backward on matrix cores in which the attention probabilities never reach
