@@ -282,3 +282,33 @@ def test_fused_backward_pointers(lib):
         assert _fused(lib, _shape(), ptrs) == 1
         ptrs[i] = ODD
         assert _fused(lib, _shape(), ptrs) == 3
+
+
+def test_plain_c_client_and_struct_layouts(lib, tmp_path):
+    """include/attn.h compiles as C99 with gcc and links against the library;
+    the struct layouts it reports are the ones the ctypes binding uses."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or the ROCm headers are not available")
+    exe = tmp_path / "abi_check"
+    src = os.path.join(ROOT, "tests", "c", "abi_check.c")
+    lib_path = attn.library_path()
+    cmd = [gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+           "-D__HIP_PLATFORM_AMD__", src, "-o", str(exe), lib_path, "-Wl,-rpath," + os.path.dirname(lib_path)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    vals = {}
+    for line in out.splitlines():
+        parts = line.split()
+        for key, val in zip(parts[0::2], parts[1::2]):
+            vals[key] = val
+    assert int(vals["attn_shape"]) == ctypes.sizeof(attn.AttnShape)
+    for f in ("rope_base", "q_stride", "kv_stride", "o_stride", "seqlens"):
+        assert int(out.split(f + " ")[1].split()[0]) == getattr(attn.AttnShape, f).offset, f
+    assert int(vals["attn_decode_shape"]) == ctypes.sizeof(attn.AttnDecodeShape)
+    assert int(vals["cache_lens"]) == attn.AttnDecodeShape.cache_lens.offset
+    dline = [l for l in out.splitlines() if l.startswith("attn_decode_shape")][0].split()
+    assert int(dline[dline.index("rope_base") + 1]) == attn.AttnDecodeShape.rope_base.offset
+    assert vals["fwd_bad_dim"] == "2" and vals["fwd_null_ptr"] == "1" and vals["fwd_bad_stride"] == "3"
+    assert "ATTN_ERR_INVALID_ARG" in out
