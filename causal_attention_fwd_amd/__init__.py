@@ -26,7 +26,7 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["attn_rope", "rope", "attn_bwd_fused", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
+__all__ = ["attn_rope", "rope", "attn_bwd_fused", "capture_decode", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode_workspace_bytes", "attn_decode", "attn_status_string",
            "forward", "backward", "decode", "capture_step", "AttnError", "library_path", "load_library",
            "STATUS"]
@@ -417,7 +417,7 @@ def backward(q, k, v, o, d_o, lse, scale: Optional[float] = None, seqlens=None, 
 # ------------------------------------------------------------------ graph capture
 
 def capture_step(q, k, v, d_o, o, lse, delta, dq, dk, dv, scale: float, seqlens=None, causal: bool = True,
-                 workspace=None):
+                 workspace=None, fused: bool = False):
     """Capture one training step of the path -- attn_fwd, attn_bwd_preprocess,
     attn_bwd (its dK/dV and dQ launches) -- into a HIP graph (torch.cuda.CUDAGraph)
     and return it; ``graph.replay()`` then reruns all four kernels with one
@@ -425,23 +425,41 @@ def capture_step(q, k, v, d_o, o, lse, delta, dq, dk, dv, scale: float, seqlens=
 
     The library is capture-safe: every entry point only enqueues kernels on the
     current stream (no allocation, no synchronisation, no memset), so the graph
-    holds exactly the four kernel nodes. Shapes, pointers, scale, seqlens and
-    causal are fixed at capture time."""
-    torch = _torch()
+    holds exactly the four kernel nodes (three with fused=True: attn_fwd then
+    attn_bwd_fused). Shapes, pointers, scale, seqlens and causal are fixed at
+    capture time."""
     cz = int(bool(causal))
-    # one eager run on the side stream first: loads the library, and checks the
-    # arguments outside the capture
+
+    def step():
+        attn_fwd(q, k, v, o, lse, scale, seqlens, cz)
+        if fused:
+            attn_bwd_fused(q, k, v, o, d_o, lse, delta, dq, dk, dv, scale, seqlens, workspace, cz)
+        else:
+            attn_bwd_preprocess(o, d_o, delta, seqlens)
+            attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, workspace, cz)
+    return _capture(step)
+
+
+def _capture(step):
+    """One eager run of `step` on a side stream (loads the library and checks
+    the arguments outside the capture), then the capture."""
+    torch = _torch()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        attn_fwd(q, k, v, o, lse, scale, seqlens, cz)
-        attn_bwd_preprocess(o, d_o, delta, seqlens)
-        attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, workspace, cz)
+        step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        attn_fwd(q, k, v, o, lse, scale, seqlens, cz)
-        attn_bwd_preprocess(o, d_o, delta, seqlens)
-        attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, workspace, cz)
+        step()
     return graph
+
+
+def capture_decode(q, k_cache, v_cache, o, lse, scale: float, cache_lens=None, workspace=None,
+                   rope_base: float = 0.0):
+    """Capture one attn_decode call (its split and merge launches) into a HIP
+    graph and return it. A serving loop refills q, the caches and cache_lens
+    in place and replays; the workspace is bound at capture time (it must be
+    at least attn_decode_workspace_bytes for these shapes)."""
+    return _capture(lambda: attn_decode(q, k_cache, v_cache, o, lse, scale, cache_lens, workspace, rope_base))

@@ -16,15 +16,22 @@ from parity import say
 pytestmark = pytest.mark.gpu
 
 
-def _eager(t, scale, sl, causal):
+def _eager(t, scale, sl, causal, fused=False):
     o, lse = attn.forward(t["q"], t["k"], t["v"], scale, sl, causal=causal)
-    dq, dk, dv, delta = attn.backward(t["q"], t["k"], t["v"], o, t["do"], lse, scale, sl, causal=causal)
+    if fused:
+        delta = torch.empty_like(lse)
+        dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+        attn.attn_bwd_fused(t["q"], t["k"], t["v"], o, t["do"], lse, delta, dq, dk, dv, scale, sl, None,
+                            int(causal))
+    else:
+        dq, dk, dv, delta = attn.backward(t["q"], t["k"], t["v"], o, t["do"], lse, scale, sl, causal=causal)
     torch.cuda.synchronize()
     return {"O": o, "LSE": lse, "D": delta, "dQ": dq, "dK": dk, "dV": dv}
 
 
-@pytest.mark.parametrize("causal,padded", [(True, False), (True, True), (False, True)])
-def test_graph_replays_match_eager(causal, padded):
+@pytest.mark.parametrize("causal,padded,fused", [(True, False, False), (True, True, False), (False, True, False),
+                                                 (True, True, True)])
+def test_graph_replays_match_eager(causal, padded, fused):
     B, S, Hq, Hkv, d = 2, 384, 8, 2, 64
     say(f"graph capture: B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} causal={causal} padded={padded}")
     dev = torch.device("cuda")
@@ -37,7 +44,8 @@ def test_graph_replays_match_eager(causal, padded):
     delta = torch.empty(B, Hq, S, device=dev)
     dq, dk, dv = torch.empty_like(buf["q"]), torch.empty_like(buf["k"]), torch.empty_like(buf["v"])
     scale = inputs[0].scale
-    graph = attn.capture_step(buf["q"], buf["k"], buf["v"], buf["do"], o, lse, delta, dq, dk, dv, scale, sl, causal)
+    graph = attn.capture_step(buf["q"], buf["k"], buf["v"], buf["do"], o, lse, delta, dq, dk, dv, scale, sl, causal,
+                              fused=fused)
     outs = {"O": o, "LSE": lse, "D": delta, "dQ": dq, "dK": dk, "dV": dv}
     for rep in range(6):
         inp = inputs[rep % 3]
@@ -51,9 +59,41 @@ def test_graph_replays_match_eager(causal, padded):
         got = {key: val.clone() for key, val in outs.items()}
         # eager work between replays, on separate tensors
         t = {n: getattr(inp, n).to(dev).contiguous() for n in ("q", "k", "v", "do")}
-        ref = _eager(t, scale, inp.seqlens.to(dev) if padded else None, causal)
+        ref = _eager(t, scale, inp.seqlens.to(dev) if padded else None, causal, fused)
         for key in got:
             bits = torch.int16 if got[key].dtype == torch.bfloat16 else torch.int32
             np.testing.assert_array_equal(got[key].view(bits).cpu().numpy(), ref[key].view(bits).cpu().numpy(),
                                           err_msg=f"replay {rep} {key}")
         say(f"  replay {rep}: all six outputs bitwise equal to eager")
+
+
+@pytest.mark.parametrize("rope_base", [0.0, 10000.0])
+def test_decode_graph_replays_match_eager(rope_base):
+    from attn_workloads import make_decode_inputs
+    B, Sq, Smax, Hq, Hkv, d = 8, 2, 3000, 16, 4, 64
+    say(f"decode graph capture: B={B} Sq={Sq} Smax={Smax} rope={rope_base}")
+    dev = torch.device("cuda")
+    inputs = [make_decode_inputs(B, Sq, Smax, Hq, Hkv, d, 950 + i, (1, Smax)) for i in range(3)]
+    q = inputs[0].q.to(dev).contiguous()
+    kc, vc = inputs[0].k_cache.to(dev).contiguous(), inputs[0].v_cache.to(dev).contiguous()
+    lens = inputs[0].cache_lens.to(dev)
+    o, lse = torch.empty_like(q), torch.empty(B, Hq, Sq, device=dev)
+    ws = torch.empty(attn.attn_decode_workspace_bytes(B, Sq, Smax, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    scale = inputs[0].scale
+    graph = attn.capture_decode(q, kc, vc, o, lse, scale, lens, ws, rope_base)
+    for rep in range(6):
+        inp = inputs[rep % 3]
+        q.copy_(inp.q.to(dev))
+        kc.copy_(inp.k_cache.to(dev))
+        vc.copy_(inp.v_cache.to(dev))
+        lens.copy_(inp.cache_lens.to(dev))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = o.clone(), lse.clone()
+        ro, rl = attn.decode(inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev), scale,
+                             inp.cache_lens.to(dev), rope_base)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got_o.view(torch.int16).cpu().numpy(), ro.view(torch.int16).cpu().numpy())
+        np.testing.assert_array_equal(got_l.view(torch.int32).cpu().numpy(), rl.view(torch.int32).cpu().numpy())
+        say(f"  decode replay {rep}: bitwise equal to eager")
