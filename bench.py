@@ -494,6 +494,10 @@ def run_decode(args):
     sets = []
     for _ in range(copies):
         q, k, v = (x.to(dev).contiguous() for x in (inp.q, inp.k_cache, inp.v_cache))
+        if args.decode_layout == "head":
+            # caches stored head-major [B, Hkv, Smax, d], passed as strided views
+            k = k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+            v = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
         sets.append((q, k, v, torch.empty_like(q), torch.empty(w.B, w.Hq, w.Sq, device=dev)))
     ws = torch.empty(max(16, attn.attn_decode_workspace_bytes(w.B, w.Sq, w.Smax, w.Hq, w.Hkv, w.d)),
                      dtype=torch.uint8, device=dev)
@@ -547,6 +551,7 @@ def run_decode(args):
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": dict(w.describe(), launch=launch, input_copies_rotated=copies,
+                       cache_layout="[B,Hkv,Smax,d]" if args.decode_layout == "head" else "[B,Smax,Hkv,d]",
                        algorithmic_bytes_per_step=nb["total"]),
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "roofline": roof,
@@ -566,6 +571,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="llama1b (default), or decode_llama1b with --decode")
     ap.add_argument("--decode", action="store_true", help="decode attention against a key/value cache")
+    ap.add_argument("--decode-layout", choices=("position", "head"), default="position",
+                    help="cache storage for --decode: position-major [B,Smax,Hkv,d] or head-major [B,Hkv,Smax,d]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work in cpu_baseline")
     ap.add_argument("--graph", action="store_true",

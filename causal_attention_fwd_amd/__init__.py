@@ -58,7 +58,8 @@ class AttnShape(ctypes.Structure):
 class AttnDecodeShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("cache_len", ctypes.c_int32),
                 ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("cache_lens", ctypes.c_void_p), ("rope_base", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("cache_lens", ctypes.c_void_p), ("rope_base", ctypes.c_float),
+                ("q_stride", ctypes.c_int64 * 3), ("kv_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3)]
 
 
 def library_path() -> str:
@@ -321,9 +322,13 @@ def attn_bwd_fused(q, k, v, o, d_o, lse, delta, dq, dk, dv, scale: float, seqlen
 # ------------------------------------------------------------------ decode
 
 def make_decode_shape(B: int, Sq: int, Smax: int, Hq: int, Hkv: int, d: int, scale: float,
-                      cache_lens_ptr: Optional[int] = None, rope_base: float = 0.0) -> AttnDecodeShape:
+                      cache_lens_ptr: Optional[int] = None, rope_base: float = 0.0, q_stride=None,
+                      kv_stride=None, o_stride=None) -> AttnDecodeShape:
+    """Stride triples are (sequence, position, head) in elements; None means dense."""
+    tri = lambda x: (ctypes.c_int64 * 3)(*(x if x is not None else (0, 0, 0)))  # noqa: E731
     return AttnDecodeShape(int(B), int(Sq), int(Smax), int(Hq), int(Hkv), int(d), float(scale),
-                           ctypes.c_void_p(cache_lens_ptr) if cache_lens_ptr else None, float(rope_base or 0.0))
+                           ctypes.c_void_p(cache_lens_ptr) if cache_lens_ptr else None, float(rope_base or 0.0),
+                           tri(q_stride), tri(kv_stride), tri(o_stride))
 
 
 def attn_decode_workspace_bytes(B: int, Sq: int, Smax: int, Hq: int, Hkv: int, d: int) -> int:
@@ -341,11 +346,13 @@ def attn_decode(q, k_cache, v_cache, o, lse, scale: float, cache_lens=None, work
     B, Sq, Hq, d = q.shape
     Smax, Hkv = k_cache.shape[1], k_cache.shape[2]
     lens = _check_gpu("cache_lens", cache_lens, torch.int32, (B,)) if cache_lens is not None else None
-    shape = make_decode_shape(B, Sq, Smax, Hq, Hkv, d, scale, lens, rope_base)
-    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, Sq, Hq, d)),
-            _check_gpu("k_cache", k_cache, torch.bfloat16, (B, Smax, Hkv, d)),
-            _check_gpu("v_cache", v_cache, torch.bfloat16, (B, Smax, Hkv, d)),
-            _check_gpu("o", o, torch.bfloat16, (B, Sq, Hq, d)),
+    shape = make_decode_shape(B, Sq, Smax, Hq, Hkv, d, scale, lens, rope_base, _strides("q", [("q", q)]),
+                              _strides("cache", [("k_cache", k_cache), ("v_cache", v_cache)]),
+                              _strides("o", [("o", o)]))
+    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, Sq, Hq, d), True),
+            _check_gpu("k_cache", k_cache, torch.bfloat16, (B, Smax, Hkv, d), True),
+            _check_gpu("v_cache", v_cache, torch.bfloat16, (B, Smax, Hkv, d), True),
+            _check_gpu("o", o, torch.bfloat16, (B, Sq, Hq, d), True),
             _check_gpu("lse", lse, torch.float32, (B, Hq, Sq))]
     ws, nbytes = None, 0
     if workspace is not None:
@@ -361,7 +368,7 @@ def decode(q, k_cache, v_cache, scale: Optional[float] = None, cache_lens=None, 
     B, Sq, Hq, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     need = attn_decode_workspace_bytes(B, Sq, k_cache.shape[1], Hq, k_cache.shape[2], d)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

@@ -82,6 +82,11 @@ attn_status check_decode_shape(const attn_decode_shape* s, attn::DecodeProblem* 
   pr->scale = s->scale;
   pr->cache_lens = s->cache_lens;
   pr->rope_base = s->rope_base;
+  if (!resolve_strides(s->q_stride, s->q_len, s->heads_q, s->head_dim, &pr->sq) ||
+      !resolve_strides(s->kv_stride, s->cache_len, s->heads_kv, s->head_dim, &pr->skv) ||
+      !resolve_strides(s->o_stride, s->q_len, s->heads_q, s->head_dim, &pr->so))
+    return ATTN_ERR_MISALIGNED;
+  if (pr->skv.s > ((int64_t)1 << 22)) return ATTN_ERR_UNSUPPORTED;  // 32-bit tile offsets
   // the count of valid 64-key tiles over all units (one per kv head and
   // 32-row block of its query rows) is a 32-bit int on the device
   const int64_t row_blocks = ((int64_t)s->q_len * (s->heads_q / s->heads_kv) + 31) / 32;

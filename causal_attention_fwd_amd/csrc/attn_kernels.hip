@@ -949,6 +949,7 @@ struct DecArgs {
   float scale;
   int rope;       // 1: query t is rotated at position L - Sq + t before use
   RopeFreq rf;
+  Strides sq, skv, so;  // q; the k and v caches; o
 };
 
 // Valid 64-key tiles of each unit of sequence b.
@@ -989,9 +990,9 @@ __device__ __forceinline__ void decode_segment(const DecArgs& a, int b, int hkv,
   const int G = a.Hq / a.Hkv;
   const int R = G * a.Sq;
   const int L = valid_len(a.lens, b, a.Smax);
-  const int64_t ks = (int64_t)a.Hkv * D;
-  const bf16* Kb = a.k + ((int64_t)b * a.Smax * a.Hkv + hkv) * D;
-  const bf16* Vb = a.v + ((int64_t)b * a.Smax * a.Hkv + hkv) * D;
+  const int64_t ks = a.skv.s;
+  const bf16* Kb = a.k + b * a.skv.b + hkv * a.skv.h;
+  const bf16* Vb = a.v + b * a.skv.b + hkv * a.skv.h;
 
   // the lane's query row rr = 32*rb + r: head hkv*G + rr / Sq, new query
   // t = rr % Sq at cache position L - Sq + t, which sees keys 0 .. L - Sq + t
@@ -1004,7 +1005,7 @@ __device__ __forceinline__ void decode_segment(const DecArgs& a, int b, int hkv,
   const int jmax = row_ok ? L - a.Sq + t : -1;  // last visible key (< 0: none)
 
   FwdState<D, 1> st;
-  const bf16* qrow = a.q + (((int64_t)b * a.Sq + t) * a.Hq + h) * D;
+  const bf16* qrow = a.q + b * a.sq.b + t * a.sq.s + h * a.sq.h;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     bf16x8 qv = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + g * 8) : zero_bf16x8();
@@ -1207,7 +1208,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecArgs a) {
       for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
     }
   }
-  bf16* orow = a.o + (((int64_t)b * a.Sq + t) * a.Hq + h) * D;
+  bf16* orow = a.o + b * a.so.b + t * a.so.s + h * a.so.h;
   const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) orow[e * 64 + lane] = (bf16)(acc[e] * inv);
@@ -1422,7 +1423,7 @@ hipError_t launch_decode(const DecodeProblem& pr, const DecodePlan& plan, const 
             reinterpret_cast<int*>(ws), reinterpret_cast<int2*>(ws + plan.off_uinfo),
             reinterpret_cast<float*>(ws + plan.off_o), reinterpret_cast<float*>(ws + plan.off_lse),
             (bf16*)o, lse, pr.B, pr.Sq, pr.Smax, pr.Hq, pr.Hkv, plan.waves, plan.rb, plan.ru, pr.scale,
-            pr.rope_base > 0.f, rope_freq_d(pr.rope_base, pr.d)};
+            pr.rope_base > 0.f, rope_freq_d(pr.rope_base, pr.d), pr.sq, pr.skv, pr.so};
   const int64_t merge_blocks = ((int64_t)pr.B * pr.Hq * pr.Sq + 3) / 4;
   hipError_t e;
   if (pr.d == 64) {

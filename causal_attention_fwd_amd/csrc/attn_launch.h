@@ -46,6 +46,7 @@ struct DecodeProblem {
   float scale;
   const int32_t* cache_lens;  // device int32[B] or nullptr (= Smax)
   float rope_base;            // > 0: new queries rotated at their positions; 0: none
+  Strides sq, skv, so;        // q [B,Sq,Hq,d]; k and v caches [B,Smax,Hkv,d]; o [B,Sq,Hq,d]
 };
 
 // How the decode work is dealt out: `waves` one-wave workgroups share the

@@ -217,6 +217,14 @@ typedef struct attn_decode_shape {
   /* Rotary embedding base for the new queries, or 0 for none (finite and
      >= 0, else ATTN_ERR_INVALID_ARG). */
   float rope_base;
+  /* Optional element strides of the (sequence, position, head) dimensions,
+     as in attn_shape (all zero: dense; multiples of 8, else
+     ATTN_ERR_MISALIGNED; cache position stride at most 2^22). q_stride: q;
+     kv_stride: both caches, e.g. {Hkv*Smax*d, d, Smax*d} for a cache stored
+     head-major as [B, Hkv, Smax, d]; o_stride: o. */
+  int64_t q_stride[3];
+  int64_t kv_stride[3];
+  int64_t o_stride[3];
 } attn_decode_shape;
 
 /*
@@ -233,7 +241,8 @@ typedef struct attn_decode_shape {
 size_t attn_decode_workspace_bytes(const attn_decode_shape* shape);
 
 /*
- * q [B,Sq,Hq,d], k_cache/v_cache [B,Smax,Hkv,d], o [B,Sq,Hq,d] bf16; lse
+ * q [B,Sq,Hq,d], k_cache/v_cache [B,Smax,Hkv,d] (any strides the shape
+ * gives), o [B,Sq,Hq,d] bf16; lse
  * [B,Hq,Sq] fp32; workspace: caller-owned device memory of at least
  * attn_decode_workspace_bytes() bytes, 16-byte aligned (ATTN_ERR_WORKSPACE
  * otherwise), overwritten by the call and free again when the stream has run

@@ -10,8 +10,10 @@ int main(void) {
   printf("attn_shape %zu rope_base %zu q_stride %zu kv_stride %zu o_stride %zu seqlens %zu\n",
          sizeof(attn_shape), offsetof(attn_shape, rope_base), offsetof(attn_shape, q_stride),
          offsetof(attn_shape, kv_stride), offsetof(attn_shape, o_stride), offsetof(attn_shape, seqlens));
-  printf("attn_decode_shape %zu cache_lens %zu rope_base %zu\n", sizeof(attn_decode_shape),
-         offsetof(attn_decode_shape, cache_lens), offsetof(attn_decode_shape, rope_base));
+  printf("attn_decode_shape %zu cache_lens %zu rope_base %zu dq_stride %zu dkv_stride %zu do_stride %zu\n",
+         sizeof(attn_decode_shape), offsetof(attn_decode_shape, cache_lens), offsetof(attn_decode_shape, rope_base),
+         offsetof(attn_decode_shape, q_stride), offsetof(attn_decode_shape, kv_stride),
+         offsetof(attn_decode_shape, o_stride));
   attn_shape s = {0};
   s.batch = 1;
   s.seqlen = 64;

@@ -310,5 +310,7 @@ def test_plain_c_client_and_struct_layouts(lib, tmp_path):
     assert int(vals["cache_lens"]) == attn.AttnDecodeShape.cache_lens.offset
     dline = [l for l in out.splitlines() if l.startswith("attn_decode_shape")][0].split()
     assert int(dline[dline.index("rope_base") + 1]) == attn.AttnDecodeShape.rope_base.offset
+    for c_name, f in (("dq_stride", "q_stride"), ("dkv_stride", "kv_stride"), ("do_stride", "o_stride")):
+        assert int(dline[dline.index(c_name) + 1]) == getattr(attn.AttnDecodeShape, f).offset, f
     assert vals["fwd_bad_dim"] == "2" and vals["fwd_null_ptr"] == "1" and vals["fwd_bad_stride"] == "3"
     assert "ATTN_ERR_INVALID_ARG" in out

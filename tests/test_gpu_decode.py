@@ -191,3 +191,25 @@ def test_decode_rope_matches_rotated_queries_without_rope():
     b = run_decode(inp_rot, 0.0)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("rope_base", [0.0, 10000.0])
+def test_decode_head_major_cache_and_views(rope_base):
+    # caches stored head-major ([B, Hkv, Smax, d], a permuted view here), q a
+    # view into a wider buffer: bitwise equal to the dense layout
+    B, Sq, Smax, Hq, Hkv, d = 3, 2, 900, 16, 4, 64
+    inp = make_decode_inputs(B, Sq, Smax, Hq, Hkv, d, 7900, (1, Smax))
+    dev = torch.device("cuda")
+    kh = inp.k_cache.to(dev).permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    vh = inp.v_cache.to(dev).permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    assert kh.stride() == (Hkv * Smax * d, d, Smax * d, 1)
+    wide = torch.zeros(B, Sq, Hq + 5, d, dtype=torch.bfloat16, device=dev)
+    wide[:, :, :Hq] = inp.q.to(dev)
+    q = wide[:, :, :Hq]
+    lens = inp.cache_lens.to(dev)
+    o, lse = attn.decode(q, kh, vh, inp.scale, lens, rope_base)
+    od, lsed = attn.decode(inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev), inp.scale, lens, rope_base)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), od.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lsed.view(torch.int32))
+    check((o.float().cpu().numpy(), lse.cpu().numpy()), ref_decode(inp, rope_base), "decode-head-major")
