@@ -1248,7 +1248,7 @@ namespace {
 #define ATTN_DQ_NT128 1
 #endif
 #ifndef ATTN_DQ_OCC128
-#define ATTN_DQ_OCC128 1
+#define ATTN_DQ_OCC128 2
 #endif
 #ifndef ATTN_DKDV_OCC128
 #define ATTN_DKDV_OCC128 1
