@@ -3,8 +3,11 @@
 
 One step = the whole path over one batch of resident synthetic inputs:
 attn_fwd -> attn_bwd_preprocess -> attn_bwd_dkdv -> attn_bwd_dq (the last two
-are exactly the two launches attn_bwd makes). Default workload: the 1B-class
-Llama attention, B=4, S=2048, Hq=32, Hkv=8, d=64, dO ~ N(0, 0.1).
+are exactly the two launches attn_bwd makes). The step is timed as replays of
+its captured HIP graph (no host-side launch cost; --eager times Python-issued
+launches instead); per-kernel times come from an eager pass with HIP events.
+Default workload: the 1B-class Llama attention, B=4, S=2048, Hq=32, Hkv=8,
+d=64, dO ~ N(0, 0.1).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload llama1b]
 
@@ -373,12 +376,13 @@ def run(args):
                   "p90": round(step_ev[min(len(step_ev) - 1, (9 * len(step_ev)) // 10)], 4)}
     ms_step = wall * 1e3 / args.steps
     launch = "eager"
-    if args.graph:
-        # the same four launches captured in one HIP graph, replayed; the
-        # per-kernel times above stay those of the eager launches
-        if args.rope:
-            sys.exit("--graph and --rope together are not supported")
-        graph = attn.capture_step(q, k, v, do, o, lse, delta, dq, dk, dv, scale, sl, causal)
+    if not args.eager:
+        # the same launches captured in one HIP graph and replayed (the
+        # default: no host-side launch cost in the timed step); the per-kernel
+        # times above stay those of the eager launches
+        graph = attn.capture_step(q, k, v, do, o, lse, delta, dq, dk, dv, scale, sl, causal, None,
+                                  fused=args.fused_bwd, rope_base=rb, q_rot=qa if args.rope else None,
+                                  k_rot=ka if args.rope else None)
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
@@ -386,8 +390,9 @@ def run(args):
         for _ in range(args.steps):
             graph.replay()
         torch.cuda.synchronize()
-        log(f"eager step {ms_step:.4f} ms, graph step {(time.perf_counter() - t0) * 1e3 / args.steps:.4f} ms")
-        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        g_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        log(f"eager step {ms_step:.4f} ms, graph step {g_step:.4f} ms")
+        ms_step = g_step
         launch = "hip graph"
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
 
@@ -523,7 +528,7 @@ def run_decode(args):
     ms_call = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     ms_step = wall * 1e3 / args.steps
     launch = "eager"
-    if args.graph:
+    if not args.eager:
         # one graph per rotated input set (a graph is bound to its tensors)
         graphs = []
         for q, k, v, o, lse in sets:
@@ -575,8 +580,10 @@ def main():
                     help="cache storage for --decode: position-major [B,Smax,Hkv,d] or head-major [B,Hkv,Smax,d]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work in cpu_baseline")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step as eager launches from Python instead of replays of its captured HIP graph")
     ap.add_argument("--graph", action="store_true",
-                    help="time the step as one captured HIP graph (fwd, preprocess, dK/dV, dQ) replayed")
+                    help="(the default) time replays of the step captured in one HIP graph")
     ap.add_argument("--non-causal", action="store_true",
                     help="bidirectional attention (causal = 0): every key of the valid prefix, all pairs priced")
     ap.add_argument("--fused-bwd", action="store_true",

@@ -424,7 +424,7 @@ def backward(q, k, v, o, d_o, lse, scale: Optional[float] = None, seqlens=None, 
 # ------------------------------------------------------------------ graph capture
 
 def capture_step(q, k, v, d_o, o, lse, delta, dq, dk, dv, scale: float, seqlens=None, causal: bool = True,
-                 workspace=None, fused: bool = False):
+                 workspace=None, fused: bool = False, rope_base: float = 0.0, q_rot=None, k_rot=None):
     """Capture one training step of the path -- attn_fwd, attn_bwd_preprocess,
     attn_bwd (its dK/dV and dQ launches) -- into a HIP graph (torch.cuda.CUDAGraph)
     and return it; ``graph.replay()`` then reruns all four kernels with one
@@ -433,17 +433,23 @@ def capture_step(q, k, v, d_o, o, lse, delta, dq, dk, dv, scale: float, seqlens=
     The library is capture-safe: every entry point only enqueues kernels on the
     current stream (no allocation, no synchronisation, no memset), so the graph
     holds exactly the four kernel nodes (three with fused=True: attn_fwd then
-    attn_bwd_fused). Shapes, pointers, scale, seqlens and causal are fixed at
+    attn_bwd_fused; one more, the attn_rope pre-pass into q_rot / k_rot, with
+    rope_base > 0). Shapes, pointers, scale, seqlens and causal are fixed at
     capture time."""
     cz = int(bool(causal))
+    if rope_base and (q_rot is None or k_rot is None):
+        raise ValueError("rope_base needs the q_rot and k_rot buffers")
+    qa, ka = (q_rot, k_rot) if rope_base else (q, k)
 
     def step():
-        attn_fwd(q, k, v, o, lse, scale, seqlens, cz)
+        if rope_base:
+            attn_rope(q, k, q_rot, k_rot, rope_base)
+        attn_fwd(qa, ka, v, o, lse, scale, seqlens, cz)
         if fused:
-            attn_bwd_fused(q, k, v, o, d_o, lse, delta, dq, dk, dv, scale, seqlens, workspace, cz)
+            attn_bwd_fused(qa, ka, v, o, d_o, lse, delta, dq, dk, dv, scale, seqlens, workspace, cz, rope_base)
         else:
             attn_bwd_preprocess(o, d_o, delta, seqlens)
-            attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, workspace, cz)
+            attn_bwd(qa, ka, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, workspace, cz, rope_base)
     return _capture(step)
 
 

@@ -16,24 +16,29 @@ from parity import say
 pytestmark = pytest.mark.gpu
 
 
-def _eager(t, scale, sl, causal, fused=False):
-    o, lse = attn.forward(t["q"], t["k"], t["v"], scale, sl, causal=causal)
+def _eager(t, scale, sl, causal, fused=False, rope_base=0.0):
+    q, k = attn.rope(t["q"], t["k"], rope_base) if rope_base else (t["q"], t["k"])
+    o, lse = attn.forward(q, k, t["v"], scale, sl, causal=causal)
     if fused:
         delta = torch.empty_like(lse)
-        dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
-        attn.attn_bwd_fused(t["q"], t["k"], t["v"], o, t["do"], lse, delta, dq, dk, dv, scale, sl, None,
-                            int(causal))
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(t["v"])
+        attn.attn_bwd_fused(q, k, t["v"], o, t["do"], lse, delta, dq, dk, dv, scale, sl, None, int(causal),
+                            rope_base)
     else:
-        dq, dk, dv, delta = attn.backward(t["q"], t["k"], t["v"], o, t["do"], lse, scale, sl, causal=causal)
+        dq, dk, dv, delta = attn.backward(q, k, t["v"], o, t["do"], lse, scale, sl, causal=causal,
+                                          rope_base=rope_base)
     torch.cuda.synchronize()
     return {"O": o, "LSE": lse, "D": delta, "dQ": dq, "dK": dk, "dV": dv}
 
 
-@pytest.mark.parametrize("causal,padded,fused", [(True, False, False), (True, True, False), (False, True, False),
-                                                 (True, True, True)])
-def test_graph_replays_match_eager(causal, padded, fused):
+@pytest.mark.parametrize("causal,padded,fused,rope_base", [(True, False, False, 0.0), (True, True, False, 0.0),
+                                                           (False, True, False, 0.0), (True, True, True, 0.0),
+                                                           (True, False, False, 10000.0),
+                                                           (True, True, True, 10000.0)])
+def test_graph_replays_match_eager(causal, padded, fused, rope_base):
     B, S, Hq, Hkv, d = 2, 384, 8, 2, 64
-    say(f"graph capture: B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} causal={causal} padded={padded}")
+    say(f"graph capture: B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} causal={causal} padded={padded} fused={fused} "
+        f"rope={rope_base}")
     dev = torch.device("cuda")
     inputs = [make_inputs(B, S, Hq, Hkv, d, 900 + i, padded=padded, seqlen_range=(200, 384)) for i in range(3)]
     # buffers the graph is bound to
@@ -44,8 +49,9 @@ def test_graph_replays_match_eager(causal, padded, fused):
     delta = torch.empty(B, Hq, S, device=dev)
     dq, dk, dv = torch.empty_like(buf["q"]), torch.empty_like(buf["k"]), torch.empty_like(buf["v"])
     scale = inputs[0].scale
+    q_rot, k_rot = (torch.empty_like(buf["q"]), torch.empty_like(buf["k"])) if rope_base else (None, None)
     graph = attn.capture_step(buf["q"], buf["k"], buf["v"], buf["do"], o, lse, delta, dq, dk, dv, scale, sl, causal,
-                              fused=fused)
+                              fused=fused, rope_base=rope_base, q_rot=q_rot, k_rot=k_rot)
     outs = {"O": o, "LSE": lse, "D": delta, "dQ": dq, "dK": dk, "dV": dv}
     for rep in range(6):
         inp = inputs[rep % 3]
@@ -59,7 +65,7 @@ def test_graph_replays_match_eager(causal, padded, fused):
         got = {key: val.clone() for key, val in outs.items()}
         # eager work between replays, on separate tensors
         t = {n: getattr(inp, n).to(dev).contiguous() for n in ("q", "k", "v", "do")}
-        ref = _eager(t, scale, inp.seqlens.to(dev) if padded else None, causal, fused)
+        ref = _eager(t, scale, inp.seqlens.to(dev) if padded else None, causal, fused, rope_base)
         for key in got:
             bits = torch.int16 if got[key].dtype == torch.bfloat16 else torch.int32
             np.testing.assert_array_equal(got[key].view(bits).cpu().numpy(), ref[key].view(bits).cpu().numpy(),
