@@ -167,9 +167,10 @@ struct KVBuf {
 };
 
 // ----------------------------------------------------------------------------
-// Forward. One workgroup = one (sequence, query head, block of 128*NT query
-// rows); wave w owns rows [q0 + 32*NT*w, +32*NT). Loop over 64-row K/V tiles up
-// to the block's last row. OCC waves per SIMD (register budget 512/OCC).
+// Forward. One workgroup of W waves = one (sequence, query head, block of
+// 32*NT*W query rows); wave w owns rows [q0 + 32*NT*w, +32*NT). Loop over 64-row
+// K/V tiles up to the block's last row. OCC waves per SIMD (register budget
+// 512/OCC).
 //
 // Online softmax with a lazily refreshed reference: each row keeps the maximum
 // it last rescaled to (mu). A tile's exponents use mu unless the row maximum
@@ -267,11 +268,11 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, NT>& st, const bf16* Ks, co
     }
 }
 
-template <int D, int NT, int OCC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+template <int D, int NT, int OCC, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fwd_kernel(FwdArgs a) {
   constexpr int BN = 64;
-  constexpr int BM = 4 * 32 * NT;
+  constexpr int BM = W * 32 * NT;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
   constexpr int KVT = TileLayout<D>::template elems<BN>();
@@ -323,8 +324,8 @@ void fwd_kernel(FwdArgs a) {
 
   const KVBuf b0{sK0, sV0, 0}, b1{sK1, sV1, 1};
   auto fetch = [&](int kt, const KVBuf& buf) {
-    tile_load_lds<BN, D, 4>(Kb, ks, kt * BN, L, buf.k, wave, lane);
-    tile_load_lds<BN, D, 4>(Vb, ks, kt * BN, L, buf.v, wave, lane);
+    tile_load_lds<BN, D, W>(Kb, ks, kt * BN, L, buf.k, wave, lane);
+    tile_load_lds<BN, D, W>(Vb, ks, kt * BN, L, buf.v, wave, lane);
   };
   auto compute = [&](int kt, const KVBuf& buf) {
     const int j0 = kt * BN;
@@ -741,11 +742,11 @@ __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, cons
     }
 }
 
-template <int D, int NT, int OCC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+template <int D, int NT, int OCC, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = 64;
-  constexpr int BM = 4 * 32 * NT;
+  constexpr int BM = W * 32 * NT;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
   constexpr int KVT = TileLayout<D>::template elems<BN>();
@@ -818,8 +819,8 @@ void bwd_dq_kernel(BwdArgs a) {
   // K/V tiles stream straight into LDS (no staging registers), double-buffered.
   const KVBuf b0{sK0, sV0, 0}, b1{sK1, sV1, 1};
   auto fetch = [&](int kt, const KVBuf& buf) {
-    tile_load_lds<BN, D, 4>(Kb, ks, kt * BN, L, buf.k, wave, lane);
-    tile_load_lds<BN, D, 4>(Vb, ks, kt * BN, L, buf.v, wave, lane);
+    tile_load_lds<BN, D, W>(Kb, ks, kt * BN, L, buf.k, wave, lane);
+    tile_load_lds<BN, D, W>(Vb, ks, kt * BN, L, buf.v, wave, lane);
   };
   auto compute = [&](int kt, const KVBuf& buf) {
     const int j0 = kt * BN;
@@ -1218,8 +1219,10 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecArgs a) {
 namespace {
 
 // Per head dimension: 32-row tiles per wave (NT: query rows in the forward and
-// dQ passes; the dK/dV pass always gives each wave 32 key rows) and waves per
-// SIMD (OCC: the register budget per wave is 512 / OCC).
+// dQ passes; the dK/dV pass always gives each wave 32 key rows), waves per
+// SIMD (OCC: the register budget per wave is 512 / OCC) and waves per
+// workgroup of the forward and dQ passes (W: the waves of a workgroup share
+// each K/V tile loaded into LDS).
 #ifndef ATTN_FWD_NT64
 #define ATTN_FWD_NT64 2
 #endif
@@ -1238,6 +1241,18 @@ namespace {
 #ifndef ATTN_DKDV_GROUPS64
 #define ATTN_DKDV_GROUPS64 2
 #endif
+#ifndef ATTN_FWD_W64
+#define ATTN_FWD_W64 4
+#endif
+#ifndef ATTN_FWD_W128
+#define ATTN_FWD_W128 8
+#endif
+#ifndef ATTN_DQ_W64
+#define ATTN_DQ_W64 4
+#endif
+#ifndef ATTN_DQ_W128
+#define ATTN_DQ_W128 4
+#endif
 #ifndef ATTN_FWD_NT128
 #define ATTN_FWD_NT128 1
 #endif
@@ -1255,13 +1270,13 @@ namespace {
 #endif
 template <int D> struct Tiles;
 template <> struct Tiles<64> {
-  static constexpr int FWD_NT = ATTN_FWD_NT64, FWD_OCC = ATTN_FWD_OCC64;
-  static constexpr int DQ_NT = ATTN_DQ_NT64, DQ_OCC = ATTN_DQ_OCC64;
+  static constexpr int FWD_NT = ATTN_FWD_NT64, FWD_OCC = ATTN_FWD_OCC64, FWD_W = ATTN_FWD_W64;
+  static constexpr int DQ_NT = ATTN_DQ_NT64, DQ_OCC = ATTN_DQ_OCC64, DQ_W = ATTN_DQ_W64;
   static constexpr int DKDV_NTJ = 1, DKDV_OCC = ATTN_DKDV_OCC64, DKDV_GROUPS = ATTN_DKDV_GROUPS64;
 };
 template <> struct Tiles<128> {
-  static constexpr int FWD_NT = ATTN_FWD_NT128, FWD_OCC = ATTN_FWD_OCC128;
-  static constexpr int DQ_NT = ATTN_DQ_NT128, DQ_OCC = ATTN_DQ_OCC128;
+  static constexpr int FWD_NT = ATTN_FWD_NT128, FWD_OCC = ATTN_FWD_OCC128, FWD_W = ATTN_FWD_W128;
+  static constexpr int DQ_NT = ATTN_DQ_NT128, DQ_OCC = ATTN_DQ_OCC128, DQ_W = ATTN_DQ_W128;
   static constexpr int DKDV_NTJ = 1, DKDV_OCC = ATTN_DKDV_OCC128, DKDV_GROUPS = 1;
 };
 
@@ -1288,10 +1303,11 @@ RopeFreq rope_freq(const Problem& pr) { return rope_freq_d(pr.rope_base, pr.d); 
 template <int D>
 hipError_t fwd_d(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,
                  hipStream_t stream) {
-  constexpr int NT = Tiles<D>::FWD_NT;
+  constexpr int NT = Tiles<D>::FWD_NT, W = Tiles<D>::FWD_W;
   FwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, pr.seqlens,
-            pr.B, pr.S, pr.Hq, pr.Hkv, cdiv(pr.S, 128 * NT), pr.scale, pr.causal, pr.sq, pr.skv, pr.so};
-  return launch((const void*)&fwd_kernel<D, NT, Tiles<D>::FWD_OCC>, (int64_t)a.nqb * pr.B * pr.Hq, a, stream);
+            pr.B, pr.S, pr.Hq, pr.Hkv, cdiv(pr.S, 32 * NT * W), pr.scale, pr.causal, pr.sq, pr.skv, pr.so};
+  return launch((const void*)&fwd_kernel<D, NT, Tiles<D>::FWD_OCC, W>, (int64_t)a.nqb * pr.B * pr.Hq, a, stream,
+                64 * W);
 }
 
 template <int D>
@@ -1319,12 +1335,13 @@ template <int D>
 hipError_t dq_d(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
                 const float* lse, const float* delta, void* dq, const void* o, float* delta_out,
                 hipStream_t stream) {
-  constexpr int NT = Tiles<D>::DQ_NT;
+  constexpr int NT = Tiles<D>::DQ_NT, W = Tiles<D>::DQ_W;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             (bf16*)dq, nullptr, nullptr, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
-            cdiv(pr.S, 128 * NT), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so,
+            cdiv(pr.S, 32 * NT * W), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so,
             (const bf16*)o, delta_out};
-  return launch((const void*)&bwd_dq_kernel<D, NT, Tiles<D>::DQ_OCC>, (int64_t)a.nblk * pr.B * pr.Hq, a, stream);
+  return launch((const void*)&bwd_dq_kernel<D, NT, Tiles<D>::DQ_OCC, W>, (int64_t)a.nblk * pr.B * pr.Hq, a, stream,
+                64 * W);
 }
 
 template <int D>
