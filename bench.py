@@ -293,6 +293,26 @@ def cpu_baseline(w, inp, budget_s: float, causal: bool = True, rope_base: float 
                       f"{dt:.1f} s"}
 
 
+def time_graph_replays(torch, makers, args):
+    """Capture one HIP graph per maker, replay them in turn (warm-up, then the
+    timed steps between synchronisations) and return ms per step; None when a
+    capture fails (the caller then keeps the eager timing)."""
+    try:
+        graphs = [make() for make in makers]
+    except Exception as e:  # capture errors only; a faulting replay is not caught
+        log(f"graph capture failed ({type(e).__name__}: {e}); timing the eager launches instead")
+        torch.cuda.synchronize()
+        return None
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / args.steps
+
+
 def run(args):
     import torch
     import causal_attention_fwd_amd as attn
@@ -380,20 +400,17 @@ def run(args):
         # the same launches captured in one HIP graph and replayed (the
         # default: no host-side launch cost in the timed step); the per-kernel
         # times above stay those of the eager launches
-        graph = attn.capture_step(q, k, v, do, o, lse, delta, dq, dk, dv, scale, sl, causal, None,
-                                  fused=args.fused_bwd, rope_base=rb, q_rot=qa if args.rope else None,
-                                  k_rot=ka if args.rope else None)
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        g_step = (time.perf_counter() - t0) * 1e3 / args.steps
-        log(f"eager step {ms_step:.4f} ms, graph step {g_step:.4f} ms")
-        ms_step = g_step
-        launch = "hip graph"
+        def capture():
+            return attn.capture_step(q, k, v, do, o, lse, delta, dq, dk, dv, scale, sl, causal, None,
+                                     fused=args.fused_bwd, rope_base=rb, q_rot=qa if args.rope else None,
+                                     k_rot=ka if args.rope else None)
+        g_step = time_graph_replays(torch, [capture], args)
+        if g_step is None:
+            launch = "eager (graph capture failed)"
+        else:
+            log(f"eager step {ms_step:.4f} ms, graph step {g_step:.4f} ms")
+            ms_step = g_step
+            launch = "hip graph"
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
 
     # roofline of the dominant kernel
@@ -530,20 +547,15 @@ def run_decode(args):
     launch = "eager"
     if not args.eager:
         # one graph per rotated input set (a graph is bound to its tensors)
-        graphs = []
-        for q, k, v, o, lse in sets:
-            graphs.append(attn.capture_decode(q, k, v, o, lse, inp.scale, lens, ws))
-        for i in range(args.warmup):
-            graphs[i % copies].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            graphs[i % copies].replay()
-        torch.cuda.synchronize()
-        g_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        log(f"eager call {ms_step:.4f} ms, graph replay {g_ms:.4f} ms")
-        ms_step = g_ms
-        launch = "hip graph"
+        makers = [lambda t=t: attn.capture_decode(t[0], t[1], t[2], t[3], t[4], inp.scale, lens, ws)
+                  for t in sets]
+        g_ms = time_graph_replays(torch, makers, args)
+        if g_ms is None:
+            launch = "eager (graph capture failed)"
+        else:
+            log(f"eager call {ms_step:.4f} ms, graph replay {g_ms:.4f} ms")
+            ms_step = g_ms
+            launch = "hip graph"
     gbs = nb["total"] / (ms_step * 1e-3) / 1e9
     achieved = nb["total"] / (ms_call * 1e-3) / 1e9
     t_split, t_merge = read_traffic("dsplit", w.name), read_traffic("dmerge", w.name)
