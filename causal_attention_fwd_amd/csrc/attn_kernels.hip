@@ -679,13 +679,18 @@ void bwd_dkdv_kernel(BwdArgs a) {
 // ----------------------------------------------------------------------------
 // Backward dQ. Same tiling as the forward: one workgroup per (sequence, query
 // head, query block); recompute S^T and dP^T per 64-row K/V tile, then
-// dQ^T += K^T dS^T.
+// dQ^T += K^T dS^T. The dP^T accumulator starts from -D (one MFMA of a ones
+// column against -D as a bf16 pair hi + lo, |hi + lo + D| <= 2^-16 |D|), so
+// dS = P (dP - D) costs one multiply per element.
 // ----------------------------------------------------------------------------
 template <int D, int NT>
 struct DqState {
   bf16x8 qf[NT][D / 16], df[NT][D / 16];
   float l2[NT], dd[NT];
   f32x16 acc[D / 32][NT];
+  // -D as a rank-one term of the dP^T product: a column of ones (A) against
+  // -D split into a bf16 pair hi + lo (B, k = 0 and 1 of the lane's query)
+  bf16x8 ones, nd[NT];
 };
 
 // One 64-key tile for one wave. MASK: key register offset must be <= lim[t]
@@ -700,7 +705,7 @@ __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, cons
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       s[mt][t] = zero16();
-      dp[mt][t] = zero16();
+      dp[mt][t] = mfma32(st.ones, st.nd[t], zero16());  // every row: -D of the lane's query
     }
   prio_mfma<ATTN_PRIO_DQ>();
 #pragma unroll
@@ -725,7 +730,7 @@ __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, cons
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(__builtin_fmaf(s[mt][t][r], c, -st.l2[t]));
         if (MASK && mt * 32 + creg_off(r) > lim[t]) p = 0.f;
-        dp[mt][t][r] = p * (dp[mt][t][r] - st.dd[t]);
+        dp[mt][t][r] = p * dp[mt][t][r];  // dS = P (dP - D)
       }
   bf16x8 sb[4][NT];
 #pragma unroll
@@ -783,6 +788,11 @@ void bwd_dq_kernel(BwdArgs a) {
   const float c = a.scale * kLog2e;
 
   DqState<D, NT> st;
+  st.ones = zero_bf16x8();
+  if (g == 0) {
+    st.ones[0] = (bf16)1.f;
+    st.ones[1] = (bf16)1.f;
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int row = qw + t * 32 + l32;
@@ -810,6 +820,17 @@ void bwd_dq_kernel(BwdArgs a) {
       if (g == 0 && row < S) a.delta_out[((int64_t)b * a.Hq + h) * S + row] = valid ? dsum : 0.f;
     } else {
       st.dd[t] = valid ? Db[row] : 0.f;
+    }
+    {
+      const float nd = -st.dd[t];
+      const bf16 hi = (bf16)nd;
+      const bf16 lo = (bf16)(nd - (float)hi);
+      bf16x8 v = zero_bf16x8();
+      if (g == 0) {
+        v[0] = hi;
+        v[1] = lo;
+      }
+      st.nd[t] = v;
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.acc[dt][t] = zero16();
