@@ -69,6 +69,18 @@ def test_fused_backward_with_rope():
     compare(got, ref, "fused-rope")
 
 
+def test_fused_backward_rope_d128_padded_bidirectional():
+    say("fused bwd with RoPE, d=128, padded, bidirectional")
+    inp = make_inputs(2, 190, 4, 2, 128, 5211, padded=True, seqlen_range=(60, 190))
+    got, sep = fused_run(inp, False, 10000.0)
+    q, k, v, do, sl = host_inputs(inp)
+    ref = oracle_rope.backward(q, k, v, do, inp.scale, sl, 10000.0, causal=False, bf16_storage=True)
+    compare(got, ref, "fused-rope-d128-bidir")
+    np.testing.assert_allclose(got["D"], sep["D"], rtol=1e-5, atol=1e-6)
+    for key in ("dQ", "dK", "dV"):
+        np.testing.assert_allclose(got[key], sep[key], rtol=0, atol=2e-2, err_msg=key)
+
+
 @pytest.mark.timeout(600)
 def test_fused_backward_llama1b_units():
     B, S, Hq, Hkv, d = 4, 2048, 32, 8, 64

@@ -116,3 +116,44 @@ def test_rope_on_views():
     same(k_rot, kd)
     for got, want in zip((o, lse, dq, dk, dv), ref):
         same(got, want)
+
+
+def test_fused_backward_on_views():
+    """attn_bwd_fused (dQ pass reading O for D) with every group strided: Q, K, V
+    views into a projection output, O / dO / dQ views into one wider buffer,
+    dK / dV into a gradient buffer of the projection's layout; bitwise equal to
+    the same call on dense copies."""
+    B, S, Hq, Hkv, d = 2, 260, 4, 2, 64
+    say(f"fused backward on views B={B} S={S} Hq={Hq} Hkv={Hkv} d={d}")
+    inp = make_inputs(B, S, Hq, Hkv, d, 4545, padded=True, seqlen_range=(70, 260))
+    sl = inp.seqlens.to(DEV)
+    H = Hq + 2 * Hkv
+    proj = torch.empty(B, S, H, d, dtype=torch.bfloat16, device=DEV)
+    proj[:, :, :Hq] = inp.q.to(DEV)
+    proj[:, :, Hq:Hq + Hkv] = inp.k.to(DEV)
+    proj[:, :, Hq + Hkv:] = inp.v.to(DEV)
+    q, k, v = proj[:, :, :Hq], proj[:, :, Hq:Hq + Hkv], proj[:, :, Hq + Hkv:]
+    obuf = torch.empty(B, S, 3 * Hq, d, dtype=torch.bfloat16, device=DEV)  # O | dO | dQ side by side
+    o, do, dq = obuf[:, :, :Hq], obuf[:, :, Hq:2 * Hq], obuf[:, :, 2 * Hq:]
+    do.copy_(inp.do.to(DEV))
+    dproj = torch.zeros_like(proj)
+    dk, dv = dproj[:, :, Hq:Hq + Hkv], dproj[:, :, Hq + Hkv:]
+    lse = torch.empty(B, Hq, S, device=DEV)
+    delta = torch.empty_like(lse)
+    attn.attn_fwd(q, k, v, o, lse, inp.scale, sl)
+    attn.attn_bwd_fused(q, k, v, o, do, lse, delta, dq, dk, dv, inp.scale, sl)
+    # the same call on dense copies
+    qc, kc, vc, doc = (x.contiguous() for x in (q, k, v, do))
+    oc, lc = torch.empty_like(qc), torch.empty_like(lse)
+    dc = torch.empty_like(lse)
+    dqc, dkc, dvc = torch.empty_like(qc), torch.empty_like(kc), torch.empty_like(vc)
+    attn.attn_fwd(qc, kc, vc, oc, lc, inp.scale, sl)
+    attn.attn_bwd_fused(qc, kc, vc, oc, doc, lc, dc, dqc, dkc, dvc, inp.scale, sl)
+    torch.cuda.synchronize()
+    for got, want in zip((o, lse, delta, dq, dk, dv), (oc, lc, dc, dqc, dkc, dvc)):
+        same(got, want)
+    assert torch.count_nonzero(dproj[:, :, :Hq]) == 0
+    host = lambda x: x.float().cpu().numpy()  # noqa: E731
+    gpu = {"O": host(o), "LSE": host(lse), "D": host(delta), "dQ": host(dq), "dK": host(dk), "dV": host(dv)}
+    qn, kn, vn, don, sln = host_inputs(inp)
+    compare(gpu, oracle.backward(qn, kn, vn, don, inp.scale, sln), "fused-bwd-views")
