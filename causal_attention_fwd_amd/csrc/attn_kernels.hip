@@ -888,53 +888,52 @@ void bwd_dq_kernel(BwdArgs a) {
 // RoPE pre-pass: q_rot, k_rot = the rotated q and k, once per step (HBM-bound:
 // every element read and written once). The forward and both backward passes
 // then read the rotated tensors; the backward passes take dQ and dK back
-// through the adjoint in their epilogues. One thread per 8 consecutive
-// elements (16 bytes, four pairs) of a row; rows of q first, then rows of k.
+// through the adjoint in their epilogues. One wave per (sequence, position):
+// its D/2 (cos, sin) pairs are computed once into LDS, then each lane rotates
+// 8 consecutive elements (16 bytes, four pairs) at a time, walking the rows of
+// every q head, then every k head, of that position.
 // ----------------------------------------------------------------------------
 struct RopeArgs {
   const bf16* q;
   const bf16* k;
   bf16* qr;
   bf16* kr;
-  int64_t nq, nk;  // 8-element chunks of q and of k
   int S, Hq, Hkv;
   RopeFreq rf;
   Strides sq, skv;  // q and q_rot; k and k_rot
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs a) {
-  int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const bf16* src = a.q;
-  bf16* dst = a.qr;
-  int H = a.Hq;
-  Strides st = a.sq;
-  if (idx >= a.nq) {
-    idx -= a.nq;
-    if (idx >= a.nk) return;
-    src = a.k;
-    dst = a.kr;
-    H = a.Hkv;
-    st = a.skv;
-  }
-  constexpr int CPR = D / 8;  // chunks per row
-  const int64_t row = idx / CPR;  // (b * S + p) * H + h
-  const int c = (int)(idx - row * CPR);
-  const int h = (int)(row % H);
-  const int64_t bp = row / H;
-  const int p = (int)(bp % a.S);
-  const int64_t off = (bp / a.S) * st.b + (int64_t)p * st.s + (int64_t)h * st.h + c * 8;
-  const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + off);
-  bf16x8 y;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
+__global__ __launch_bounds__(64) void rope_kernel(RopeArgs a) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  __shared__ float2 cs_tab[D / 2];
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x / a.S;
+  const int p = blockIdx.x - b * a.S;
+  if (lane < D / 2) {
     float cs, sn;
-    rope_cos_sin(a.rf.phi[c * 4 + e], p, cs, sn);
-    const float x0 = (float)x[2 * e], x1 = (float)x[2 * e + 1];
-    y[2 * e] = (bf16)(x0 * cs - x1 * sn);
-    y[2 * e + 1] = (bf16)(x0 * sn + x1 * cs);
+    rope_cos_sin(a.rf.phi[lane], p, cs, sn);
+    cs_tab[lane] = make_float2(cs, sn);
   }
-  *reinterpret_cast<bf16x8*>(dst + off) = y;
+  __syncthreads();
+  const int nq = a.Hq * CPR, n = (a.Hq + a.Hkv) * CPR;
+  for (int i = lane; i < n; i += 64) {
+    const bool isq = i < nq;
+    const int ih = isq ? i : i - nq;
+    const int h = ih / CPR, c = ih % CPR;
+    const Strides& st = isq ? a.sq : a.skv;
+    const int64_t off = (int64_t)b * st.b + (int64_t)p * st.s + (int64_t)h * st.h + c * 8;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>((isq ? a.q : a.k) + off);
+    bf16x8 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float2 t = cs_tab[c * 4 + e];
+      const float x0 = (float)x[2 * e], x1 = (float)x[2 * e + 1];
+      y[2 * e] = (bf16)(x0 * t.x - x1 * t.y);
+      y[2 * e + 1] = (bf16)(x0 * t.y + x1 * t.x);
+    }
+    *reinterpret_cast<bf16x8*>((isq ? a.qr : a.kr) + off) = y;
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -1367,10 +1366,8 @@ hipError_t dq_d(const Problem& pr, const void* q, const void* k, const void* v, 
 
 template <int D>
 hipError_t rope_d(const Problem& pr, const void* q, const void* k, void* qr, void* kr, hipStream_t stream) {
-  RopeArgs a{(const bf16*)q, (const bf16*)k, (bf16*)qr, (bf16*)kr,
-             (int64_t)pr.B * pr.S * pr.Hq * (D / 8), (int64_t)pr.B * pr.S * pr.Hkv * (D / 8),
-             pr.S, pr.Hq, pr.Hkv, rope_freq(pr), pr.sq, pr.skv};
-  return launch((const void*)&rope_kernel<D>, (a.nq + a.nk + kThreads - 1) / kThreads, a, stream);
+  RopeArgs a{(const bf16*)q, (const bf16*)k, (bf16*)qr, (bf16*)kr, pr.S, pr.Hq, pr.Hkv, rope_freq(pr), pr.sq, pr.skv};
+  return launch((const void*)&rope_kernel<D>, (int64_t)pr.B * pr.S, a, stream, 64);
 }
 
 }  // namespace
@@ -1413,8 +1410,8 @@ int64_t max_grid(const Problem& pr) {
   const int64_t nb = (pr.S + 127) / 128;
   int64_t m = nb * pr.B * pr.Hq;
   const int64_t pre = ((int64_t)pr.B * pr.S * pr.Hq + 15) / 16;
-  // RoPE pre-pass: one thread per 8 elements of q and k
-  const int64_t rope = ((int64_t)pr.B * pr.S * (pr.Hq + pr.Hkv) * (pr.d / 8) + kThreads - 1) / kThreads;
+  // RoPE pre-pass: one workgroup per (sequence, position)
+  const int64_t rope = (int64_t)pr.B * pr.S;
   m = m > pre ? m : pre;
   return m > rope ? m : rope;
 }
