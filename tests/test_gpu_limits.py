@@ -65,3 +65,50 @@ def test_decode_many_short_caches():
     fin = np.isfinite(rl)
     assert np.max(np.abs(lg[fin] - rl[fin])) <= 1e-3
     assert np.linalg.norm(og - ro) / np.linalg.norm(ro) <= 1e-2 and np.max(np.abs(og - ro)) <= 5e-2
+
+
+@pytest.mark.timeout(600)
+def test_longest_sequence_sampled_rows_and_gradient_identities():
+    """One sequence of 131072 positions (one kv group of four query heads).
+    Forward: sampled rows against the oracle, each row being the last row of its
+    causal prefix, which the oracle's decode form computes from that prefix
+    alone. Backward: identities that hold at any size because every row of P
+    sums to one: sum_j dV_j equals the group's sum_i dO_i, and sum_j dS_ij = 0 so
+    sum_j dK_j = 0 (they catch skipped tiles, a wrong LSE or D; the sampled rows
+    check the mask)."""
+    B, S, Hq, Hkv, d = 1, 131072, 4, 1, 64
+    say(f"longest sequence B={B} S={S} Hq={Hq} Hkv={Hkv} d={d}")
+    inp = make_inputs(B, S, Hq, Hkv, d, 131072)
+    dev = torch.device("cuda")
+    q, k, v, do = (getattr(inp, n).to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = attn.forward(q, k, v, inp.scale)
+    dq, dk, dv, _ = attn.backward(q, k, v, o, do, lse, inp.scale)
+    torch.cuda.synchronize()
+    for name, t in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert torch.isfinite(t.float()).all(), name
+    qn, kn, vn, _, _ = host_inputs(inp)
+    on, ln = o.float().cpu().numpy(), lse.cpu().numpy()
+    for i in (0, 1, 63, 64, 4095, 65535, 65536, 100003, S - 1):
+        ro, rl = oracle.decode(qn[:, i:i + 1], kn[:, :i + 1], vn[:, :i + 1], inp.scale)
+        err_o = float(np.max(np.abs(on[:, i] - ro[:, 0])))
+        err_l = float(np.max(np.abs(ln[:, :, i] - rl[:, :, 0])))
+        say(f"  row {i}: O max err {err_o:.2e}, LSE max err {err_l:.2e}")
+        assert err_o <= TOL_MAX_ABS and err_l <= TOL_LSE, i
+    # sums over all keys, in fp64, against the same sums of dO; the bound is a
+    # multiple of the expected bf16 rounding noise, far below a missing tile's effect
+    sdv = dv.double().sum(dim=1)[0, 0]
+    sdo = do.double().sum(dim=(1, 2))[0]
+    sdk = dk.double().sum(dim=1)[0, 0]
+    noise_v = float(dv.double().pow(2).sum().sqrt()) * 2.0 ** -7 + float(do.double().pow(2).sum().sqrt()) * 2.0 ** -7
+    # dK also carries D's own rounding (D comes from the bf16 O): row i's
+    # sum_j dS_ij is off by up to 2^-9 sum_c |dO_ic O_ic|, entering as scale * Q_i
+    dterm = (do.double() * o.double()).abs().sum(dim=-1) * 2.0 ** -9          # [B, S, Hq]
+    qn2 = q.double().pow(2).sum(dim=-1)                                        # [B, S, Hq]
+    noise_k = (float(dk.double().pow(2).sum().sqrt()) * 2.0 ** -7
+               + 4 * inp.scale * float((dterm.pow(2) * qn2).sum().sqrt()))
+    err_v = float((sdv - sdo).norm())
+    err_k = float(sdk.norm())
+    say(f"  |sum dV - sum dO| = {err_v:.3e} (|sum dO| = {float(sdo.norm()):.3e}, bound {noise_v:.3e}); "
+        f"|sum dK| = {err_k:.3e} (bound {noise_k:.3e})")
+    assert err_v <= noise_v
+    assert err_k <= noise_k
