@@ -112,3 +112,23 @@ def test_longest_sequence_sampled_rows_and_gradient_identities():
         f"|sum dK| = {err_k:.3e} (bound {noise_k:.3e})")
     assert err_v <= noise_v
     assert err_k <= noise_k
+
+
+@pytest.mark.timeout(600)
+def test_decode_million_position_cache():
+    """Decode against a 2^20-position cache (positions far past 2^16, one unit
+    spread over every wave of the split), compared with the oracle."""
+    B, Sq, Smax, Hq, Hkv, d = 1, 2, 1 << 20, 8, 2, 64
+    inp = make_decode_inputs(B, Sq, Smax, Hq, Hkv, d, 1 << 20, (900000, Smax))
+    say(f"decode B={B} Sq={Sq} Smax={Smax} Hq={Hq} Hkv={Hkv} d={d} lens={inp.cache_lens.tolist()}")
+    dev = torch.device("cuda")
+    o, lse = attn.decode(inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev), inp.scale,
+                         inp.cache_lens.to(dev))
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(inp.q.float().numpy(), inp.k_cache.float().numpy(), inp.v_cache.float().numpy(),
+                           inp.scale, inp.cache_lens.numpy())
+    on, ln = o.float().cpu().numpy(), lse.cpu().numpy()
+    rel, mx = metrics(on, ro)
+    err_l = float(np.max(np.abs(ln - rl)))
+    say(f"  O rel_fro={rel:.2e} max_abs={mx:.2e}; LSE max err {err_l:.2e}")
+    assert rel <= TOL_REL_FRO and mx <= TOL_MAX_ABS and err_l <= TOL_LSE
