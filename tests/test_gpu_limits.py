@@ -67,29 +67,32 @@ def test_decode_many_short_caches():
     assert np.linalg.norm(og - ro) / np.linalg.norm(ro) <= 1e-2 and np.max(np.abs(og - ro)) <= 5e-2
 
 
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "bidirectional"])
 @pytest.mark.timeout(600)
-def test_longest_sequence_sampled_rows_and_gradient_identities():
+def test_longest_sequence_sampled_rows_and_gradient_identities(causal):
     """One sequence of 131072 positions (one kv group of four query heads).
     Forward: sampled rows against the oracle, each row being the last row of its
     causal prefix, which the oracle's decode form computes from that prefix
     alone. Backward: identities that hold at any size because every row of P
     sums to one: sum_j dV_j equals the group's sum_i dO_i, and sum_j dS_ij = 0 so
     sum_j dK_j = 0 (they catch skipped tiles, a wrong LSE or D; the sampled rows
-    check the mask)."""
+    check the mask; a bidirectional row is the decode form over the whole
+    sequence)."""
     B, S, Hq, Hkv, d = 1, 131072, 4, 1, 64
-    say(f"longest sequence B={B} S={S} Hq={Hq} Hkv={Hkv} d={d}")
+    say(f"longest sequence B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
     inp = make_inputs(B, S, Hq, Hkv, d, 131072)
     dev = torch.device("cuda")
     q, k, v, do = (getattr(inp, n).to(dev) for n in ("q", "k", "v", "do"))
-    o, lse = attn.forward(q, k, v, inp.scale)
-    dq, dk, dv, _ = attn.backward(q, k, v, o, do, lse, inp.scale)
+    o, lse = attn.forward(q, k, v, inp.scale, causal=causal)
+    dq, dk, dv, _ = attn.backward(q, k, v, o, do, lse, inp.scale, causal=causal)
     torch.cuda.synchronize()
     for name, t in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
         assert torch.isfinite(t.float()).all(), name
     qn, kn, vn, _, _ = host_inputs(inp)
     on, ln = o.float().cpu().numpy(), lse.cpu().numpy()
     for i in (0, 1, 63, 64, 4095, 65535, 65536, 100003, S - 1):
-        ro, rl = oracle.decode(qn[:, i:i + 1], kn[:, :i + 1], vn[:, :i + 1], inp.scale)
+        last = i + 1 if causal else S
+        ro, rl = oracle.decode(qn[:, i:i + 1], kn[:, :last], vn[:, :last], inp.scale)
         err_o = float(np.max(np.abs(on[:, i] - ro[:, 0])))
         err_l = float(np.max(np.abs(ln[:, :, i] - rl[:, :, 0])))
         say(f"  row {i}: O max err {err_o:.2e}, LSE max err {err_l:.2e}")
