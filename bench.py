@@ -291,9 +291,25 @@ def cpu_baseline(w, inp, budget_s: float, causal: bool = True, rope_base: float 
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    # the forward alone, timed separately on one pass over the same units
+    ffl, t1 = 0.0, time.perf_counter()
+    for b, g in units:
+        hs = slice(g * G, (g + 1) * G)
+        args = (q[b:b + 1, :, hs], k[b:b + 1, :, g:g + 1], v[b:b + 1, :, g:g + 1], inp.scale,
+                None if sl is None else sl[b:b + 1])
+        if rope_base:
+            oracle.rope.forward(*args, base=rope_base, dtype=np.float32, causal=causal)
+        else:
+            oracle.forward(*args, dtype=np.float32, causal=causal)
+        ffl += 4.0 * w.d * G * valid_pairs(w.S, 1, None if sl is None else sl[b:b + 1], causal)
+        if time.perf_counter() - t1 >= budget_s / 4:
+            break
+    dtf = time.perf_counter() - t1
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "fwd_value": ffl / dtf / 1e12,
             "sample": f"{done} (sequence, kv head) unit evaluations ({done / len(units):.2f} passes over the "
-                      f"{len(units)} units) of {w.name}, fwd+bwd, numpy fp32, {dt:.1f} s"}
+                      f"{len(units)} units) of {w.name}, fwd+bwd, numpy fp32, {dt:.1f} s; fwd_value: the "
+                      f"forward alone on the same units, {dtf:.1f} s"}
 
 
 def time_graph_replays(torch, makers, args):
