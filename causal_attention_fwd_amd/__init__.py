@@ -138,6 +138,7 @@ def _check_gpu(name, t, dtype, shape=None, strided=False):
     if strided:
         if t.dim() != 4 or t.stride(3) != 1:
             raise ValueError(f"{name} must be 4-D with its last dimension contiguous")
+        _reject_expanded(name, t)
     elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
@@ -145,13 +146,31 @@ def _check_gpu(name, t, dtype, shape=None, strided=False):
     return t.data_ptr()
 
 
+def _reject_expanded(name, t):
+    """An expanded view (stride 0 on a dimension of size > 1) lets one row of
+    memory stand for many; the kernels would read or write it as distinct rows
+    (outputs would race), so such views are refused."""
+    if any(t.shape[i] > 1 and t.stride(i) == 0 for i in range(3)):
+        raise ValueError(f"{name} has an expanded (stride-0) dimension; pass a tensor with real strides "
+                         f"(e.g. .contiguous())")
+
+
+def _dense_triple(t):
+    """Element strides of a dense [B, S, H, d] tensor of t's shape."""
+    _, S, H, d = t.shape
+    return (S * H * d, H * d, d)
+
+
 def _strides(group, tensors):
     """The (sequence, position, head) element strides the tensors of one stride
-    group share (the C ABI takes one triple per group); size-1 dimensions
-    count as stride 0."""
+    group share (the C ABI takes one triple per group). The stride of a size-1
+    dimension never moves an address, so it is taken as the dense one: the
+    triple then never reads as the all-zero "dense" marker by accident, and
+    tensors that differ only there still share a triple."""
     got = None
     for name, t in tensors:
-        st = tuple(0 if t.shape[i] == 1 else int(t.stride(i)) for i in range(3))
+        dense = _dense_triple(t)
+        st = tuple(dense[i] if t.shape[i] == 1 else int(t.stride(i)) for i in range(3))
         if got is None:
             got = st
         elif st != got:

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["attn_kernels.hip", "attn_api.cpp"]
+SOURCES = ["attn_kernels.hip", "attn_api.cpp", "attn_plan.cpp"]
 ARCH = "gfx950"
 
 

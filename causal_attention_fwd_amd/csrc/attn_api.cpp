@@ -12,6 +12,10 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Longest sequence (and cache) accepted: positions and block counts are
+// 32-bit ints on the device and in the launch arithmetic, rounded up there.
+constexpr int32_t kMaxLen = 1 << 30;
+
 // A stride triple (sequence, position, head) in elements; all zero means the
 // dense [B, S, H, d] layout. Returns false for a negative stride or one that
 // is not a multiple of 8 elements (rows must stay 16-byte aligned).
@@ -32,6 +36,7 @@ attn_status check_shape(const attn_shape* s, attn::Problem* pr) {
   if (s->heads_q % s->heads_kv != 0) return ATTN_ERR_INVALID_ARG;
   if (!(isfinite(s->scale) && s->scale > 0.f)) return ATTN_ERR_INVALID_ARG;
   if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (s->seqlen > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   if (s->causal != 0 && s->causal != 1) return ATTN_ERR_INVALID_ARG;
   if (!(isfinite(s->rope_base) && s->rope_base >= 0.f)) return ATTN_ERR_INVALID_ARG;
   if (s->seqlens && (reinterpret_cast<uintptr_t>(s->seqlens) & 3u) != 0) return ATTN_ERR_MISALIGNED;
@@ -69,6 +74,7 @@ attn_status check_decode_shape(const attn_decode_shape* s, attn::DecodeProblem* 
   if (s->heads_q % s->heads_kv != 0) return ATTN_ERR_INVALID_ARG;
   if (!(isfinite(s->scale) && s->scale > 0.f)) return ATTN_ERR_INVALID_ARG;
   if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (s->cache_len > kMaxLen || s->q_len > kMaxLen) return ATTN_ERR_UNSUPPORTED;
   if (!(isfinite(s->rope_base) && s->rope_base >= 0.f)) return ATTN_ERR_INVALID_ARG;
   if (s->cache_lens && (reinterpret_cast<uintptr_t>(s->cache_lens) & 3u) != 0) return ATTN_ERR_MISALIGNED;
   // 32-bit tile offsets (as for the training path) and grid size
@@ -220,9 +226,15 @@ attn_status attn_decode(const attn_decode_shape* shape, const void* q, const voi
 const char* attn_status_string(attn_status status) {
   switch (status) {
     case ATTN_OK: return "ATTN_OK";
-    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: null pointer, bad size, Hq % Hkv != 0 or bad scale";
-    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: head_dim must be 64 or 128";
-    case ATTN_ERR_MISALIGNED: return "ATTN_ERR_MISALIGNED: tensor pointers must be 16-byte aligned";
+    case ATTN_ERR_INVALID_ARG:
+      return "ATTN_ERR_INVALID_ARG: null pointer, non-positive size, Hq % Hkv != 0, scale not finite and > 0, "
+             "causal not 0 or 1, or rope_base negative or not finite";
+    case ATTN_ERR_UNSUPPORTED:
+      return "ATTN_ERR_UNSUPPORTED: head_dim must be 64 or 128, lengths at most 2^30, heads * head_dim and "
+             "every position stride at most 2^22 elements, and no launch above 2^31 - 1 blocks";
+    case ATTN_ERR_MISALIGNED:
+      return "ATTN_ERR_MISALIGNED: tensor pointers must be 16-byte aligned (lengths 4-byte) and strides "
+             "non-negative multiples of 8 elements";
     case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing, misaligned or smaller than required";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: the HIP runtime reported a launch error";
   }

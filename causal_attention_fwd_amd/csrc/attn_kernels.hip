@@ -117,46 +117,11 @@ struct BwdArgs {
 
 constexpr int kThreads = 256;  // four waves, one per SIMD
 
-#ifdef ATTN_TRACE
-// Profiling builds only: per-workgroup (hardware id, XCC id, start, end)
-// timestamps of the last launch of each kernel kind, read back by the host.
-__device__ unsigned long long g_trace[4][65536][4];
-#define ATTN_TRACE_BEGIN()                                    \
-  unsigned long long trace_t0 = __builtin_amdgcn_s_memrealtime();
-#define ATTN_TRACE_END(kind)                                                                        \
-  if (threadIdx.x == 0 && blockIdx.x < 65536) {                                                     \
-    g_trace[kind][blockIdx.x][0] = __builtin_amdgcn_s_getreg(0xF804);                             \
-    g_trace[kind][blockIdx.x][1] = __builtin_amdgcn_s_getreg(0xF814);                             \
-    g_trace[kind][blockIdx.x][2] = trace_t0;                                                        \
-    g_trace[kind][blockIdx.x][3] = __builtin_amdgcn_s_memrealtime();                              \
-  }
-extern "C" void* attn_trace_buffer() {
-  void* p = nullptr;
-  if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_trace)) != hipSuccess) return nullptr;
-  return p;
-}
-#else
-#define ATTN_TRACE_BEGIN()
-#define ATTN_TRACE_END(kind)
-#endif
-
-#ifndef ATTN_PRIO_DKDV
-#define ATTN_PRIO_DKDV 1
-#endif
-#ifndef ATTN_PRIO_DQ
-#define ATTN_PRIO_DQ 1
-#endif
-// Wave priority while a wave issues its first run of MFMAs (0: leave the
-// default), so that the pipe is refilled promptly while a sibling wave on the
-// same SIMD runs VALU work.
-template <int PRIO>
-__device__ __forceinline__ void prio_mfma() {
-  if constexpr (PRIO != 0) __builtin_amdgcn_s_setprio(PRIO);
-}
-template <int PRIO>
-__device__ __forceinline__ void prio_base() {
-  if constexpr (PRIO != 0) __builtin_amdgcn_s_setprio(0);
-}
+// Wave priority 1 while a wave issues its first run of MFMAs, so that the pipe
+// is refilled promptly while a sibling wave on the same SIMD runs VALU work;
+// back to 0 afterwards.
+__device__ __forceinline__ void prio_mfma() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void prio_base() { __builtin_amdgcn_s_setprio(0); }
 
 // One stage of a K/V (or Q/dO) tile pipeline: two swizzled LDS tiles, and the
 // stage's index for side data kept in indexed arrays.
@@ -283,7 +248,6 @@ void fwd_kernel(FwdArgs a) {
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
-  ATTN_TRACE_BEGIN();
   int qb, b, h;
   decode_qblock(blockIdx.x, a.nqb, a.B, a.Hq, a.Hkv, qb, b, h);
   const int S = a.S;
@@ -362,7 +326,6 @@ void fwd_kernel(FwdArgs a) {
       if (g == 0) LSEb[i] = valid ? (st.mu[t] * c + __log2f(lt)) * kLn2 : kNegInf;
     }
   }
-  ATTN_TRACE_END(0);
 }
 
 // ----------------------------------------------------------------------------
@@ -436,7 +399,7 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
       dp[m2][t] = nd;
     }
   }
-  prio_mfma<ATTN_PRIO_DKDV>();
+  prio_mfma();
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -450,7 +413,7 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
       }
     }
   }
-  prio_base<ATTN_PRIO_DKDV>();
+  prio_base();
   // P = exp2(S*c - LSE*log2e), dS = P (dP - D); rows m2*32 + rr*8 + g*4 + e of
   // the lane's registers rr*4 + e, read four at a time
 #pragma unroll
@@ -514,7 +477,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
       sO1[GROUPS * TILE];
   __shared__ __attribute__((aligned(16))) float sstat[GROUPS][2][2][BMQ];  // [group][buf][LSE*log2e, -D]
 
-  ATTN_TRACE_BEGIN();
   const int grp = wave_id() >> 2;
   const int gtid = threadIdx.x & (kThreads - 1);
   const int lane = threadIdx.x & 63;
@@ -673,7 +635,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
     }
   }
-  ATTN_TRACE_END(2);
 }
 
 // ----------------------------------------------------------------------------
@@ -707,7 +668,7 @@ __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, cons
       s[mt][t] = zero16();
       dp[mt][t] = mfma32(st.ones, st.nd[t], zero16());  // every row: -D of the lane's query
     }
-  prio_mfma<ATTN_PRIO_DQ>();
+  prio_mfma();
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -721,7 +682,7 @@ __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, cons
       }
     }
   }
-  prio_base<ATTN_PRIO_DQ>();
+  prio_base();
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -762,7 +723,6 @@ void bwd_dq_kernel(BwdArgs a) {
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
-  ATTN_TRACE_BEGIN();
   int qb, b, h;
   decode_qblock(blockIdx.x, a.nblk, a.B, a.Hq, a.Hkv, qb, b, h);
   const int S = a.S;
@@ -881,7 +841,6 @@ void bwd_dq_kernel(BwdArgs a) {
         }
     }
   }
-  ATTN_TRACE_END(3);
 }
 
 // ----------------------------------------------------------------------------
@@ -1243,61 +1202,16 @@ namespace {
 // SIMD (OCC: the register budget per wave is 512 / OCC) and waves per
 // workgroup of the forward and dQ passes (W: the waves of a workgroup share
 // each K/V tile loaded into LDS).
-#ifndef ATTN_FWD_NT64
-#define ATTN_FWD_NT64 2
-#endif
-#ifndef ATTN_FWD_OCC64
-#define ATTN_FWD_OCC64 2
-#endif
-#ifndef ATTN_DQ_NT64
-#define ATTN_DQ_NT64 1
-#endif
-#ifndef ATTN_DQ_OCC64
-#define ATTN_DQ_OCC64 3
-#endif
-#ifndef ATTN_DKDV_OCC64
-#define ATTN_DKDV_OCC64 2
-#endif
-#ifndef ATTN_DKDV_GROUPS64
-#define ATTN_DKDV_GROUPS64 2
-#endif
-#ifndef ATTN_FWD_W64
-#define ATTN_FWD_W64 4
-#endif
-#ifndef ATTN_FWD_W128
-#define ATTN_FWD_W128 8
-#endif
-#ifndef ATTN_DQ_W64
-#define ATTN_DQ_W64 4
-#endif
-#ifndef ATTN_DQ_W128
-#define ATTN_DQ_W128 4
-#endif
-#ifndef ATTN_FWD_NT128
-#define ATTN_FWD_NT128 1
-#endif
-#ifndef ATTN_FWD_OCC128
-#define ATTN_FWD_OCC128 2
-#endif
-#ifndef ATTN_DQ_NT128
-#define ATTN_DQ_NT128 1
-#endif
-#ifndef ATTN_DQ_OCC128
-#define ATTN_DQ_OCC128 2
-#endif
-#ifndef ATTN_DKDV_OCC128
-#define ATTN_DKDV_OCC128 1
-#endif
 template <int D> struct Tiles;
 template <> struct Tiles<64> {
-  static constexpr int FWD_NT = ATTN_FWD_NT64, FWD_OCC = ATTN_FWD_OCC64, FWD_W = ATTN_FWD_W64;
-  static constexpr int DQ_NT = ATTN_DQ_NT64, DQ_OCC = ATTN_DQ_OCC64, DQ_W = ATTN_DQ_W64;
-  static constexpr int DKDV_NTJ = 1, DKDV_OCC = ATTN_DKDV_OCC64, DKDV_GROUPS = ATTN_DKDV_GROUPS64;
+  static constexpr int FWD_NT = 2, FWD_OCC = 2, FWD_W = 4;
+  static constexpr int DQ_NT = 1, DQ_OCC = 3, DQ_W = 4;
+  static constexpr int DKDV_NTJ = 1, DKDV_OCC = 2, DKDV_GROUPS = 2;
 };
 template <> struct Tiles<128> {
-  static constexpr int FWD_NT = ATTN_FWD_NT128, FWD_OCC = ATTN_FWD_OCC128, FWD_W = ATTN_FWD_W128;
-  static constexpr int DQ_NT = ATTN_DQ_NT128, DQ_OCC = ATTN_DQ_OCC128, DQ_W = ATTN_DQ_W128;
-  static constexpr int DKDV_NTJ = 1, DKDV_OCC = ATTN_DKDV_OCC128, DKDV_GROUPS = 1;
+  static constexpr int FWD_NT = 1, FWD_OCC = 2, FWD_W = 8;
+  static constexpr int DQ_NT = 1, DQ_OCC = 2, DQ_W = 4;
+  static constexpr int DKDV_NTJ = 1, DKDV_OCC = 1, DKDV_GROUPS = 1;
 };
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -1405,51 +1319,6 @@ hipError_t launch_bwd_dq_with_delta(const Problem& pr, const void* q, const void
                     : dq_d<128>(pr, q, k, v, d_o, lse, nullptr, dq, o, delta, stream);
 }
 
-int64_t max_grid(const Problem& pr) {
-  // smallest blocks: 128 query rows (forward/dQ), 128 key rows (dK/dV), 16 rows (preprocess)
-  const int64_t nb = (pr.S + 127) / 128;
-  int64_t m = nb * pr.B * pr.Hq;
-  const int64_t pre = ((int64_t)pr.B * pr.S * pr.Hq + 15) / 16;
-  // RoPE pre-pass: one workgroup per (sequence, position)
-  const int64_t rope = (int64_t)pr.B * pr.S;
-  m = m > pre ? m : pre;
-  return m > rope ? m : rope;
-}
-
-#ifndef ATTN_DEC_STAGES
-#define ATTN_DEC_STAGES 2
-#endif
-#ifndef ATTN_DEC_ROUNDS
-#define ATTN_DEC_ROUNDS 1
-#endif
-
-// Workspace layout: [hdr: 256 B][uinfo: int2 per unit][partial LSE][partial O],
-// each part 256-byte aligned.
-namespace {
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-}  // namespace
-
-DecodePlan plan_decode(const DecodeProblem& pr) {
-  // one wave per decode workgroup; as many waves as fit on the 256 CUs at
-  // once (LDS decides: two 64-key K and V tiles per stage), times ATTN_DEC_ROUNDS,
-  // but no more than there can be tiles
-  constexpr int kCUs = 256;
-  const int per_cu = (pr.d == 64 ? 8 : 4) / ATTN_DEC_STAGES;
-  const int64_t rows = (int64_t)(pr.Hq / pr.Hkv) * pr.Sq;  // query rows per kv head
-  DecodePlan plan;
-  plan.rb = (int)((rows + 31) / 32);
-  plan.ru = plan.rb == 1 ? (int)rows : 32;
-  const int64_t units = (int64_t)pr.B * pr.Hkv * plan.rb;
-  const int64_t tmax = units * ((pr.Smax + 63) / 64);
-  plan.waves = (int)std::min<int64_t>((int64_t)kCUs * per_cu * ATTN_DEC_ROUNDS, tmax);
-  const int64_t slots = plan.waves + units - 1;
-  const int64_t R = plan.ru;
-  plan.off_uinfo = 256;
-  plan.off_lse = plan.off_uinfo + align256((size_t)units * 8);
-  plan.off_o = plan.off_lse + align256((size_t)(slots * R) * sizeof(float));
-  plan.workspace_bytes = plan.off_o + (size_t)(slots * R) * pr.d * sizeof(float);
-  return plan;
-}
 
 hipError_t launch_decode(const DecodeProblem& pr, const DecodePlan& plan, const void* q, const void* k_cache,
                          const void* v_cache, void* o, float* lse, void* workspace, hipStream_t stream) {
@@ -1462,10 +1331,10 @@ hipError_t launch_decode(const DecodeProblem& pr, const DecodePlan& plan, const 
   const int64_t merge_blocks = ((int64_t)pr.B * pr.Hq * pr.Sq + 3) / 4;
   hipError_t e;
   if (pr.d == 64) {
-    e = launch((const void*)&decode_split_kernel<64, 2, ATTN_DEC_STAGES>, plan.waves, a, stream, 64);
+    e = launch((const void*)&decode_split_kernel<64, 2, kDecodeStages>, plan.waves, a, stream, 64);
     if (e == hipSuccess) e = launch((const void*)&decode_merge_kernel<64>, merge_blocks, a, stream);
   } else {
-    e = launch((const void*)&decode_split_kernel<128, 1, ATTN_DEC_STAGES>, plan.waves, a, stream, 64);
+    e = launch((const void*)&decode_split_kernel<128, 1, kDecodeStages>, plan.waves, a, stream, 64);
     if (e == hipSuccess) e = launch((const void*)&decode_merge_kernel<128>, merge_blocks, a, stream);
   }
   return e;

@@ -49,6 +49,9 @@ struct DecodeProblem {
   Strides sq, skv, so;        // q [B,Sq,Hq,d]; k and v caches [B,Smax,Hkv,d]; o [B,Sq,Hq,d]
 };
 
+// LDS pipeline stages of the decode split kernel (K and V tiles per stage).
+constexpr int kDecodeStages = 2;
+
 // How the decode work is dealt out: `waves` one-wave workgroups share the
 // valid 64-key tiles of all (sequence, kv head) units evenly; each writes one
 // partial (O, LSE) per unit it touches, and a merge pass combines them by

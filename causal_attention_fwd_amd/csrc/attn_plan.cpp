@@ -1,0 +1,53 @@
+// Host-side planning shared by the C ABI and the launchers: the largest grid a
+// problem launches (checked against the hardware limit before any launch) and
+// the decode work split with its workspace layout. Plain C++ (no device code),
+// so a host-only build (the sanitizer test) links the same planning logic.
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "attn_launch.h"
+
+namespace attn {
+
+int64_t max_grid(const Problem& pr) {
+  // smallest blocks: 64 query rows (forward/dQ), 64 key rows (dK/dV), 16 rows (preprocess)
+  const int64_t nb = ((int64_t)pr.S + 63) / 64;
+  int64_t m = nb * pr.B * pr.Hq;
+  const int64_t pre = ((int64_t)pr.B * pr.S * pr.Hq + 15) / 16;
+  // RoPE pre-pass: one workgroup per (sequence, position)
+  const int64_t rope = (int64_t)pr.B * pr.S;
+  m = m > pre ? m : pre;
+  return m > rope ? m : rope;
+}
+
+namespace {
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+// Workspace layout: [hdr: 256 B][uinfo: int2 per unit][partial LSE][partial O],
+// each part 256-byte aligned.
+DecodePlan plan_decode(const DecodeProblem& pr) {
+  // one wave per decode workgroup; as many waves as fit on the 256 CUs at
+  // once (LDS decides: kDecodeStages stages of a 64-key K and V tile), but no
+  // more than there are tiles
+  constexpr int kCUs = 256;
+  const int per_cu = (pr.d == 64 ? 8 : 4) / kDecodeStages;
+  const int64_t rows = (int64_t)(pr.Hq / pr.Hkv) * pr.Sq;  // query rows per kv head
+  DecodePlan plan;
+  plan.rb = (int)((rows + 31) / 32);
+  plan.ru = plan.rb == 1 ? (int)rows : 32;
+  const int64_t units = (int64_t)pr.B * pr.Hkv * plan.rb;
+  const int64_t tmax = units * (((int64_t)pr.Smax + 63) / 64);
+  plan.waves = (int)std::min<int64_t>((int64_t)kCUs * per_cu, tmax);
+  const int64_t slots = plan.waves + units - 1;
+  const int64_t R = plan.ru;
+  plan.off_uinfo = 256;
+  plan.off_lse = plan.off_uinfo + align256((size_t)units * 8);
+  plan.off_o = plan.off_lse + align256((size_t)(slots * R) * sizeof(float));
+  plan.workspace_bytes = plan.off_o + (size_t)(slots * R) * pr.d * sizeof(float);
+  return plan;
+}
+
+}  // namespace attn

@@ -60,9 +60,11 @@ typedef enum attn_status {
   ATTN_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, Hq % Hkv != 0,
                                 non-finite or non-positive scale, causal not 0/1,
                                 negative or non-finite rope_base */
-  ATTN_ERR_UNSUPPORTED = 2,  /* head_dim not in {64, 128},
-                                heads_q * head_dim > 2^22 (tile offsets are
-                                32-bit), or a grid beyond 2^31 - 1 blocks */
+  ATTN_ERR_UNSUPPORTED = 2,  /* head_dim not in {64, 128}; a sequence or cache
+                                length above 2^30; heads_q * head_dim
+                                (decode: heads_kv * head_dim) above 2^22, or a
+                                position stride above 2^22 (tile offsets are
+                                32-bit); or a launch beyond 2^31 - 1 blocks */
   ATTN_ERR_MISALIGNED = 3,   /* a pointer is not 16-byte aligned, or a stride is
                                 negative or not a multiple of 8 elements */
   ATTN_ERR_WORKSPACE = 4,    /* workspace smaller than attn_bwd_workspace_bytes() */
@@ -71,7 +73,7 @@ typedef enum attn_status {
 
 typedef struct attn_shape {
   int32_t batch;       /* B >= 1 */
-  int32_t seqlen;      /* S >= 1 (query and key lengths are equal) */
+  int32_t seqlen;      /* 1 <= S <= 2^30 (query and key lengths are equal) */
   int32_t heads_q;     /* Hq >= 1, a multiple of heads_kv */
   int32_t heads_kv;    /* Hkv >= 1 */
   int32_t head_dim;    /* d: 64 or 128 */
@@ -121,31 +123,39 @@ attn_status attn_rope(const attn_shape* shape, const void* q, const void* k, voi
                       hipStream_t stream);
 
 /*
- * Forward: O = softmax(scale * Q K^T + causal/padding mask) V, and the fp32
- * natural-log row normaliser LSE. Q [B,S,Hq,d], K/V [B,S,Hkv,d], O [B,S,Hq,d]
- * bf16; LSE [B,Hq,S] fp32. Deterministic (bitwise repeatable).
+ * Forward ("Axis", Zyora Labs page, feature list: the fused flash-attention
+ * forward whose probabilities never reach memory, bf16 storage, fp32
+ * accumulation): O = softmax(scale * Q K^T + causal/padding mask) V, and the
+ * fp32 natural-log row normaliser LSE that the backward recomputes P from.
+ * Q [B,S,Hq,d], K/V [B,S,Hkv,d], O [B,S,Hq,d] bf16; LSE [B,Hq,S] fp32.
+ * Deterministic (bitwise repeatable).
  */
 attn_status attn_fwd(const attn_shape* shape, const void* q, const void* k, const void* v,
                      void* o, float* lse, hipStream_t stream);
 
 /*
- * Backward preprocess: D[b,h,i] = sum_c dO[b,i,h,c] * O[b,i,h,c] accumulated in
- * fp32 from the bf16 inputs (0 on padded rows). O, dO [B,S,Hq,d] bf16; D
- * [B,Hq,S] fp32.
+ * Backward preprocess (the row term D of the softmax gradient used by the
+ * fused backward of the "Axis" Zyora Labs page, feature list; the pages give
+ * no formula, D is the standard one for the exact gradient of softmax
+ * attention): D[b,h,i] = sum_c dO[b,i,h,c] * O[b,i,h,c] accumulated in fp32
+ * from the bf16 inputs (0 on padded rows). O, dO [B,S,Hq,d] bf16; D [B,Hq,S]
+ * fp32.
  */
 attn_status attn_bwd_preprocess(const attn_shape* shape, const void* o, const void* d_o,
                                 float* delta, hipStream_t stream);
 
 /*
  * Bytes of device workspace attn_bwd needs for `shape`: O(B*S*H*d) at most,
- * never O(S^2). The current algorithm computes dQ in a separate pass and needs
+ * never O(S^2) (the "Axis" Zyora Labs page, feature list: memory stays flat as
+ * the sequence grows). The current algorithm computes dQ in a separate pass and needs
  * none (returns 0). Returns 0 for a NULL shape.
  */
 size_t attn_bwd_workspace_bytes(const attn_shape* shape);
 
 /*
- * Backward: dQ, dK, dV from Q, K, V, dO, the forward's LSE and the
- * preprocess's D. The probabilities are recomputed from LSE tile by tile.
+ * Backward ("Axis", Zyora Labs page, feature list: the fused flash-attention
+ * backward; grouped kv heads per the "AxiomLM" PyPI page, "Key Features"):
+ * dQ, dK, dV from Q, K, V, dO, the forward's LSE and the preprocess's D. The probabilities are recomputed from LSE tile by tile.
  * dQ [B,S,Hq,d], dK/dV [B,S,Hkv,d] bf16 (dK/dV summed over each kv head's
  * query-head group). `workspace` may be NULL when attn_bwd_workspace_bytes()
  * is 0; otherwise it must be 16-byte aligned and hold at least that many
@@ -157,7 +167,8 @@ attn_status attn_bwd(const attn_shape* shape, const void* q, const void* k, cons
                      hipStream_t stream);
 
 /*
- * The two passes attn_bwd runs, exported separately. They read the same inputs,
+ * The two passes attn_bwd runs, exported separately (same operation and
+ * citation as attn_bwd). They read the same inputs,
  * write disjoint outputs and do not depend on each other, so a caller may run
  * them in either order or concurrently on two streams; attn_bwd enqueues
  * attn_bwd_dkdv then attn_bwd_dq on one stream.
@@ -174,7 +185,8 @@ attn_status attn_bwd_dq(const attn_shape* shape, const void* q, const void* k, c
                         void* dq, hipStream_t stream);
 
 /*
- * Backward with the preprocess folded in: the dQ pass computes D = rowsum(dO * O)
+ * Backward with the preprocess folded in (same operation and citation as
+ * attn_bwd_preprocess followed by attn_bwd): the dQ pass computes D = rowsum(dO * O)
  * from the O and dO rows it loads (fp32 from the bf16 inputs, 0 on padded
  * rows), writes it to `delta` [B,Hq,S] fp32 (an output here) and uses it; the
  * dK/dV pass then reads it. Same results as attn_bwd_preprocess followed by
@@ -203,9 +215,9 @@ attn_status attn_bwd_fused(const attn_shape* shape, const void* q, const void* k
  */
 typedef struct attn_decode_shape {
   int32_t batch;       /* B >= 1 */
-  int32_t q_len;       /* Sq >= 1 new queries per sequence (the Sq * Hq / Hkv
+  int32_t q_len;       /* 1 <= Sq <= 2^30 new queries per sequence (the Sq * Hq / Hkv
                           query rows of a kv head run in blocks of 32) */
-  int32_t cache_len;   /* Smax >= 1: cache capacity (positions) per sequence */
+  int32_t cache_len;   /* 1 <= Smax <= 2^30: cache capacity (positions) per sequence */
   int32_t heads_q;     /* Hq >= 1, a multiple of heads_kv */
   int32_t heads_kv;    /* Hkv >= 1 */
   int32_t head_dim;    /* d: 64 or 128 */
@@ -252,7 +264,9 @@ size_t attn_decode_workspace_bytes(const attn_decode_shape* shape);
 attn_status attn_decode(const attn_decode_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                         void* o, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Static, human-readable name of a status code (never NULL). */
+/* Static, human-readable name of a status code and the conditions that return
+   it (never NULL). Not an operation of the pages: the error convention of this
+   library (validation on the host before any launch). */
 const char* attn_status_string(attn_status status);
 
 #ifdef __cplusplus

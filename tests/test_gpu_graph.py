@@ -1,17 +1,31 @@
 """GPU: the whole step captured in one HIP graph (torch.cuda.CUDAGraph).
 
 The graph is replayed several times, with the program's own eager work, new
-inputs copied in place and synchronisations between replays, and every replay
-is compared bit for bit with an eager run of the same entry points on the same
-inputs (the kernels are deterministic).
+inputs copied in place and synchronisations between replays. Every replay is
+checked twice: against the oracle (oracle.backward, oracle.rope.backward or
+oracle.decode in fp64) on that replay's own inputs, to the parity bar of
+tests/parity.py, and bit for bit against an eager run of the same entry
+points on the same inputs (the kernels are deterministic).
 """
 import numpy as np
 import pytest
 import torch
 
 import causal_attention_fwd_amd as attn
+import oracle
 from attn_workloads import make_inputs
-from parity import say
+from oracle import rope as oracle_rope
+from parity import compare, say
+
+
+def _oracle_step(inp, causal, rope_base):
+    """The oracle's forward and backward on one replay's inputs (host fp64)."""
+    q, k, v, do = (getattr(inp, n).float().numpy() for n in ("q", "k", "v", "do"))
+    sl = inp.seqlens.numpy() if inp.seqlens is not None else None
+    if rope_base:
+        # the rotated q and k are bf16 tensors in the pipeline
+        return oracle_rope.backward(q, k, v, do, inp.scale, sl, rope_base, causal=causal, bf16_storage=True)
+    return oracle.backward(q, k, v, do, inp.scale, sl, causal=causal)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +77,8 @@ def test_graph_replays_match_eager(causal, padded, fused, rope_base):
         graph.replay()
         torch.cuda.synchronize()
         got = {key: val.clone() for key, val in outs.items()}
+        host = {key: val.float().cpu().numpy() for key, val in got.items()}
+        compare(host, _oracle_step(inp, causal, rope_base), f"replay {rep} vs oracle")
         # eager work between replays, on separate tensors
         t = {n: getattr(inp, n).to(dev).contiguous() for n in ("q", "k", "v", "do")}
         ref = _eager(t, scale, inp.seqlens.to(dev) if padded else None, causal, fused, rope_base)
@@ -71,6 +87,23 @@ def test_graph_replays_match_eager(causal, padded, fused, rope_base):
             np.testing.assert_array_equal(got[key].view(bits).cpu().numpy(), ref[key].view(bits).cpu().numpy(),
                                           err_msg=f"replay {rep} {key}")
         say(f"  replay {rep}: all six outputs bitwise equal to eager")
+
+
+def _check_decode_oracle(o, lse, inp, rope_base, label):
+    from parity import TOL_LSE, TOL_MAX_ABS, TOL_REL_FRO, metrics
+    lens = inp.cache_lens.numpy() if inp.cache_lens is not None else None
+    args = (inp.q.float().numpy(), inp.k_cache.float().numpy(), inp.v_cache.float().numpy(), inp.scale, lens)
+    ro, rl = (oracle_rope.decode(*args, base=rope_base, bf16_storage=True) if rope_base else oracle.decode(*args))
+    go, gl = o.float().cpu().numpy(), lse.float().cpu().numpy()
+    assert np.all(np.isfinite(go)), f"{label}: non-finite O"
+    rel, mx = metrics(go, ro)
+    assert rel <= TOL_REL_FRO and mx <= TOL_MAX_ABS, f"{label} O: rel_fro={rel:.3e} max_abs={mx:.3e}"
+    rl = np.asarray(rl, dtype=np.float64)
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl)), f"{label}: LSE -inf pattern differs"
+    fin = np.isfinite(rl)
+    lmx = float(np.max(np.abs(gl[fin] - rl[fin]))) if np.any(fin) else 0.0
+    assert lmx <= TOL_LSE, f"{label} LSE: max_abs={lmx:.3e}"
+    say(f"  {label}: O rel={rel:.2e} max={mx:.2e} LSE max={lmx:.2e}")
 
 
 @pytest.mark.parametrize("rope_base", [0.0, 10000.0])
@@ -97,6 +130,7 @@ def test_decode_graph_replays_match_eager(rope_base):
         graph.replay()
         torch.cuda.synchronize()
         got_o, got_l = o.clone(), lse.clone()
+        _check_decode_oracle(got_o, got_l, inp, rope_base, f"decode replay {rep} vs oracle")
         ro, rl = attn.decode(inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev), scale,
                              inp.cache_lens.to(dev), rope_base)
         torch.cuda.synchronize()
