@@ -16,6 +16,7 @@ Entry points (same names as the C ABI):
     attn_bwd_fused(q, k, v, o, d_o, lse, delta, dq, dk, dv, scale, seqlens=None, workspace=None)
     attn_decode_workspace_bytes(B, Sq, Smax, Hq, Hkv, d)
     attn_decode(q, k_cache, v_cache, o, lse, scale, cache_lens=None, workspace=None)
+    attn_decode_noalloc(q, k_cache, v_cache, o, lse, scale, cache_lens=None)
     attn_status_string(code)
 and allocating conveniences `rope(...)`, `forward(...)`, `backward(...)`, `decode(...)`.
 """
@@ -27,7 +28,7 @@ import os
 from typing import Optional
 
 __all__ = ["attn_rope", "rope", "attn_bwd_fused", "capture_decode", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
-           "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode_workspace_bytes", "attn_decode", "attn_status_string",
+           "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_noalloc", "attn_status_string",
            "forward", "backward", "decode", "capture_step", "AttnError", "library_path", "load_library",
            "STATUS"]
 
@@ -39,7 +40,8 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3:
 
 # The symbols include/attn.h declares.
 EXPORTED = ("attn_rope", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_dkdv",
-            "attn_bwd_dq", "attn_bwd_fused", "attn_decode_workspace_bytes", "attn_decode", "attn_status_string")
+            "attn_bwd_dq", "attn_bwd_fused", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_noalloc",
+            "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -97,6 +99,8 @@ def load_library():
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode.argtypes = [dshp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_decode.restype = i32
+    lib.attn_decode_noalloc.argtypes = [dshp, vp, vp, vp, vp, vp, vp]
+    lib.attn_decode_noalloc.restype = i32
     lib.attn_bwd_fused.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_bwd_fused.restype = i32
     lib.attn_rope.argtypes = [shp, vp, vp, vp, vp, vp]
@@ -355,10 +359,7 @@ def attn_decode_workspace_bytes(B: int, Sq: int, Smax: int, Hq: int, Hkv: int, d
     return int(load_library().attn_decode_workspace_bytes(ctypes.byref(shape)))
 
 
-def attn_decode(q, k_cache, v_cache, o, lse, scale: float, cache_lens=None, workspace=None, rope_base: float = 0.0):
-    """O, LSE <- decode attention of q [B,Sq,Hq,d] against the caches [B,Smax,Hkv,d]
-    (with rope_base > 0 the queries are rotated at their positions; the cache
-    holds rotated keys)."""
+def _decode_args(q, k_cache, v_cache, o, lse, scale, cache_lens, rope_base):
     torch = _torch()
     if q.dim() != 4 or k_cache.dim() != 4:
         raise ValueError("q must be [B,Sq,Hq,d] and the caches [B,Smax,Hkv,d]")
@@ -373,6 +374,24 @@ def attn_decode(q, k_cache, v_cache, o, lse, scale: float, cache_lens=None, work
             _check_gpu("v_cache", v_cache, torch.bfloat16, (B, Smax, Hkv, d), True),
             _check_gpu("o", o, torch.bfloat16, (B, Sq, Hq, d), True),
             _check_gpu("lse", lse, torch.float32, (B, Hq, Sq))]
+    return shape, ptrs
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, o, lse, scale: float, cache_lens=None, rope_base: float = 0.0):
+    """attn_decode without a workspace: the library's static per-GPU scratch
+    (ATTN_DECODE_SCRATCH_BYTES) holds the partials; nothing is allocated.
+    Calls that overlap on one GPU race (the scratch is shared)."""
+    shape, ptrs = _decode_args(q, k_cache, v_cache, o, lse, scale, cache_lens, rope_base)
+    _call(load_library().attn_decode_noalloc, "attn_decode_noalloc", ctypes.byref(shape),
+          *[ctypes.c_void_p(p) for p in ptrs], _stream())
+
+
+def attn_decode(q, k_cache, v_cache, o, lse, scale: float, cache_lens=None, workspace=None, rope_base: float = 0.0):
+    """O, LSE <- decode attention of q [B,Sq,Hq,d] against the caches [B,Smax,Hkv,d]
+    (with rope_base > 0 the queries are rotated at their positions; the cache
+    holds rotated keys)."""
+    torch = _torch()
+    shape, ptrs = _decode_args(q, k_cache, v_cache, o, lse, scale, cache_lens, rope_base)
     ws, nbytes = None, 0
     if workspace is not None:
         ws = _check_gpu("workspace", workspace, torch.uint8)

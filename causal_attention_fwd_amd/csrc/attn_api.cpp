@@ -223,6 +223,21 @@ attn_status attn_decode(const attn_decode_shape* shape, const void* q, const voi
   return from_hip(attn::launch_decode(pr, plan, q, k_cache, v_cache, o, lse, workspace, stream));
 }
 
+attn_status attn_decode_noalloc(const attn_decode_shape* shape, const void* q, const void* k_cache,
+                                const void* v_cache, void* o, float* lse, hipStream_t stream) {
+  attn::DecodeProblem pr;
+  attn_status st = check_decode_shape(shape, &pr);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k_cache, v_cache, o, lse});
+  if (st != ATTN_OK) return st;
+  const attn::DecodePlan plan = attn::plan_decode(pr);
+  if (plan.workspace_bytes > attn::kDecodeScratchBytes) return ATTN_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  st = from_hip(attn::decode_scratch(&scratch));
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_decode(pr, plan, q, k_cache, v_cache, o, lse, scratch, stream));
+}
+
 const char* attn_status_string(attn_status status) {
   switch (status) {
     case ATTN_OK: return "ATTN_OK";
@@ -235,7 +250,9 @@ const char* attn_status_string(attn_status status) {
     case ATTN_ERR_MISALIGNED:
       return "ATTN_ERR_MISALIGNED: tensor pointers must be 16-byte aligned (lengths 4-byte) and strides "
              "non-negative multiples of 8 elements";
-    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing, misaligned or smaller than required";
+    case ATTN_ERR_WORKSPACE:
+      return "ATTN_ERR_WORKSPACE: workspace missing, misaligned or smaller than required (attn_decode_noalloc: "
+             "the problem needs more than its 32 MiB static scratch)";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: the HIP runtime reported a launch error";
   }
   return "ATTN_ERR_UNKNOWN";

@@ -30,6 +30,7 @@
 //    LSE is exported as a natural log.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "attn_common.h"
 #include "attn_launch.h"
@@ -1319,6 +1320,35 @@ hipError_t launch_bwd_dq_with_delta(const Problem& pr, const void* q, const void
                     : dq_d<128>(pr, q, k, v, d_o, lse, nullptr, dq, o, delta, stream);
 }
 
+
+// Scratch of the allocation-free decode entry point: one copy per GPU, alive
+// until the process ends. Host code never passes `scratch` itself to a kernel
+// (on the host it names a stand-in, not device memory): it uses the address
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeProblem& pr, const DecodePlan& plan, const void* q, const void* k_cache,
                          const void* v_cache, void* o, float* lse, void* workspace, hipStream_t stream) {

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace attn {
@@ -65,5 +66,12 @@ struct DecodePlan {
 DecodePlan plan_decode(const DecodeProblem& pr);
 hipError_t launch_decode(const DecodeProblem& pr, const DecodePlan& plan, const void* q, const void* k_cache,
                          const void* v_cache, void* o, float* lse, void* workspace, hipStream_t stream);
+
+// The allocation-free decode entry point keeps its workspace in a static
+// device array of this many bytes, one per GPU.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+// Device address of the current GPU's scratch array (looked up once per
+// device with hipGetSymbolAddress, then cached).
+hipError_t decode_scratch(void** out);
 
 }  // namespace attn

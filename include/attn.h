@@ -264,6 +264,24 @@ size_t attn_decode_workspace_bytes(const attn_decode_shape* shape);
 attn_status attn_decode(const attn_decode_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                         void* o, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * attn_decode without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid hipMalloc. Same operation,
+ * layouts, validation and results as attn_decode (bit for bit: the same
+ * kernels and work split); the partial results live in a static device array
+ * of ATTN_DECODE_SCRATCH_BYTES (32 MiB) that the library holds on each GPU it
+ * runs on until the process ends (its address is looked up on the first call
+ * on each device). A problem whose attn_decode_workspace_bytes() exceeds that
+ * returns ATTN_ERR_WORKSPACE and enqueues nothing. Every call on one GPU uses
+ * the same array: calls that may overlap on one GPU (several streams, several
+ * host threads without ordering) race and must be serialised by the caller.
+ * Nothing in the array has to start at zero; each call writes what it reads.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+attn_status attn_decode_noalloc(const attn_decode_shape* shape, const void* q, const void* k_cache,
+                                const void* v_cache, void* o, float* lse, hipStream_t stream);
+
 /* Static, human-readable name of a status code and the conditions that return
    it (never NULL). Not an operation of the pages: the error convention of this
    library (validation on the host before any launch). */

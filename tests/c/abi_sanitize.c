@@ -177,6 +177,16 @@ int main(void) {
     expect("decode misaligned lens", attn_decode(&e, P(1), P(2), P(3), P(4), (float*)P(5), P(14), ws, 0),
            ATTN_ERR_MISALIGNED, n, 0);
     if (attn_decode_workspace_bytes(NULL) != 0) { printf("FAIL decode null shape\n"); ++failures; }
+    /* the allocation-free variant: same validation, scratch limit instead of a workspace */
+    n = g_stub_launches;
+    expect("decode noalloc", attn_decode_noalloc(&d, P(1), P(2), P(3), P(4), (float*)P(5), 0), ATTN_OK, n, 1);
+    e = d; e.batch = 64; e.q_len = 64; e.cache_len = 64; e.heads_q = 64; e.heads_kv = 64;
+    n = g_stub_launches;
+    expect("decode noalloc beyond scratch", attn_decode_noalloc(&e, P(1), P(2), P(3), P(4), (float*)P(5), 0),
+           ATTN_ERR_WORKSPACE, n, 0);
+    n = g_stub_launches;
+    expect("decode noalloc null o", attn_decode_noalloc(&d, P(1), P(2), P(3), NULL, (float*)P(5), 0),
+           ATTN_ERR_INVALID_ARG, n, 0);
   }
 
   /* status strings: every code has a non-empty static string */
