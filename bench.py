@@ -360,6 +360,7 @@ def run(args):
     if args.rope:
         # the rotated copies the forward and backward read (kept like saved activations)
         qa, ka = torch.empty_like(q), torch.empty_like(k)
+    ws = attn.bwd_workspace(q, k)  # the backward's workspace (None when the shape needs none)
 
     def step(ev=None):
         if ev is not None:
@@ -375,7 +376,7 @@ def run(args):
             # preprocess folded into dQ, which runs first; events 2 and 3 bracket dQ + D
             if ev is not None:
                 ev[2].record()
-            attn.attn_bwd_fused(qa, ka, v, o, do, lse, delta, dq, dk, dv, scale, sl, None, cz, rb)
+            attn.attn_bwd_fused(qa, ka, v, o, do, lse, delta, dq, dk, dv, scale, sl, ws, cz, rb)
             if ev is not None:
                 ev[3].record()
                 ev[4].record()
@@ -383,7 +384,7 @@ def run(args):
             attn.attn_bwd_preprocess(o, do, delta, sl)
             if ev is not None:
                 ev[2].record()
-            attn.attn_bwd_dkdv(qa, ka, v, do, lse, delta, dk, dv, scale, sl, cz, rb)
+            attn.attn_bwd_dkdv(qa, ka, v, do, lse, delta, dk, dv, scale, sl, cz, rb, ws)
             if ev is not None:
                 ev[3].record()
             attn.attn_bwd_dq(qa, ka, v, do, lse, delta, dq, scale, sl, cz, rb)
@@ -420,7 +421,7 @@ def run(args):
         # default: no host-side launch cost in the timed step); the per-kernel
         # times above stay those of the eager launches
         def capture():
-            return attn.capture_step(q, k, v, do, o, lse, delta, dq, dk, dv, scale, sl, causal, None,
+            return attn.capture_step(q, k, v, do, o, lse, delta, dq, dk, dv, scale, sl, causal, ws,
                                      fused=args.fused_bwd, rope_base=rb, q_rot=qa if args.rope else None,
                                      k_rot=ka if args.rope else None)
         g_step = time_graph_replays(torch, [capture], args)

@@ -11,7 +11,7 @@ Entry points (same names as the C ABI):
     attn_bwd_preprocess(o, d_o, delta, seqlens=None)
     attn_bwd_workspace_bytes(B, S, Hq, Hkv, d)
     attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale, seqlens=None, workspace=None)
-    attn_bwd_dkdv(q, k, v, d_o, lse, delta, dk, dv, scale, seqlens=None)
+    attn_bwd_dkdv(q, k, v, d_o, lse, delta, dk, dv, scale, seqlens=None, workspace=None)
     attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale, seqlens=None)
     attn_bwd_fused(q, k, v, o, d_o, lse, delta, dq, dk, dv, scale, seqlens=None, workspace=None)
     attn_decode_workspace_bytes(B, Sq, Smax, Hq, Hkv, d)
@@ -28,7 +28,7 @@ import os
 from typing import Optional
 
 __all__ = ["attn_rope", "rope", "attn_bwd_fused", "capture_decode", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
-           "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_noalloc", "attn_status_string",
+           "attn_bwd_dkdv", "attn_bwd_dq", "bwd_workspace", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_noalloc", "attn_status_string",
            "forward", "backward", "decode", "capture_step", "AttnError", "library_path", "load_library",
            "STATUS"]
 
@@ -90,7 +90,7 @@ def load_library():
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_bwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_bwd.restype = i32
-    lib.attn_bwd_dkdv.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_bwd_dkdv.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_bwd_dkdv.restype = i32
     lib.attn_bwd_dq.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.attn_bwd_dq.restype = i32
@@ -271,10 +271,7 @@ def attn_bwd(q, k, v, d_o, lse, delta, dq, dk, dv, scale: float, seqlens=None, w
             _check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d), True),
             _check_gpu("dk", dk, torch.bfloat16, (B, S, Hkv, d), True),
             _check_gpu("dv", dv, torch.bfloat16, (B, S, Hkv, d), True)]
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        ws_ptr = _check_gpu("workspace", workspace, workspace.dtype)
-        ws_bytes = workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace_arg(workspace, q, k)
     _call(load_library().attn_bwd, "attn_bwd", ctypes.byref(shape), *[ctypes.c_void_p(p) for p in ptrs],
           ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), _stream())
 
@@ -293,16 +290,39 @@ def _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal, rope_base, kv_
     return shape, (B, S, Hq, Hkv, d), ptrs
 
 
+def _workspace_arg(workspace, q, k):
+    """(pointer, bytes) of the backward workspace; when none is given and the
+    shape needs one, a torch tensor is allocated on q's stream (stream-ordered
+    reuse by torch's allocator keeps it valid until the kernels have run)."""
+    if workspace is None:
+        workspace = bwd_workspace(q, k)
+        if workspace is None:
+            return None, 0
+    return _check_gpu("workspace", workspace, workspace.dtype), workspace.numel() * workspace.element_size()
+
+
 def attn_bwd_dkdv(q, k, v, d_o, lse, delta, dk, dv, scale: float, seqlens=None, causal: int = 1,
-                  rope_base: float = 0.0):
-    """dK, dV <- the key-block pass of the backward (writes into `dk`, `dv`)."""
+                  rope_base: float = 0.0, workspace=None):
+    """dK, dV <- the key-block pass of the backward (writes into `dk`, `dv`;
+    `workspace` must hold attn_bwd_workspace_bytes() bytes when that is
+    nonzero)."""
     torch = _torch()
     shape, (B, S, Hq, Hkv, d), ptrs = _bwd_common(q, k, v, d_o, lse, delta, scale, seqlens, causal, rope_base,
                                                   kv_out=[("dk", dk), ("dv", dv)])
     ptrs += [_check_gpu("dk", dk, torch.bfloat16, (B, S, Hkv, d), True),
              _check_gpu("dv", dv, torch.bfloat16, (B, S, Hkv, d), True)]
+    ws_ptr, ws_bytes = _workspace_arg(workspace, q, k)
     _call(load_library().attn_bwd_dkdv, "attn_bwd_dkdv", ctypes.byref(shape),
-          *[ctypes.c_void_p(p) for p in ptrs], _stream())
+          *[ctypes.c_void_p(p) for p in ptrs], ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), _stream())
+
+
+def bwd_workspace(q, k):
+    """A workspace tensor of attn_bwd_workspace_bytes() bytes for q and k's
+    shapes, or None when none is needed."""
+    torch = _torch()
+    B, S, Hq, d = q.shape
+    need = attn_bwd_workspace_bytes(B, S, Hq, k.shape[2], d)
+    return torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
 
 
 def attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale: float, seqlens=None, causal: int = 1,
@@ -334,10 +354,7 @@ def attn_bwd_fused(q, k, v, o, d_o, lse, delta, dq, dk, dv, scale: float, seqlen
             _check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d), True),
             _check_gpu("dk", dk, torch.bfloat16, (B, S, Hkv, d), True),
             _check_gpu("dv", dv, torch.bfloat16, (B, S, Hkv, d), True)]
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        ws_ptr = _check_gpu("workspace", workspace, workspace.dtype)
-        ws_bytes = workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace_arg(workspace, q, k)
     _call(load_library().attn_bwd_fused, "attn_bwd_fused", ctypes.byref(shape), *[ctypes.c_void_p(p) for p in ptrs],
           ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), _stream())
 
@@ -449,8 +466,7 @@ def backward(q, k, v, o, d_o, lse, scale: Optional[float] = None, seqlens=None, 
         scale = 1.0 / math.sqrt(d)
     delta = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     attn_bwd_preprocess(o, d_o, delta, seqlens)
-    need = attn_bwd_workspace_bytes(B, S, Hq, k.shape[2], d)
-    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    ws = bwd_workspace(q, k)
     # dQ shares dO's strides and dK, dV share K's (one stride triple per group)
     dq = torch.empty_strided(d_o.shape, d_o.stride(), dtype=q.dtype, device=q.device)
     dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
@@ -478,6 +494,8 @@ def capture_step(q, k, v, d_o, o, lse, delta, dq, dk, dv, scale: float, seqlens=
     if rope_base and (q_rot is None or k_rot is None):
         raise ValueError("rope_base needs the q_rot and k_rot buffers")
     qa, ka = (q_rot, k_rot) if rope_base else (q, k)
+    if workspace is None:
+        workspace = bwd_workspace(q, k)  # allocated before the capture, bound to the graph
 
     def step():
         if rope_base:
@@ -488,7 +506,9 @@ def capture_step(q, k, v, d_o, o, lse, delta, dq, dk, dv, scale: float, seqlens=
         else:
             attn_bwd_preprocess(o, d_o, delta, seqlens)
             attn_bwd(qa, ka, v, d_o, lse, delta, dq, dk, dv, scale, seqlens, workspace, cz, rope_base)
-    return _capture(step)
+    graph = _capture(step)
+    graph.attn_workspace = workspace  # kept alive as long as the graph
+    return graph
 
 
 def _capture(step):

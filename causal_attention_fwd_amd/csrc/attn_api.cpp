@@ -112,6 +112,15 @@ attn_status check_ptrs(std::initializer_list<const void*> ptrs) {
 
 attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
+// The workspace rule of the backward entry points: at least
+// attn_bwd_workspace_bytes() bytes, 16-byte aligned when any are needed.
+attn_status check_workspace(const attn::Problem& pr, const void* workspace, size_t workspace_bytes) {
+  const size_t need = attn::bwd_workspace_bytes(pr);
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return ATTN_ERR_WORKSPACE;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,18 +157,22 @@ attn_status attn_rope(const attn_shape* shape, const void* q, const void* k, voi
 }
 
 size_t attn_bwd_workspace_bytes(const attn_shape* shape) {
-  (void)shape;
-  return 0;  // dQ has its own pass: no accumulation buffer
+  attn::Problem pr;
+  if (check_shape(shape, &pr) != ATTN_OK) return 0;
+  return attn::bwd_workspace_bytes(pr);
 }
 
 attn_status attn_bwd_dkdv(const attn_shape* shape, const void* q, const void* k, const void* v, const void* d_o,
-                          const float* lse, const float* delta, void* dk, void* dv, hipStream_t stream) {
+                          const float* lse, const float* delta, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
   attn::Problem pr;
   attn_status st = check_shape(shape, &pr);
   if (st != ATTN_OK) return st;
   st = check_ptrs({q, k, v, d_o, lse, delta, dk, dv});
   if (st != ATTN_OK) return st;
-  return from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, stream));
+  st = check_workspace(pr, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream));
 }
 
 attn_status attn_bwd_dq(const attn_shape* shape, const void* q, const void* k, const void* v, const void* d_o,
@@ -180,10 +193,9 @@ attn_status attn_bwd(const attn_shape* shape, const void* q, const void* k, cons
   if (st != ATTN_OK) return st;
   st = check_ptrs({q, k, v, d_o, lse, delta, dq, dk, dv});
   if (st != ATTN_OK) return st;
-  const size_t need = attn_bwd_workspace_bytes(shape);
-  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (need > 0 && (!workspace || !aligned16(workspace))) return ATTN_ERR_WORKSPACE;
-  st = from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, stream));
+  st = check_workspace(pr, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  st = from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream));
   if (st != ATTN_OK) return st;
   return from_hip(attn::launch_bwd_dq(pr, q, k, v, d_o, lse, delta, dq, stream));
 }
@@ -196,13 +208,12 @@ attn_status attn_bwd_fused(const attn_shape* shape, const void* q, const void* k
   if (st != ATTN_OK) return st;
   st = check_ptrs({q, k, v, o, d_o, lse, delta, dq, dk, dv});
   if (st != ATTN_OK) return st;
-  const size_t need = attn_bwd_workspace_bytes(shape);
-  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (need > 0 && (!workspace || !aligned16(workspace))) return ATTN_ERR_WORKSPACE;
+  st = check_workspace(pr, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
   // dQ first: it computes D, which the dK/dV pass then reads
   st = from_hip(attn::launch_bwd_dq_with_delta(pr, q, k, v, o, d_o, lse, delta, dq, stream));
   if (st != ATTN_OK) return st;
-  return from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, stream));
+  return from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream));
 }
 
 size_t attn_decode_workspace_bytes(const attn_decode_shape* shape) {

@@ -114,6 +114,13 @@ struct BwdArgs {
   // preprocess folded in); delta is then not read
   const bf16* o;
   float* delta_out;
+  // dK/dV pass only: with parts > 1 the (head, query tile) iterations of each
+  // key block are split into `parts` contiguous ranges, one workgroup each,
+  // whose unscaled fp32 dK and dV partial sums go to part_dk / part_dv
+  // ([part, B, S, Hkv, d], dense) for dkdv_reduce_kernel to add up
+  int parts;
+  float* part_dk;
+  float* part_dv;
 };
 
 constexpr int kThreads = 256;  // four waves, one per SIMD
@@ -479,14 +486,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sstat[GROUPS][2][2][BMQ];  // [group][buf][LSE*log2e, -D]
 
   const int grp = wave_id() >> 2;
+  const int swave = wave_id() & 3;  // wave within the group, in a scalar register
   const int gtid = threadIdx.x & (kThreads - 1);
   const int lane = threadIdx.x & 63;
   const int wave = gtid >> 6;
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
-  int kb, b, hkv;
-  decode_kblock(blockIdx.x, a.nblk, a.B, a.Hkv, GROUPS == 1, kb, b, hkv);
+  int kb, b, hkv, part;
+  decode_kblock(blockIdx.x, a.nblk, a.parts, a.B, a.Hkv, GROUPS == 1 && a.parts == 1, kb, part, b, hkv);
   const int S = a.S;
   const int L = valid_len(a.seqlens, b, S);
   const int G = a.Hq / a.Hkv;
@@ -521,22 +529,28 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int qt0 = a.causal ? j0 / BMQ : 0;  // first query tile with rows at or below the block
   const int nq = (j0 < L) ? (L - 1) / BMQ - qt0 + 1 : 0;  // query tiles per head
   const int iters = nq * G;                               // (head, query tile) pairs
-  const int trips = (iters + GROUPS - 1) / GROUPS;        // this group does it = trip*GROUPS + grp
+  // this workgroup's share of them: [it_lo, it_hi)
+  const int it_lo = (int)((int64_t)part * iters / a.parts);
+  const int it_hi = (int)((int64_t)(part + 1) * iters / a.parts);
+  const int trips = (it_hi - it_lo + GROUPS - 1) / GROUPS;  // this group does it = it_lo + trip*GROUPS + grp
 
-  float st_reg = 0.f;  // threads 0..63 of a group carry LSE, 64..127 carry D
+  float st_reg = 0.f;  // wave 0 of a group carries LSE, wave 1 D
   const KVBuf b0{sQ0 + grp * TILE, sO0 + grp * TILE, 0}, b1{sQ1 + grp * TILE, sO1 + grp * TILE, 1};
-  // this group handles (head, query tile) pair it = trip * GROUPS + grp
+  // this group handles (head, query tile) pair it = it_lo + trip * GROUPS + grp
   auto fetch = [&](int trip, const KVBuf& buf) {
-    const int it = trip * GROUPS + grp;
-    if (it >= iters) return;
+    const int it = it_lo + trip * GROUPS + grp;
+    if (it >= it_hi) return;
     const int hh = it / nq;
     const int qt = qt0 + (it - hh * nq);
     const int h = hkv * G + hh;
-    if (gtid < 2 * BMQ) {
+    if (swave < 2) {
       // raw value only: any arithmetic on it here would make the compiler wait
-      // for this load before the tile's compute
-      const int i = qt * BMQ + (gtid & (BMQ - 1));
-      const float* src = gtid < BMQ ? a.lse : a.delta;
+      // for this load before the tile's compute. Wave 0 of the group loads
+      // LSE, wave 1 D; the choice is made on the scalar wave index (a
+      // per-lane choice between the two pointers is compiled into a vector
+      // load of the pointer from the argument block, waited for at once)
+      const int i = qt * BMQ + lane;
+      const float* src = swave == 0 ? a.lse : a.delta;
       st_reg = 0.f;
       if (i < L) st_reg = src[((int64_t)b * a.Hq + h) * S + i];
     }
@@ -546,12 +560,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
     tile_load_lds<BMQ, D, 4>(dOb, os, qt * BMQ, L, buf.v, wave, lane);
   };
   auto land = [&](int trip, const KVBuf& buf) {
-    if (trip * GROUPS + grp < iters && gtid < 2 * BMQ)
-      sstat[grp][buf.idx][gtid / BMQ][gtid & (BMQ - 1)] = gtid < BMQ ? st_reg * kLog2e : -st_reg;
+    if (it_lo + trip * GROUPS + grp < it_hi && swave < 2)
+      sstat[grp][buf.idx][swave][lane] = swave == 0 ? st_reg * kLog2e : -st_reg;
   };
   auto compute = [&](int trip, const KVBuf& buf) {
-    const int it = trip * GROUPS + grp;
-    if (it >= iters) return;
+    const int it = it_lo + trip * GROUPS + grp;
+    if (it >= it_hi) return;
     const int hh = it / nq;
     const int qt = qt0 + (it - hh * nq);
     const int i0 = qt * BMQ;
@@ -608,6 +622,31 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
   }
 
+  if (a.parts > 1) {
+    // split: this part's unscaled fp32 sums for the valid key rows; the
+    // reduce pass adds the parts, scales dK, rotates back and converts
+    const int64_t prow = ((int64_t)part * a.B + b) * S;
+#pragma unroll
+    for (int t = 0; t < NTJ; ++t) {
+      const int j = jw + t * 32 + l32;
+      if (j < L) {
+        float* pk = a.part_dk + ((prow + j) * a.Hkv + hkv) * D;
+        float* pv = a.part_dv + ((prow + j) * a.Hkv + hkv) * D;
+#pragma unroll
+        for (int ct = 0; ct < DT; ++ct)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int c0 = ct * 32 + rr * 8 + g * 4;
+            *reinterpret_cast<float4*>(pk + c0) = make_float4(st.dk[ct][t][rr * 4 + 0], st.dk[ct][t][rr * 4 + 1],
+                                                              st.dk[ct][t][rr * 4 + 2], st.dk[ct][t][rr * 4 + 3]);
+            *reinterpret_cast<float4*>(pv + c0) = make_float4(st.dv[ct][t][rr * 4 + 0], st.dv[ct][t][rr * 4 + 1],
+                                                              st.dv[ct][t][rr * 4 + 2], st.dv[ct][t][rr * 4 + 3]);
+          }
+      }
+    }
+    return;
+  }
+
   // Epilogue: dK = scale * dK^T, dV = dV^T transposed back; lane owns key row j.
   bf16* dKb = a.dk + b * a.skv.b + hkv * a.skv.h;
   bf16* dVb = a.dv + b * a.skv.b + hkv * a.skv.h;
@@ -636,6 +675,52 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
     }
   }
+}
+
+// ----------------------------------------------------------------------------
+// dK/dV reduce (split dK/dV pass only): dK = scale * sum_p part_dk[p], dV =
+// sum_p part_dv[p] over the parts in a fixed order (deterministic), the
+// rotation's adjoint applied to dK, rounded to bf16 and written through the
+// K strides; padded key rows (j >= L) get zeros. One thread per 4 consecutive
+// elements of a (sequence, position, kv head) row.
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(BwdArgs a) {
+  constexpr int C4 = D / 4;
+  const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t total = (int64_t)a.B * a.S * a.Hkv * C4;
+  if (tid >= total) return;
+  const int c4 = (int)(tid % C4);
+  const int64_t row = tid / C4;  // (b * S + j) * Hkv + hkv
+  const int hkv = (int)(row % a.Hkv);
+  const int64_t bj = row / a.Hkv;
+  const int j = (int)(bj % a.S);
+  const int b = (int)(bj / a.S);
+  const int L = valid_len(a.seqlens, b, a.S);
+  float kx[4] = {0.f, 0.f, 0.f, 0.f}, vx[4] = {0.f, 0.f, 0.f, 0.f};
+  if (j < L) {
+    const int64_t pstride = (int64_t)a.B * a.S * a.Hkv * D;
+    const int64_t off = row * D + c4 * 4;
+    for (int p = 0; p < a.parts; ++p) {
+      const float4 k4 = *reinterpret_cast<const float4*>(a.part_dk + p * pstride + off);
+      const float4 v4 = *reinterpret_cast<const float4*>(a.part_dv + p * pstride + off);
+      kx[0] += k4.x; kx[1] += k4.y; kx[2] += k4.z; kx[3] += k4.w;
+      vx[0] += v4.x; vx[1] += v4.y; vx[2] += v4.z; vx[3] += v4.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kx[e] *= a.scale;
+    // pairs (d, d+1), (d+2, d+3) with d = c4 * 4 = d0 + 4g
+    if (a.rope) rope_adjoint4(a.rf, (c4 * 4) & ~7, c4 & 1, j, kx);
+  }
+  bf16x4 k4b, v4b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    k4b[e] = (bf16)kx[e];
+    v4b[e] = (bf16)vx[e];
+  }
+  const int64_t o = b * a.skv.b + (int64_t)j * a.skv.s + hkv * a.skv.h + c4 * 4;
+  *reinterpret_cast<bf16x4*>(a.dk + o) = k4b;
+  *reinterpret_cast<bf16x4*>(a.dv + o) = v4b;
 }
 
 // ----------------------------------------------------------------------------
@@ -1203,17 +1288,25 @@ namespace {
 // SIMD (OCC: the register budget per wave is 512 / OCC) and waves per
 // workgroup of the forward and dQ passes (W: the waves of a workgroup share
 // each K/V tile loaded into LDS).
+// Per head dimension: 32-row tiles per wave (NT: query rows in the forward and
+// dQ passes; the dK/dV pass always gives each wave 32 key rows), waves per
+// SIMD (OCC: the register budget per wave is 512 / OCC) and waves per
+// workgroup of the forward and dQ passes (W: the waves of a workgroup share
+// each K/V tile loaded into LDS). The *_SMALL configurations (64-row query
+// blocks) are used when the default blocks would leave CUs without work.
 template <int D> struct Tiles;
 template <> struct Tiles<64> {
-  static constexpr int FWD_NT = 2, FWD_OCC = 2, FWD_W = 4;
-  static constexpr int DQ_NT = 1, DQ_OCC = 3, DQ_W = 4;
+  static constexpr int FWD_NT = 2, FWD_OCC = 2, FWD_W = 4;   // 256-row blocks
+  static constexpr int DQ_NT = 1, DQ_OCC = 3, DQ_W = 4;      // 128-row blocks
   static constexpr int DKDV_NTJ = 1, DKDV_OCC = 2, DKDV_GROUPS = 2;
 };
 template <> struct Tiles<128> {
-  static constexpr int FWD_NT = 1, FWD_OCC = 2, FWD_W = 8;
-  static constexpr int DQ_NT = 1, DQ_OCC = 2, DQ_W = 4;
+  static constexpr int FWD_NT = 1, FWD_OCC = 2, FWD_W = 8;   // 256-row blocks
+  static constexpr int DQ_NT = 1, DQ_OCC = 2, DQ_W = 4;      // 128-row blocks
   static constexpr int DKDV_NTJ = 1, DKDV_OCC = 1, DKDV_GROUPS = 1;
 };
+// small-grid configurations: 64-row blocks of two waves
+constexpr int kSmallNT = 1, kSmallW = 2;
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -1235,14 +1328,22 @@ hipError_t launch(const void* fn, int64_t grid, Args args, hipStream_t stream, i
 // phi_i = base^(-2i/d) / (2 pi), in fp64 (zeros when RoPE is off)
 RopeFreq rope_freq(const Problem& pr) { return rope_freq_d(pr.rope_base, pr.d); }
 
+// Workgroups that fill the chip once: 256 CUs, each holding this many
+// workgroups of the default forward / dQ configuration at once.
+constexpr int64_t kCUs = 256;
+
 template <int D>
 hipError_t fwd_d(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,
                  hipStream_t stream) {
-  constexpr int NT = Tiles<D>::FWD_NT, W = Tiles<D>::FWD_W;
+  constexpr int NT = Tiles<D>::FWD_NT, W = Tiles<D>::FWD_W, OCC = Tiles<D>::FWD_OCC;
   FwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, pr.seqlens,
             pr.B, pr.S, pr.Hq, pr.Hkv, cdiv(pr.S, 32 * NT * W), pr.scale, pr.causal, pr.sq, pr.skv, pr.so};
-  return launch((const void*)&fwd_kernel<D, NT, Tiles<D>::FWD_OCC, W>, (int64_t)a.nqb * pr.B * pr.Hq, a, stream,
-                64 * W);
+  const int64_t wgs = (int64_t)a.nqb * pr.B * pr.Hq;
+  if (wgs >= kCUs * (4 * OCC / W))
+    return launch((const void*)&fwd_kernel<D, NT, OCC, W>, wgs, a, stream, 64 * W);
+  a.nqb = cdiv(pr.S, 32 * kSmallNT * kSmallW);
+  return launch((const void*)&fwd_kernel<D, kSmallNT, OCC, kSmallW>, (int64_t)a.nqb * pr.B * pr.Hq, a,
+                stream, 64 * kSmallW);
 }
 
 template <int D>
@@ -1255,28 +1356,39 @@ hipError_t pre_d(const Problem& pr, const void* o, const void* d_o, float* delta
 
 template <int D>
 hipError_t dkdv_d(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
-                  const float* lse, const float* delta, void* dk, void* dv, hipStream_t stream) {
+                  const float* lse, const float* delta, void* dk, void* dv, void* workspace, hipStream_t stream) {
   constexpr int NTJ = Tiles<D>::DKDV_NTJ;
+  const int parts = dkdv_parts(pr);
+  const size_t part_elems = (size_t)pr.B * pr.S * pr.Hkv * D * parts;
+  float* part_dk = parts > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
+  float* part_dv = parts > 1 ? part_dk + part_elems : nullptr;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             nullptr, (bf16*)dk, (bf16*)dv, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
             cdiv(pr.S, 128 * NTJ), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so,
-            nullptr, nullptr};
+            nullptr, nullptr, parts, part_dk, part_dv};
   constexpr int GR = Tiles<D>::DKDV_GROUPS;
-  return launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR>, (int64_t)a.nblk * pr.B * pr.Hkv, a,
-                stream, kThreads * GR);
+  hipError_t e = launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR>,
+                        (int64_t)a.nblk * parts * pr.B * pr.Hkv, a, stream, kThreads * GR);
+  if (e != hipSuccess || parts == 1) return e;
+  const int64_t threads = (int64_t)pr.B * pr.S * pr.Hkv * (D / 4);
+  return launch((const void*)&dkdv_reduce_kernel<D>, (threads + kThreads - 1) / kThreads, a, stream);
 }
 
 template <int D>
 hipError_t dq_d(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
                 const float* lse, const float* delta, void* dq, const void* o, float* delta_out,
                 hipStream_t stream) {
-  constexpr int NT = Tiles<D>::DQ_NT, W = Tiles<D>::DQ_W;
+  constexpr int NT = Tiles<D>::DQ_NT, W = Tiles<D>::DQ_W, OCC = Tiles<D>::DQ_OCC;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             (bf16*)dq, nullptr, nullptr, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
             cdiv(pr.S, 32 * NT * W), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so,
-            (const bf16*)o, delta_out};
-  return launch((const void*)&bwd_dq_kernel<D, NT, Tiles<D>::DQ_OCC, W>, (int64_t)a.nblk * pr.B * pr.Hq, a, stream,
-                64 * W);
+            (const bf16*)o, delta_out, 1, nullptr, nullptr};
+  const int64_t wgs = (int64_t)a.nblk * pr.B * pr.Hq;
+  if (wgs >= kCUs * (4 * OCC / W))
+    return launch((const void*)&bwd_dq_kernel<D, NT, OCC, W>, wgs, a, stream, 64 * W);
+  a.nblk = cdiv(pr.S, 32 * kSmallNT * kSmallW);
+  return launch((const void*)&bwd_dq_kernel<D, kSmallNT, OCC, kSmallW>, (int64_t)a.nblk * pr.B * pr.Hq,
+                a, stream, 64 * kSmallW);
 }
 
 template <int D>
@@ -1302,9 +1414,10 @@ hipError_t launch_preprocess(const Problem& pr, const void* o, const void* d_o, 
 }
 
 hipError_t launch_bwd_dkdv(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
-                           const float* lse, const float* delta, void* dk, void* dv, hipStream_t stream) {
-  return pr.d == 64 ? dkdv_d<64>(pr, q, k, v, d_o, lse, delta, dk, dv, stream)
-                    : dkdv_d<128>(pr, q, k, v, d_o, lse, delta, dk, dv, stream);
+                           const float* lse, const float* delta, void* dk, void* dv, void* workspace,
+                           hipStream_t stream) {
+  return pr.d == 64 ? dkdv_d<64>(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream)
+                    : dkdv_d<128>(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream);
 }
 
 hipError_t launch_bwd_dq(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,

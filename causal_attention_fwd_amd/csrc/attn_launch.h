@@ -27,8 +27,10 @@ hipError_t launch_fwd(const Problem& pr, const void* q, const void* k, const voi
 hipError_t launch_rope(const Problem& pr, const void* q, const void* k, void* q_rot, void* k_rot,
                        hipStream_t stream);
 hipError_t launch_preprocess(const Problem& pr, const void* o, const void* d_o, float* delta, hipStream_t stream);
+// workspace: bwd_workspace_bytes(pr) bytes (may be null when that is 0)
 hipError_t launch_bwd_dkdv(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
-                           const float* lse, const float* delta, void* dk, void* dv, hipStream_t stream);
+                           const float* lse, const float* delta, void* dk, void* dv, void* workspace,
+                           hipStream_t stream);
 hipError_t launch_bwd_dq(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
                          const float* lse, const float* delta, void* dq, hipStream_t stream);
 // The dQ pass computing D = rowsum(dO * O) itself (written to delta) instead
@@ -40,6 +42,16 @@ hipError_t launch_bwd_dq_with_delta(const Problem& pr, const void* q, const void
 // Largest grid any launch for this problem would use (checked against the
 // hardware's 2^31-1 workgroup limit by the API layer).
 int64_t max_grid(const Problem& pr);
+
+// Parts each 128-key block of the dK/dV pass is split into (1: no split).
+// When the key blocks alone would leave CUs idle, the (head, query tile)
+// iterations of every block are shared by several workgroups whose fp32
+// partial sums are added by a reduce pass.
+int dkdv_parts(const Problem& pr);
+
+// Device workspace the backward needs: the split dK/dV pass's fp32 partial
+// sums (2 * parts * B * S * Hkv * d floats), 0 without a split.
+size_t bwd_workspace_bytes(const Problem& pr);
 
 // Decode: Sq new queries per sequence against a [B, Smax, Hkv, d] key/value cache.
 struct DecodeProblem {

@@ -22,6 +22,26 @@ int64_t max_grid(const Problem& pr) {
   return m > rope ? m : rope;
 }
 
+int dkdv_parts(const Problem& pr) {
+  constexpr int64_t kCUs = 256, kMaxParts = 8;
+  // the dK/dV pass runs one 8-wave (d = 64) or 4-wave (d = 128) workgroup per
+  // CU over 128-key blocks
+  const int64_t units = ((int64_t)pr.S + 127) / 128 * pr.B * pr.Hkv;
+  if (units >= kCUs) return 1;
+  const int64_t want = (kCUs + units - 1) / units;
+  // every part of the longest block keeps at least four (head, query tile)
+  // iterations (two per wave group)
+  const int64_t iters0 = ((int64_t)pr.S + 63) / 64 * (pr.Hq / pr.Hkv);
+  const int64_t cap = std::max<int64_t>(1, iters0 / 4);
+  return (int)std::min(std::min(want, cap), kMaxParts);
+}
+
+size_t bwd_workspace_bytes(const Problem& pr) {
+  const int parts = dkdv_parts(pr);
+  if (parts <= 1) return 0;
+  return (size_t)2 * parts * pr.B * pr.S * pr.Hkv * pr.d * sizeof(float);
+}
+
 namespace {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace

@@ -145,10 +145,14 @@ attn_status attn_bwd_preprocess(const attn_shape* shape, const void* o, const vo
                                 float* delta, hipStream_t stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for `shape`: O(B*S*H*d) at most,
- * never O(S^2) (the "Axis" Zyora Labs page, feature list: memory stays flat as
- * the sequence grows). The current algorithm computes dQ in a separate pass and needs
- * none (returns 0). Returns 0 for a NULL shape.
+ * Bytes of device workspace attn_bwd, attn_bwd_dkdv and attn_bwd_fused need
+ * for `shape`: O(B*S*Hkv*d) at most, never O(S^2) (the "Axis" Zyora Labs page,
+ * feature list: memory stays flat as the sequence grows). It is 0 unless the
+ * shape has too few 128-key blocks (B * ceil(S/128) * Hkv < 256) to give every
+ * CU work; then each block's work is split into P <= 8 parts whose fp32
+ * partial dK and dV sums (2 * P * B * S * Hkv * d floats) are added by a
+ * reduce pass. Depends only on batch, seqlen, heads and head_dim. Returns 0
+ * for a NULL or invalid shape.
  */
 size_t attn_bwd_workspace_bytes(const attn_shape* shape);
 
@@ -173,13 +177,17 @@ attn_status attn_bwd(const attn_shape* shape, const void* q, const void* k, cons
  * them in either order or concurrently on two streams; attn_bwd enqueues
  * attn_bwd_dkdv then attn_bwd_dq on one stream.
  *   attn_bwd_dkdv: dK, dV [B,S,Hkv,d] bf16 (one pass per key block over the
- *                  query rows of every head in the kv head's group).
- *   attn_bwd_dq:   dQ [B,S,Hq,d] bf16 (one pass per query block over its keys).
- * Same validation, layouts and error codes as attn_bwd.
+ *                  query rows of every head in the kv head's group; with a
+ *                  nonzero attn_bwd_workspace_bytes() the blocks are split and
+ *                  a reduce pass follows, using the workspace).
+ *   attn_bwd_dq:   dQ [B,S,Hq,d] bf16 (one pass per query block over its keys;
+ *                  no workspace).
+ * Same validation, layouts and error codes as attn_bwd. Two concurrent
+ * attn_bwd_dkdv calls need distinct workspaces.
  */
 attn_status attn_bwd_dkdv(const attn_shape* shape, const void* q, const void* k, const void* v,
                           const void* d_o, const float* lse, const float* delta,
-                          void* dk, void* dv, hipStream_t stream);
+                          void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
 attn_status attn_bwd_dq(const attn_shape* shape, const void* q, const void* k, const void* v,
                         const void* d_o, const float* lse, const float* delta,
                         void* dq, hipStream_t stream);

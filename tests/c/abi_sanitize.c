@@ -55,8 +55,11 @@ static attn_decode_shape base_decode(void) {
 }
 
 #define CALL_FWD(s) attn_fwd(&(s), P(1), P(2), P(3), P(4), (float*)P(5), 0)
+/* the backward gets a workspace of exactly the size it asks for (a placeholder
+   address: the stubs never dereference it) */
 #define CALL_BWD(s) \
-  attn_bwd(&(s), P(1), P(2), P(3), P(6), (float*)P(5), (float*)P(7), P(8), P(9), P(10), NULL, 0, 0)
+  attn_bwd(&(s), P(1), P(2), P(3), P(6), (float*)P(5), (float*)P(7), P(8), P(9), P(10), P(15), \
+           attn_bwd_workspace_bytes(&(s)), 0)
 
 int main(void) {
   int n;
@@ -67,13 +70,33 @@ int main(void) {
   n = g_stub_launches; expect("pre", attn_bwd_preprocess(&s, P(4), P(6), (float*)P(7), 0), ATTN_OK, n, 1);
   n = g_stub_launches; expect("bwd", CALL_BWD(s), ATTN_OK, n, 2);
   n = g_stub_launches;
-  expect("dkdv", attn_bwd_dkdv(&s, P(1), P(2), P(3), P(6), (float*)P(5), (float*)P(7), P(9), P(10), 0), ATTN_OK,
-         n, 1);
+  expect("dkdv", attn_bwd_dkdv(&s, P(1), P(2), P(3), P(6), (float*)P(5), (float*)P(7), P(9), P(10), P(15),
+                               attn_bwd_workspace_bytes(&s), 0), ATTN_OK, n, 1);
+  /* this shape has few key blocks: the split needs a workspace, refused when short or missing */
+  if (attn_bwd_workspace_bytes(&s) == 0) { printf("FAIL small shape needs no workspace\n"); ++failures; }
+  n = g_stub_launches;
+  expect("dkdv short ws", attn_bwd_dkdv(&s, P(1), P(2), P(3), P(6), (float*)P(5), (float*)P(7), P(9), P(10), P(15),
+                                        attn_bwd_workspace_bytes(&s) - 1, 0), ATTN_ERR_WORKSPACE, n, 0);
+  n = g_stub_launches;
+  expect("bwd null ws", attn_bwd(&s, P(1), P(2), P(3), P(6), (float*)P(5), (float*)P(7), P(8), P(9), P(10), NULL,
+                                 attn_bwd_workspace_bytes(&s), 0), ATTN_ERR_WORKSPACE, n, 0);
+  n = g_stub_launches;
+  expect("bwd misaligned ws", attn_bwd(&s, P(1), P(2), P(3), P(6), (float*)P(5), (float*)P(7), P(8), P(9), P(10),
+                                       (void*)(arena + 4), attn_bwd_workspace_bytes(&s), 0), ATTN_ERR_WORKSPACE, n, 0);
+  {
+    /* many key blocks: no split, no workspace */
+    attn_shape big = base_shape();
+    big.batch = 16; big.seqlen = 4096; big.heads_q = 32; big.heads_kv = 8;
+    if (attn_bwd_workspace_bytes(&big) != 0) { printf("FAIL large shape asks for a workspace\n"); ++failures; }
+    n = g_stub_launches;
+    expect("bwd no ws needed", attn_bwd(&big, P(1), P(2), P(3), P(6), (float*)P(5), (float*)P(7), P(8), P(9), P(10),
+                                        NULL, 0, 0), ATTN_OK, n, 2);
+  }
   n = g_stub_launches;
   expect("dq", attn_bwd_dq(&s, P(1), P(2), P(3), P(6), (float*)P(5), (float*)P(7), P(8), 0), ATTN_OK, n, 1);
   n = g_stub_launches;
   expect("fused", attn_bwd_fused(&s, P(1), P(2), P(3), P(4), P(6), (float*)P(5), (float*)P(7), P(8), P(9), P(10),
-                                 NULL, 0, 0), ATTN_OK, n, 2);
+                                 P(15), attn_bwd_workspace_bytes(&s), 0), ATTN_OK, n, 2);
   s.rope_base = 10000.f;
   n = g_stub_launches; expect("rope", attn_rope(&s, P(1), P(2), P(11), P(12), 0), ATTN_OK, n, 1);
   s.rope_base = 0.f;

@@ -69,9 +69,10 @@ hipError_t launch_preprocess(const Problem& pr, const void* o, const void* d_o, 
 }
 
 hipError_t launch_bwd_dkdv(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
-                           const float* lse, const float* delta, void* dk, void* dv, hipStream_t) {
+                           const float* lse, const float* delta, void* dk, void* dv, void* workspace, hipStream_t) {
   check_problem(pr);
   check_ptrs({q, k, v, d_o, lse, delta, dk, dv});
+  if (bwd_workspace_bytes(pr) > 0) check_ptrs({workspace});
   return done();
 }
 

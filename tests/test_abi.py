@@ -74,7 +74,8 @@ def _bwd(lib, shape, ptrs=(GOOD,) * 9, ws=None, ws_bytes=0):
 
 
 def _dkdv(lib, shape, ptrs=(GOOD,) * 8):
-    return lib.attn_bwd_dkdv(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], P(0))
+    return lib.attn_bwd_dkdv(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], None, 0,
+                             P(0))
 
 
 def _dq(lib, shape, ptrs=(GOOD,) * 7):
