@@ -195,9 +195,7 @@ attn_status attn_bwd(const attn_shape* shape, const void* q, const void* k, cons
   if (st != ATTN_OK) return st;
   st = check_workspace(pr, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
-  st = from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream));
-  if (st != ATTN_OK) return st;
-  return from_hip(attn::launch_bwd_dq(pr, q, k, v, d_o, lse, delta, dq, stream));
+  return from_hip(attn::launch_bwd(pr, q, k, v, d_o, lse, delta, dq, dk, dv, workspace, stream));
 }
 
 attn_status attn_bwd_fused(const attn_shape* shape, const void* q, const void* k, const void* v, const void* o,
@@ -210,10 +208,7 @@ attn_status attn_bwd_fused(const attn_shape* shape, const void* q, const void* k
   if (st != ATTN_OK) return st;
   st = check_workspace(pr, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
-  // dQ first: it computes D, which the dK/dV pass then reads
-  st = from_hip(attn::launch_bwd_dq_with_delta(pr, q, k, v, o, d_o, lse, delta, dq, stream));
-  if (st != ATTN_OK) return st;
-  return from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream));
+  return from_hip(attn::launch_bwd_fused(pr, q, k, v, o, d_o, lse, delta, dq, dk, dv, workspace, stream));
 }
 
 size_t attn_decode_workspace_bytes(const attn_decode_shape* shape) {
