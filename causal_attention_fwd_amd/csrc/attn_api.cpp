@@ -195,7 +195,9 @@ attn_status attn_bwd(const attn_shape* shape, const void* q, const void* k, cons
   if (st != ATTN_OK) return st;
   st = check_workspace(pr, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
-  return from_hip(attn::launch_bwd(pr, q, k, v, d_o, lse, delta, dq, dk, dv, workspace, stream));
+  st = from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream));
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd_dq(pr, q, k, v, d_o, lse, delta, dq, stream));
 }
 
 attn_status attn_bwd_fused(const attn_shape* shape, const void* q, const void* k, const void* v, const void* o,
@@ -208,7 +210,10 @@ attn_status attn_bwd_fused(const attn_shape* shape, const void* q, const void* k
   if (st != ATTN_OK) return st;
   st = check_workspace(pr, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
-  return from_hip(attn::launch_bwd_fused(pr, q, k, v, o, d_o, lse, delta, dq, dk, dv, workspace, stream));
+  // dQ first: it computes D, which the dK/dV pass then reads
+  st = from_hip(attn::launch_bwd_dq_with_delta(pr, q, k, v, o, d_o, lse, delta, dq, stream));
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream));
 }
 
 size_t attn_decode_workspace_bytes(const attn_decode_shape* shape) {

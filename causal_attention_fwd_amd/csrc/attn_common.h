@@ -130,14 +130,6 @@ __device__ __forceinline__ bf16x8 frag_tr(const bf16* tile, int row0, int col0, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Element offset of (row x, column c) in a TileLayout<D> tile.
-template <int D>
-__device__ __forceinline__ int tile_off(int x, int c) {
-  constexpr int BE = TileLayout<D>::kBlockElems;
-  const int ch = c >> 3;
-  return (x >> 3) * BE + (ch * 8 + ((x & 7) ^ (((ch >> 1) & 1) << 2))) * 8 + (c & 7);
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Direct global -> LDS load of rows [row0, row0 + R) of one (sequence, head)

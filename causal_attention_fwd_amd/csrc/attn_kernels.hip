@@ -58,7 +58,6 @@ struct PreArgs {
   int B, S, Hq;
   int64_t rows;  // B * Hq * S
   Strides so;    // O and dO
-  float* dq_acc;  // when set: the fp32 dQ sums [B, S, Hq, d] are zeroed here
 };
 
 // Rotary position embedding ("AxiomLM" PyPI page, "Key Features" and "8.
@@ -122,9 +121,6 @@ struct BwdArgs {
   int parts;
   float* part_dk;
   float* part_dv;
-  // dK/dV pass with dQ by atomics only: fp32 dQ sums [B, S, Hq, d] (zeroed
-  // beforehand), each workgroup adding dS K over its key block
-  float* dq_acc;
 };
 
 constexpr int kThreads = 256;  // four waves, one per SIMD
@@ -366,18 +362,6 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(PreArgs a) {
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (r < a.rows && part == 0) a.delta[r] = s < valid_len(a.seqlens, b, a.S) ? acc : 0.f;
-  if (a.dq_acc && r < a.rows) {
-    const int h = (int)((r / a.S) % a.Hq);
-    float4* z = reinterpret_cast<float4*>(a.dq_acc + (((int64_t)b * a.S + s) * a.Hq + h) * D + part * 8);
-    z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-    z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-}
-
-// Zero n4 float4s (the fp32 dQ sums before a backward that adds into them).
-__global__ __launch_bounds__(kThreads) void zero_kernel(float4* p, int64_t n4) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // ----------------------------------------------------------------------------
@@ -396,10 +380,10 @@ struct DkdvState {
 // One 64-row query tile for one wave. MASK: query row i of register (m2, r)
 // takes part only if lo[t] <= m2*32 + creg_off(r) <= hi[t] (causal, and both
 // positions inside the valid length).
-template <int D, int NTJ, bool MASK, bool DSOUT = false>
+template <int D, int NTJ, bool MASK>
 __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs, const bf16* dOs, const float* lse2,
                                           const float* ndl, int lane, float c, const int (&lo)[NTJ],
-                                          const int (&hi)[NTJ], bf16* dsT = nullptr, int kw = 0) {
+                                          const int (&hi)[NTJ]) {
   constexpr int KK = D / 16, DT = D / 32;
   const int g = lane >> 5;
   // dP starts from -D (row i of register rr*4 + e is m2*32 + rr*8 + g*4 + e,
@@ -470,22 +454,6 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
       pb[u][t] = pack8(s[u >> 1][t], (u & 1) * 8);
       sb[u][t] = pack8(dp[u >> 1][t], (u & 1) * 8);
     }
-  if constexpr (DSOUT) {
-    // dS^T into the block's [key, query row] tile for the dQ product: the
-    // lane's key row kw + t*32 + l%32; sb[u] holds query rows u*16 + g*4 + 0..3
-    // and u*16 + 8 + g*4 + 0..3, two 8-byte pieces
-#pragma unroll
-    for (int t = 0; t < NTJ; ++t) {
-      const int x = kw + t * 32 + (lane & 31);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r0 = u * 16 + g * 4;
-        const bf16x8 v = sb[u][t];
-        *reinterpret_cast<bf16x4*>(dsT + tile_off<64>(x, r0)) = (bf16x4){v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<bf16x4*>(dsT + tile_off<64>(x, r0 + 8)) = (bf16x4){v[4], v[5], v[6], v[7]};
-      }
-    }
-  }
 #pragma unroll
   for (int ct = 0; ct < DT; ++ct)
 #pragma unroll
@@ -504,13 +472,7 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
 // own the same key rows and split the (head, query tile) sequence by parity;
 // their partial dK/dV are summed through LDS at the end. With two groups each
 // SIMD keeps two waves busy for the whole block, however long it is.
-// With DQA (d = 64, one 32-key tile per wave), the pass also adds each query
-// tile's dQ = dS K over the block's 128 keys into a.dq_acc with fp32 atomics:
-// every wave writes its dS^T slice into a [128 key, 64 query row] LDS tile
-// (double-buffered per group), and in the next trip (after the barrier) each
-// of the group's four waves computes one 32 x 32 block of dQ from that tile
-// and K^T fragments it keeps in registers.
-template <int D, int NTJ, int OCC, int GROUPS, bool DQA = false>
+template <int D, int NTJ, int OCC, int GROUPS>
 __global__ __launch_bounds__(kThreads * GROUPS) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BMQ = 64;
@@ -518,14 +480,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
   constexpr int TILE = TileLayout<D>::template elems<BMQ>();
-  static_assert(!DQA || (D == 64 && NTJ == 1), "dQ by atomics: d = 64, 32 keys per wave");
   // [group] tiles; Q and dO of the two pipeline stages live in distinct arrays
   __shared__ __attribute__((aligned(16))) bf16 sQ0[GROUPS * TILE], sO0[GROUPS * TILE], sQ1[GROUPS * TILE],
       sO1[GROUPS * TILE];
   __shared__ __attribute__((aligned(16))) float sstat[GROUPS][2][2][BMQ];  // [group][buf][LSE*log2e, -D]
-  // dQA: [group] dS^T tiles of the two trip parities (128 key rows x 64 query columns)
-  constexpr int DST = TileLayout<64>::template elems<128>();
-  __shared__ __attribute__((aligned(16))) bf16 sS0[DQA ? GROUPS * DST : 8], sS1[DQA ? GROUPS * DST : 8];
 
   const int grp = wave_id() >> 2;
   const int swave = wave_id() & 3;  // wave within the group, in a scalar register
@@ -549,19 +507,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int j0 = kb * BN;
   const int jw = j0 + wave * 32 * NTJ;
   const float c = a.scale * kLog2e;
-
-  // dQA: this wave's block of each query tile's dQ is rows dqm*32.., columns
-  // dqn*32..; kq[u] = K^T fragment of keys u*16.. for those columns
-  const int dqm = wave >> 1, dqn = wave & 1;
-  bf16x8 kq[DQA ? 8 : 1];
-  if constexpr (DQA) {
-    // the block's K rows staged through the first dS tile
-    tile_load_lds<128, 64, 4 * GROUPS>(Kb, ks, j0, L, sS0, wave_id(), lane);
-    wait_vmem();
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 8; ++u) kq[u] = frag_tr<64>(sS0, u * 16, dqn * 32, lane);
-  }
 
   DkdvState<D, NTJ> st;
 #pragma unroll
@@ -618,36 +563,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     if (it_lo + trip * GROUPS + grp < it_hi && swave < 2)
       sstat[grp][buf.idx][swave][lane] = swave == 0 ? st_reg * kLog2e : -st_reg;
   };
-  // dQA: dQ block of the group's trip `tr` from its dS^T tile, added to dq_acc
-  auto dq_trip = [&](int tr, const bf16* dsT) {
-    const int it = it_lo + tr * GROUPS + grp;
-    if (it >= it_hi) return;
-    const int hh = it / nq;
-    const int qt = qt0 + (it - hh * nq);
-    const int i0 = qt * BMQ;
-    const int h = hkv * G + hh;
-    // keys at or past kmax have dS = 0 for every row of the tile (and their
-    // waves may have skipped it, leaving stale data): 16-key chunks below it only
-    const int kmax = a.causal ? min(i0 + BMQ, L) : L;
-    const int nch = min(8, (kmax - j0 + 15) >> 4);
-    f32x16 acc = zero16();
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (u < nch) acc = mfma32(frag_tr<64>(dsT, u * 16, dqm * 32, lane), kq[u], acc);
-    float* base = a.dq_acc + ((int64_t)b * S * a.Hq + h) * 64 + dqn * 32 + l32;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = i0 + dqm * 32 + creg_off(r) + g * 4;
-      if (i < L) __hip_atomic_fetch_add(base + (int64_t)i * a.Hq * 64, acc[r], __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    }
-  };
   auto compute = [&](int trip, const KVBuf& buf) {
-    if constexpr (DQA) {
-      // the previous trip's dS^T tile (the other parity) is complete: every
-      // wave of the group wrote its slice before the barrier ending that trip
-      if (trip > 0) dq_trip(trip - 1, (buf.idx == 0 ? sS1 : sS0) + grp * DST);
-    }
     const int it = it_lo + trip * GROUPS + grp;
     if (it >= it_hi) return;
     const int hh = it / nq;
@@ -666,19 +582,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
         lo[t] = a.causal ? j - i0 - g * 4 : -(1 << 30);  // causal: i >= j
         hi[t] = (j < L) ? L - 1 - i0 - g * 4 : -1;  // i < L, and no rows when j >= L
       }
-      dkdv_tile<D, NTJ, true, DQA>(st, buf.k, buf.v, ls, ds, lane, c, lo, hi,
-                                   (buf.idx == 0 ? sS0 : sS1) + grp * DST, wave * 32);
+      dkdv_tile<D, NTJ, true>(st, buf.k, buf.v, ls, ds, lane, c, lo, hi);
     } else {
       const int lo[NTJ] = {}, hi[NTJ] = {};
-      dkdv_tile<D, NTJ, false, DQA>(st, buf.k, buf.v, ls, ds, lane, c, lo, hi,
-                                    (buf.idx == 0 ? sS0 : sS1) + grp * DST, wave * 32);
+      dkdv_tile<D, NTJ, false>(st, buf.k, buf.v, ls, ds, lane, c, lo, hi);
     }
   };
   tile_pipeline(trips, b0, b1, fetch, land, compute);
-  // the last trip's dQ (the pipeline ends with a barrier)
-  if constexpr (DQA) {
-    if (trips > 0) dq_trip(trips - 1, (((trips - 1) & 1) ? sS1 : sS0) + grp * DST);
-  }
 
   if constexpr (GROUPS == 2) {
     // group 1 hands its partial sums to group 0 through LDS (the tile buffers
@@ -811,38 +721,6 @@ __global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(BwdArgs a) {
   const int64_t o = b * a.skv.b + (int64_t)j * a.skv.s + hkv * a.skv.h + c4 * 4;
   *reinterpret_cast<bf16x4*>(a.dk + o) = k4b;
   *reinterpret_cast<bf16x4*>(a.dv + o) = v4b;
-}
-
-// ----------------------------------------------------------------------------
-// dQ convert (dQ by atomics only): dQ = scale * dq_acc, the rotation's adjoint
-// applied, rounded to bf16 and written through the dQ strides; padded rows
-// (i >= L) get zeros. One thread per 4 consecutive elements of a row.
-// ----------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kThreads) void dq_convert_kernel(BwdArgs a) {
-  constexpr int C4 = D / 4;
-  const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.S * a.Hq * C4;
-  if (tid >= total) return;
-  const int c4 = (int)(tid % C4);
-  const int64_t row = tid / C4;  // (b * S + i) * Hq + h
-  const int h = (int)(row % a.Hq);
-  const int64_t bi = row / a.Hq;
-  const int i = (int)(bi % a.S);
-  const int b = (int)(bi / a.S);
-  float x[4] = {0.f, 0.f, 0.f, 0.f};
-  if (i < valid_len(a.seqlens, b, a.S)) {
-    const float4 v = *reinterpret_cast<const float4*>(a.dq_acc + row * D + c4 * 4);
-    x[0] = v.x * a.scale;
-    x[1] = v.y * a.scale;
-    x[2] = v.z * a.scale;
-    x[3] = v.w * a.scale;
-    if (a.rope) rope_adjoint4(a.rf, (c4 * 4) & ~7, c4 & 1, i, x);
-  }
-  bf16x4 o;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = (bf16)x[e];
-  *reinterpret_cast<bf16x4*>(a.dq + b * a.so.b + (int64_t)i * a.so.s + h * a.so.h + c4 * 4) = o;
 }
 
 // ----------------------------------------------------------------------------
@@ -1469,51 +1347,31 @@ hipError_t fwd_d(const Problem& pr, const void* q, const void* k, const void* v,
 }
 
 template <int D>
-hipError_t pre_d(const Problem& pr, const void* o, const void* d_o, float* delta, hipStream_t stream,
-                 float* dq_acc = nullptr) {
+hipError_t pre_d(const Problem& pr, const void* o, const void* d_o, float* delta, hipStream_t stream) {
   PreArgs a{(const bf16*)o, (const bf16*)d_o, delta, pr.seqlens, pr.B, pr.S, pr.Hq,
-            (int64_t)pr.B * pr.S * pr.Hq, pr.so, dq_acc};
+            (int64_t)pr.B * pr.S * pr.Hq, pr.so};
   constexpr int rows_per_block = kThreads / (D / 8);
   return launch((const void*)&preprocess_kernel<D>, (a.rows + rows_per_block - 1) / rows_per_block, a, stream);
 }
 
 template <int D>
 hipError_t dkdv_d(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
-                  const float* lse, const float* delta, void* dk, void* dv, void* workspace, hipStream_t stream,
-                  float* dq_acc = nullptr, void* dq = nullptr) {
+                  const float* lse, const float* delta, void* dk, void* dv, void* workspace, hipStream_t stream) {
   constexpr int NTJ = Tiles<D>::DKDV_NTJ;
-  const BwdPlan plan = plan_bwd(pr);
-  const int parts = plan.parts;
+  const int parts = dkdv_parts(pr);
   const size_t part_elems = (size_t)pr.B * pr.S * pr.Hkv * D * parts;
-  float* part_dk = parts > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.off_parts)
-                             : nullptr;
+  float* part_dk = parts > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
   float* part_dv = parts > 1 ? part_dk + part_elems : nullptr;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
-            (bf16*)dq, (bf16*)dk, (bf16*)dv, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
+            nullptr, (bf16*)dk, (bf16*)dv, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
             cdiv(pr.S, 128 * NTJ), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so,
-            nullptr, nullptr, parts, part_dk, part_dv, dq_acc};
+            nullptr, nullptr, parts, part_dk, part_dv};
   constexpr int GR = Tiles<D>::DKDV_GROUPS;
-  const int64_t grid = (int64_t)a.nblk * parts * pr.B * pr.Hkv;
-  hipError_t e;
-  if constexpr (D == 64) {
-    e = dq_acc ? launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR, true>, grid, a, stream,
-                        kThreads * GR)
-               : launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR>, grid, a, stream,
-                        kThreads * GR);
-  } else {
-    e = launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR>, grid, a, stream, kThreads * GR);
-  }
-  if (e != hipSuccess) return e;
-  if (parts > 1) {
-    const int64_t threads = (int64_t)pr.B * pr.S * pr.Hkv * (D / 4);
-    e = launch((const void*)&dkdv_reduce_kernel<D>, (threads + kThreads - 1) / kThreads, a, stream);
-    if (e != hipSuccess) return e;
-  }
-  if (dq_acc) {
-    const int64_t threads = (int64_t)pr.B * pr.S * pr.Hq * (D / 4);
-    e = launch((const void*)&dq_convert_kernel<D>, (threads + kThreads - 1) / kThreads, a, stream);
-  }
-  return e;
+  hipError_t e = launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR>,
+                        (int64_t)a.nblk * parts * pr.B * pr.Hkv, a, stream, kThreads * GR);
+  if (e != hipSuccess || parts == 1) return e;
+  const int64_t threads = (int64_t)pr.B * pr.S * pr.Hkv * (D / 4);
+  return launch((const void*)&dkdv_reduce_kernel<D>, (threads + kThreads - 1) / kThreads, a, stream);
 }
 
 template <int D>
@@ -1524,7 +1382,7 @@ hipError_t dq_d(const Problem& pr, const void* q, const void* k, const void* v, 
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,
             (bf16*)dq, nullptr, nullptr, pr.seqlens, pr.B, pr.S, pr.Hq, pr.Hkv,
             cdiv(pr.S, 32 * NT * W), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so,
-            (const bf16*)o, delta_out, 1, nullptr, nullptr, nullptr};
+            (const bf16*)o, delta_out, 1, nullptr, nullptr};
   const int64_t wgs = (int64_t)a.nblk * pr.B * pr.Hq;
   if (wgs >= kCUs * (4 * OCC / W))
     return launch((const void*)&bwd_dq_kernel<D, NT, OCC, W>, wgs, a, stream, 64 * W);
@@ -1566,43 +1424,6 @@ hipError_t launch_bwd_dq(const Problem& pr, const void* q, const void* k, const 
                          const float* lse, const float* delta, void* dq, hipStream_t stream) {
   return pr.d == 64 ? dq_d<64>(pr, q, k, v, d_o, lse, delta, dq, nullptr, nullptr, stream)
                     : dq_d<128>(pr, q, k, v, d_o, lse, delta, dq, nullptr, nullptr, stream);
-}
-
-hipError_t launch_bwd(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
-                      const float* lse, const float* delta, void* dq, void* dk, void* dv, void* workspace,
-                      hipStream_t stream) {
-  const BwdPlan plan = plan_bwd(pr);
-  if (plan.dq_atomic) {
-    float* acc = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.off_dq);
-    float4* acc4 = reinterpret_cast<float4*>(acc);
-    int64_t n4 = (int64_t)pr.B * pr.S * pr.Hq * pr.d / 4;
-    void* kargs[] = {&acc4, &n4};
-    hipError_t e = hipLaunchKernel((const void*)&zero_kernel, dim3((unsigned)((n4 + kThreads - 1) / kThreads)),
-                                   dim3(kThreads), kargs, 0, stream);
-    if (e != hipSuccess) return e;
-    return dkdv_d<64>(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream, acc, dq);
-  }
-  hipError_t e = launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream);
-  if (e != hipSuccess) return e;
-  return launch_bwd_dq(pr, q, k, v, d_o, lse, delta, dq, stream);
-}
-
-hipError_t launch_bwd_fused(const Problem& pr, const void* q, const void* k, const void* v, const void* o,
-                            const void* d_o, const float* lse, float* delta, void* dq, void* dk, void* dv,
-                            void* workspace, hipStream_t stream) {
-  const BwdPlan plan = plan_bwd(pr);
-  if (plan.dq_atomic) {
-    // the preprocess computes D and zeroes the dQ sums, then one pass does
-    // dK, dV and the dQ sums, then dQ is converted
-    float* acc = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.off_dq);
-    hipError_t e = pre_d<64>(pr, o, d_o, delta, stream, acc);
-    if (e != hipSuccess) return e;
-    return dkdv_d<64>(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream, acc, dq);
-  }
-  // dQ first: it computes D, which the dK/dV pass then reads
-  hipError_t e = launch_bwd_dq_with_delta(pr, q, k, v, o, d_o, lse, delta, dq, stream);
-  if (e != hipSuccess) return e;
-  return launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream);
 }
 
 hipError_t launch_bwd_dq_with_delta(const Problem& pr, const void* q, const void* k, const void* v,

@@ -49,26 +49,9 @@ int64_t max_grid(const Problem& pr);
 // partial sums are added by a reduce pass.
 int dkdv_parts(const Problem& pr);
 
-// The backward's workspace: the split dK/dV pass's fp32 partial sums
-// (2 * parts * B * S * Hkv * d floats) and, when dQ is accumulated with
-// atomics inside the dK/dV pass, the fp32 dQ sums (B * S * Hq * d floats).
-struct BwdPlan {
-  int parts;        // dkdv_parts(pr)
-  bool dq_atomic;   // dQ added into dq_acc by the dK/dV pass, then converted
-  size_t off_parts, off_dq;
-  size_t bytes;     // total workspace bytes (0: none needed)
-};
-BwdPlan plan_bwd(const Problem& pr);
+// Device workspace the backward needs: the split dK/dV pass's fp32 partial
+// sums (2 * parts * B * S * Hkv * d floats), 0 without a split.
 size_t bwd_workspace_bytes(const Problem& pr);
-
-// The whole backward (attn_bwd: D given) and the backward with the
-// preprocess folded in (attn_bwd_fused: D computed and written to delta).
-hipError_t launch_bwd(const Problem& pr, const void* q, const void* k, const void* v, const void* d_o,
-                      const float* lse, const float* delta, void* dq, void* dk, void* dv, void* workspace,
-                      hipStream_t stream);
-hipError_t launch_bwd_fused(const Problem& pr, const void* q, const void* k, const void* v, const void* o,
-                            const void* d_o, const float* lse, float* delta, void* dq, void* dk, void* dv,
-                            void* workspace, hipStream_t stream);
 
 // Decode: Sq new queries per sequence against a [B, Smax, Hkv, d] key/value cache.
 struct DecodeProblem {

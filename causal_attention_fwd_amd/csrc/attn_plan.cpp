@@ -36,27 +36,15 @@ int dkdv_parts(const Problem& pr) {
   return (int)std::min(std::min(want, cap), kMaxParts);
 }
 
+size_t bwd_workspace_bytes(const Problem& pr) {
+  const int parts = dkdv_parts(pr);
+  if (parts <= 1) return 0;
+  return (size_t)2 * parts * pr.B * pr.S * pr.Hkv * pr.d * sizeof(float);
+}
+
 namespace {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
-
-BwdPlan plan_bwd(const Problem& pr) {
-  BwdPlan p;
-  p.parts = dkdv_parts(pr);
-#ifdef ATTN_DQ_ATOMIC
-  p.dq_atomic = pr.d == 64;
-#else
-  p.dq_atomic = false;
-#endif
-  const size_t dq_bytes = p.dq_atomic ? (size_t)pr.B * pr.S * pr.Hq * pr.d * sizeof(float) : 0;
-  const size_t part_bytes = p.parts > 1 ? (size_t)2 * p.parts * pr.B * pr.S * pr.Hkv * pr.d * sizeof(float) : 0;
-  p.off_dq = 0;
-  p.off_parts = align256(dq_bytes);
-  p.bytes = part_bytes ? p.off_parts + part_bytes : dq_bytes;
-  return p;
-}
-
-size_t bwd_workspace_bytes(const Problem& pr) { return plan_bwd(pr).bytes; }
 
 // Workspace layout: [hdr: 256 B][uinfo: int2 per unit][partial LSE][partial O],
 // each part 256-byte aligned.
