@@ -258,6 +258,19 @@ def copy_calibration(args):
 
 # ----------------------------------------------------------------------------- the benchmark
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, inp, budget_s: float, causal: bool = True, rope_base: float = 0.0):
     """The oracle (fp32 mode, untuned) on whole (sequence, kv head) units of the
     same workload until about `budget_s` seconds of CPU work have been spent."""
@@ -306,6 +319,7 @@ def cpu_baseline(w, inp, budget_s: float, causal: bool = True, rope_base: float 
             break
     dtf = time.perf_counter() - t1
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
             "fwd_value": ffl / dtf / 1e12,
             "sample": f"{done} (sequence, kv head) unit evaluations ({done / len(units):.2f} passes over the "
                       f"{len(units)} units) of {w.name}, fwd+bwd, numpy fp32, {dt:.1f} s; fwd_value: the "
@@ -478,12 +492,82 @@ def run(args):
                            "attn_bwd_fused": round(fl["bwd"] / (per["dkdv"] * 1e-3) / 1e12, 1)}),
         "roofline": roof,
     }
+    if not args.no_hbm:
+        result["hbm_rotated"] = hbm_rotated(torch, attn, q, k, do, o, sl, rb if args.rope else 0.0, args)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, causal, rb)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def hbm_rotated(torch, attn, q, k, do, o, sl, rope_base, args):
+    """HBM throughput of the bandwidth-bound kernels on inputs that are not in
+    the 256 MB last-level cache: enough copies of the preprocess's O and dO
+    (and of the RoPE pre-pass's q and k) that the set rotated through exceeds
+    three times the cache and holds at least four copies. Each launch reads a
+    copy the previous launches have pushed out; HIP events on the library's
+    stream time replays of a HIP graph holding one launch per copy. Algorithmic bytes: preprocess 2 * (B*S*Hq*d*2)
+    read + B*Hq*S*4 written; RoPE (B*S*(Hq+Hkv)*d*2) read + the same written.
+    A plain device copy timed the same way gives the bandwidth the box
+    sustains for reference."""
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    out = {}
+
+    def timed(n_copies, launch):
+        # one launch per copy, captured in a HIP graph so that host-side
+        # launch cost cannot set the pace; the graph is replayed and timed
+        for i in range(n_copies):  # eager pass (checks the arguments)
+            launch(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n_copies):
+                launch(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        replays = 5
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(replays):
+            graph.replay()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / (replays * n_copies)
+
+    pre_read = 2.0 * B * S * Hq * d * 2
+    pre_bytes = pre_read + B * Hq * S * 4.0
+    copies = max(4, math.ceil(3 * MALL_BYTES / pre_read) + 1)
+    sets = [(o.clone(), do.clone(), torch.empty(B, Hq, S, device=q.device)) for _ in range(copies)]
+    ms = timed(copies, lambda i: attn.attn_bwd_preprocess(sets[i][0], sets[i][1], sets[i][2], sl))
+    out["preprocess_kernel"] = {"gbs": round(pre_bytes / (ms * 1e-3) / 1e9, 1),
+                                "frac_of_8tbs": round(pre_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                                "ms_per_launch": round(ms, 5), "bytes_per_launch": pre_bytes,
+                                "input_copies_rotated": copies}
+    del sets
+    if rope_base:
+        rope_bytes = 2.0 * B * S * (Hq + Hkv) * d * 2
+        copies = max(4, math.ceil(3 * MALL_BYTES / (rope_bytes / 2)) + 1)
+        rsets = [(q.clone(), k.clone(), torch.empty_like(q), torch.empty_like(k)) for _ in range(copies)]
+        ms = timed(copies, lambda i: attn.attn_rope(*rsets[i], rope_base))
+        out["rope_kernel"] = {"gbs": round(rope_bytes / (ms * 1e-3) / 1e9, 1),
+                              "frac_of_8tbs": round(rope_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                              "ms_per_launch": round(ms, 5), "bytes_per_launch": rope_bytes,
+                              "input_copies_rotated": copies}
+        del rsets
+    # reference: a plain device copy (torch's copy kernel) of 512 MiB, read
+    # and written once per launch (the pair is larger than the cache)
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device=q.device).fill_(1)
+    dst = torch.empty_like(src)
+    ms = timed(2, lambda i: (dst if i == 0 else src).copy_(src if i == 0 else dst))
+    out["device_copy"] = {"gbs": round(2.0 * n / (ms * 1e-3) / 1e9, 1), "bytes_per_launch": 2.0 * n,
+                          "kernel": "torch copy_ (512 MiB each way)"}
+    del src, dst
+    torch.cuda.synchronize()
+    return out
 
 
 def decode_cpu_baseline(w, inp, budget_s: float):
@@ -511,6 +595,7 @@ def decode_cpu_baseline(w, inp, budget_s: float):
             break
     dt = time.perf_counter() - t0
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{done} of {w.B} sequences of {w.name}, numpy fp32, {dt:.1f} s"}
 
 
@@ -611,6 +696,8 @@ def main():
     ap.add_argument("--decode-layout", choices=("position", "head"), default="position",
                     help="cache storage for --decode: position-major [B,Smax,Hkv,d] or head-major [B,Hkv,Smax,d]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hbm", action="store_true",
+                    help="skip the rotated-input HBM measurement of the preprocess (and RoPE) kernels")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work in cpu_baseline")
     ap.add_argument("--eager", action="store_true",
                     help="time the step as eager launches from Python instead of replays of its captured HIP graph")
