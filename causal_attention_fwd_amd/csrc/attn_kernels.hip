@@ -241,18 +241,28 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, NT>& st, const bf16* Ks, co
     }
 }
 
-template <int D, int NT, int OCC, int W>
+// KS = 2 (small grids): the workgroup's waves form two halves over the same
+// query rows; each pipeline step brings two 64-key tiles, the first half of
+// the waves takes the even tiles, the second half the odd ones, and at the
+// end the second half hands its softmax state (reference maximum, partial
+// row sums, unnormalised O) through LDS to the first, which merges the two
+// by log-sum-exp. Half as many steps per block, twice the waves.
+template <int D, int NT, int OCC, int W, int KS = 1>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fwd_kernel(FwdArgs a) {
   constexpr int BN = 64;
-  constexpr int BM = W * 32 * NT;
+  constexpr int WR = W / KS;  // waves per key half (each owns 32*NT query rows)
+  constexpr int BM = WR * 32 * NT;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
-  constexpr int KVT = TileLayout<D>::template elems<BN>();
+  constexpr int KVT = TileLayout<D>::template elems<KS * BN>();
+  static_assert(KS == 1 || KS == 2, "key split");
   __shared__ __attribute__((aligned(16))) bf16 sK0[KVT], sV0[KVT], sK1[KVT], sV1[KVT];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave_all = threadIdx.x >> 6;
+  const int wave = wave_all % WR;   // row wave
+  const int kh = wave_all / WR;     // key half
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
@@ -274,7 +284,7 @@ void fwd_kernel(FwdArgs a) {
   const int qw = q0 + wave * 32 * NT;
   // causal: key tiles up to the block's last row; bidirectional: all of them
   const int kend = a.causal ? min(q0 + BM, L) : L;
-  const int ntiles = (q0 < L) ? (kend - 1) / BN + 1 : 0;
+  const int ntiles = (q0 < L) ? (kend - 1) / (KS * BN) + 1 : 0;  // pipeline steps of KS tiles
   const int wave_last = min(qw + 32 * NT, L) - 1;  // < qw when the wave is all padding
   const int key_last = a.causal ? wave_last : (wave_last < qw ? -1 : L - 1);  // last key a row of the wave sees
   const float c = a.scale * kLog2e;
@@ -296,23 +306,65 @@ void fwd_kernel(FwdArgs a) {
 
   const KVBuf b0{sK0, sV0, 0}, b1{sK1, sV1, 1};
   auto fetch = [&](int kt, const KVBuf& buf) {
-    tile_load_lds<BN, D, W>(Kb, ks, kt * BN, L, buf.k, wave, lane);
-    tile_load_lds<BN, D, W>(Vb, ks, kt * BN, L, buf.v, wave, lane);
+    tile_load_lds<KS * BN, D, W>(Kb, ks, kt * KS * BN, L, buf.k, wave_all, lane);
+    tile_load_lds<KS * BN, D, W>(Vb, ks, kt * KS * BN, L, buf.v, wave_all, lane);
   };
   auto compute = [&](int kt, const KVBuf& buf) {
-    const int j0 = kt * BN;
+    const int j0 = (kt * KS + kh) * BN;
     if (j0 > key_last) return;
+    // this half's 64-key tile: rows kh*64.. of the step's tile
+    const bf16* Ks = buf.k + kh * TileLayout<D>::template elems<BN>();
+    const bf16* Vs = buf.v + kh * TileLayout<D>::template elems<BN>();
     if ((a.causal && j0 + BN - 1 > qw) || (j0 + BN > L)) {
       int lim[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) lim[t] = (a.causal ? min(qw + t * 32 + l32, L - 1) : L - 1) - j0 - g * 4;
-      fwd_tile<D, NT, true>(st, buf.k, buf.v, lane, c, lim);
+      fwd_tile<D, NT, true>(st, Ks, Vs, lane, c, lim);
     } else {
       const int lim[NT] = {};
-      fwd_tile<D, NT, false>(st, buf.k, buf.v, lane, c, lim);
+      fwd_tile<D, NT, false>(st, Ks, Vs, lane, c, lim);
     }
   };
   tile_pipeline(ntiles, b0, b1, fetch, [](int, const KVBuf&) {}, compute);
+
+  if constexpr (KS == 2) {
+    // the odd-tile half hands its state to the even-tile half over the same
+    // rows (the tile buffers are free after the pipeline's last barrier):
+    // [register][lane] floats, oacc then mu and the partial row sums
+    constexpr int NREG = DT * NT * 16 + 2 * NT;
+    static_assert(NREG * 64 * sizeof(float) <= sizeof(sK0), "merge buffer");
+    float* red = reinterpret_cast<float*>(wave == 0 ? sK0 : wave == 1 ? sV0 : wave == 2 ? sK1 : sV1) + lane;
+    static_assert(WR <= 4, "merge buffers");
+    if (kh == 1) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((t * DT + dt) * 16 + r) * 64] = st.oacc[dt][t][r];
+        red[(DT * NT * 16 + 2 * t) * 64] = st.mu[t];
+        red[(DT * NT * 16 + 2 * t + 1) * 64] = st.lsum[t];
+      }
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float mu_b = red[(DT * NT * 16 + 2 * t) * 64];
+      const float ls_b = red[(DT * NT * 16 + 2 * t + 1) * 64];
+      const float mu = fmaxf(st.mu[t], mu_b);
+      // a half that saw no key has mu = -inf and nothing accumulated
+      const float fa = mu == kNegInf ? 1.f : fast_exp2((st.mu[t] - mu) * c);
+      const float fb = mu == kNegInf ? 0.f : fast_exp2((mu_b - mu) * c);
+      st.lsum[t] = st.lsum[t] * fa + ls_b * fb;
+      st.mu[t] = mu;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          st.oacc[dt][t][r] = st.oacc[dt][t][r] * fa + red[((t * DT + dt) * 16 + r) * 64] * fb;
+    }
+  }
 
   // Epilogue: O = acc / l (bf16), LSE = mu*scale + ln l; padded rows 0 / -inf.
 #pragma unroll
@@ -794,18 +846,25 @@ __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, cons
     }
 }
 
-template <int D, int NT, int OCC, int W>
+// KS = 2 (small grids): as in the forward, two halves of the workgroup's
+// waves take the even and the odd 64-key tiles of the same query rows; the
+// odd half's dQ sums are added to the even half's through LDS at the end.
+template <int D, int NT, int OCC, int W, int KS = 1>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = 64;
-  constexpr int BM = W * 32 * NT;
+  constexpr int WR = W / KS;  // waves per key half (each owns 32*NT query rows)
+  constexpr int BM = WR * 32 * NT;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
-  constexpr int KVT = TileLayout<D>::template elems<BN>();
+  constexpr int KVT = TileLayout<D>::template elems<KS * BN>();
+  static_assert(KS == 1 || KS == 2, "key split");
   __shared__ __attribute__((aligned(16))) bf16 sK0[KVT], sV0[KVT], sK1[KVT], sV1[KVT];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave_all = threadIdx.x >> 6;
+  const int wave = wave_all % WR;   // row wave
+  const int kh = wave_all / WR;     // key half
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
@@ -828,7 +887,7 @@ void bwd_dq_kernel(BwdArgs a) {
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32 * NT;
   const int kend = a.causal ? min(q0 + BM, L) : L;
-  const int ntiles = (q0 < L) ? (kend - 1) / BN + 1 : 0;
+  const int ntiles = (q0 < L) ? (kend - 1) / (KS * BN) + 1 : 0;  // pipeline steps of KS tiles
   const int wave_last = min(qw + 32 * NT, L) - 1;
   const int key_last = a.causal ? wave_last : (wave_last < qw ? -1 : L - 1);
   const float c = a.scale * kLog2e;
@@ -863,7 +922,7 @@ void bwd_dq_kernel(BwdArgs a) {
       }
       const float dsum = xhalf_sum(part);
       st.dd[t] = valid ? dsum : 0.f;
-      if (g == 0 && row < S) a.delta_out[((int64_t)b * a.Hq + h) * S + row] = valid ? dsum : 0.f;
+      if (g == 0 && kh == 0 && row < S) a.delta_out[((int64_t)b * a.Hq + h) * S + row] = valid ? dsum : 0.f;
     } else {
       st.dd[t] = valid ? Db[row] : 0.f;
     }
@@ -886,12 +945,14 @@ void bwd_dq_kernel(BwdArgs a) {
   // K/V tiles stream straight into LDS (no staging registers), double-buffered.
   const KVBuf b0{sK0, sV0, 0}, b1{sK1, sV1, 1};
   auto fetch = [&](int kt, const KVBuf& buf) {
-    tile_load_lds<BN, D, W>(Kb, ks, kt * BN, L, buf.k, wave, lane);
-    tile_load_lds<BN, D, W>(Vb, ks, kt * BN, L, buf.v, wave, lane);
+    tile_load_lds<KS * BN, D, W>(Kb, ks, kt * KS * BN, L, buf.k, wave_all, lane);
+    tile_load_lds<KS * BN, D, W>(Vb, ks, kt * KS * BN, L, buf.v, wave_all, lane);
   };
   auto compute = [&](int kt, const KVBuf& buf) {
-    const int j0 = kt * BN;
+    const int j0 = (kt * KS + kh) * BN;
     if (j0 > key_last) return;
+    const bf16* Ks = buf.k + kh * TileLayout<D>::template elems<BN>();
+    const bf16* Vs = buf.v + kh * TileLayout<D>::template elems<BN>();
     if ((a.causal && j0 + BN - 1 > qw) || (j0 + BN > L) || (qw + 32 * NT > L)) {
       int lim[NT];
 #pragma unroll
@@ -899,13 +960,38 @@ void bwd_dq_kernel(BwdArgs a) {
         const int i = qw + t * 32 + l32;
         lim[t] = i < L ? (a.causal ? i : L - 1) - j0 - g * 4 : -1;
       }
-      dq_tile<D, NT, true>(st, buf.k, buf.v, lane, c, lim);
+      dq_tile<D, NT, true>(st, Ks, Vs, lane, c, lim);
     } else {
       const int lim[NT] = {};
-      dq_tile<D, NT, false>(st, buf.k, buf.v, lane, c, lim);
+      dq_tile<D, NT, false>(st, Ks, Vs, lane, c, lim);
     }
   };
   tile_pipeline(ntiles, b0, b1, fetch, [](int, const KVBuf&) {}, compute);
+
+  if constexpr (KS == 2) {
+    // the odd-tile half adds its dQ sums to the even-tile half's through LDS
+    // (the tile buffers are free after the pipeline's last barrier)
+    constexpr int NREG = DT * NT * 16;
+    static_assert(NREG * 64 * sizeof(float) <= sizeof(sK0), "reduction buffer");
+    static_assert(WR <= 4, "reduction buffers");
+    float* red = reinterpret_cast<float*>(wave == 0 ? sK0 : wave == 1 ? sV0 : wave == 2 ? sK1 : sV1) + lane;
+    if (kh == 1) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((t * DT + dt) * 16 + r) * 64] = st.acc[dt][t][r];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.acc[dt][t][r] += red[((t * DT + dt) * 16 + r) * 64];
+  }
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -1305,8 +1391,9 @@ template <> struct Tiles<128> {
   static constexpr int DQ_NT = 1, DQ_OCC = 2, DQ_W = 4;      // 128-row blocks
   static constexpr int DKDV_NTJ = 1, DKDV_OCC = 1, DKDV_GROUPS = 1;
 };
-// small-grid configurations: 64-row blocks of two waves
-constexpr int kSmallNT = 1, kSmallW = 2;
+// small-grid configurations: 64-row blocks of four waves, two per 64-key
+// tile of each 128-key pipeline step (the key range split in two halves)
+constexpr int kSmallNT = 1, kSmallW = 4, kSmallKS = 2;
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -1341,8 +1428,8 @@ hipError_t fwd_d(const Problem& pr, const void* q, const void* k, const void* v,
   const int64_t wgs = (int64_t)a.nqb * pr.B * pr.Hq;
   if (wgs >= kCUs * (4 * OCC / W))
     return launch((const void*)&fwd_kernel<D, NT, OCC, W>, wgs, a, stream, 64 * W);
-  a.nqb = cdiv(pr.S, 32 * kSmallNT * kSmallW);
-  return launch((const void*)&fwd_kernel<D, kSmallNT, OCC, kSmallW>, (int64_t)a.nqb * pr.B * pr.Hq, a,
+  a.nqb = cdiv(pr.S, 32 * kSmallNT * (kSmallW / kSmallKS));
+  return launch((const void*)&fwd_kernel<D, kSmallNT, OCC, kSmallW, kSmallKS>, (int64_t)a.nqb * pr.B * pr.Hq, a,
                 stream, 64 * kSmallW);
 }
 
@@ -1386,8 +1473,8 @@ hipError_t dq_d(const Problem& pr, const void* q, const void* k, const void* v, 
   const int64_t wgs = (int64_t)a.nblk * pr.B * pr.Hq;
   if (wgs >= kCUs * (4 * OCC / W))
     return launch((const void*)&bwd_dq_kernel<D, NT, OCC, W>, wgs, a, stream, 64 * W);
-  a.nblk = cdiv(pr.S, 32 * kSmallNT * kSmallW);
-  return launch((const void*)&bwd_dq_kernel<D, kSmallNT, OCC, kSmallW>, (int64_t)a.nblk * pr.B * pr.Hq,
+  a.nblk = cdiv(pr.S, 32 * kSmallNT * (kSmallW / kSmallKS));
+  return launch((const void*)&bwd_dq_kernel<D, kSmallNT, OCC, kSmallW, kSmallKS>, (int64_t)a.nblk * pr.B * pr.Hq,
                 a, stream, 64 * kSmallW);
 }
 
