@@ -15,11 +15,7 @@ Prints ONE JSON line on stdout (diagnostics go to stderr). Throughput counts
 algorithmic flops only: 4*d per valid causal (query, key) pair per query head
 forward, 2.5x that backward (five products including the QK^T recompute).
 
-Other modes (measurement tooling, used under rocprofv3):
-    --copy-calibration       run a plain device copy of known size (counter scale)
-    --pmc-summary DIR ...    turn rocprofv3 --pmc outputs into profiles/*_pmc.txt
-    --trace-summary DIR      turn a rocprofv3 --kernel-trace --stats run into profiles/*_trace.txt
-    --sq-summary DIR ...     turn rocprofv3 --pmc runs of SQ counters into profiles/*_sq.txt
+Other modes:
     --decode                 decode attention against a key/value cache instead
                              (workload decode_llama1b; HBM GB/s, one step = one
                              attn_decode call)
@@ -27,7 +23,6 @@ Other modes (measurement tooling, used under rocprofv3):
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -79,181 +74,6 @@ def read_traffic(kernel: str, workload: str):
         return float(fields["traffic_bytes_per_dispatch"])
     except (KeyError, ValueError):
         return None
-
-
-def _pmc_rows(d):
-    import csv
-    rows = []
-    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-        with open(f) as fh:
-            rows += list(csv.DictReader(fh))
-    return rows
-
-
-def _avg_counter(rows, match, counter):
-    vals = {}
-    for r in rows:
-        if match in r.get("Kernel_Name", "") and r.get("Counter_Name") == counter:
-            key = r.get("Dispatch_Id") or r.get("Correlation_Id") or str(len(vals))
-            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
-    return (sum(vals.values()) / len(vals), len(vals)) if vals else (None, 0)
-
-
-def pmc_summary(args):
-    """profiles/<kernel>_<workload>_pmc.txt from four rocprofv3 --pmc runs:
-    FETCH_SIZE and WRITE_SIZE of the bench and of the copy calibration."""
-    fetch = _pmc_rows(args.pmc_summary[0])
-    write = _pmc_rows(args.pmc_summary[1])
-    cfetch = _pmc_rows(args.pmc_summary[2])
-    cwrite = _pmc_rows(args.pmc_summary[3])
-    copy_bytes = float(args.copy_bytes)
-    # the copy kernel reads and writes copy_bytes each; counters are in KiB
-    cf, _ = _avg_counter(cfetch, args.copy_kernel, "FETCH_SIZE")
-    cw, _ = _avg_counter(cwrite, args.copy_kernel, "WRITE_SIZE")
-    f_scale = copy_bytes / (cf * 1024.0)
-    w_scale = copy_bytes / (cw * 1024.0)
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    for key, kname in KERNEL_NAMES.items():
-        fk, n1 = _avg_counter(fetch, kname, "FETCH_SIZE")
-        wk, n2 = _avg_counter(write, kname, "WRITE_SIZE")
-        if fk is None or wk is None:
-            continue
-        traffic = fk * 1024.0 * f_scale + wk * 1024.0 * w_scale
-        path = os.path.join(ROOT, "profiles", f"{kname}_{args.workload}_pmc.txt")
-        with open(path, "w") as out:
-            out.write(f"# HBM traffic of {kname} on workload {args.workload} (rocprofv3 --pmc)\n")
-            out.write(f"# commands: {args.pmc_command}\n")
-            out.write(f"kernel_source_sha256_16: {kernel_source_sha()}\n")
-            out.write(f"dispatches_fetch: {n1}\ndispatches_write: {n2}\n")
-            out.write(f"fetch_kib_per_dispatch: {fk:.1f}\nwrite_kib_per_dispatch: {wk:.1f}\n")
-            out.write(f"copy_bytes: {copy_bytes:.0f}\n")
-            out.write(f"copy_fetch_kib: {cf:.1f}\ncopy_write_kib: {cw:.1f}\n")
-            out.write(f"scale_fetch: {f_scale:.4f}\nscale_write: {w_scale:.4f}\n")
-            out.write(f"traffic_bytes_per_dispatch: {traffic:.0f}\n")
-        log(f"wrote {path}: {traffic / 1e6:.1f} MB per dispatch")
-
-
-def sq_summary(args):
-    """profiles/<kernel>_<workload>_sq.txt from rocprofv3 --pmc runs of SQ
-    counters (any split over runs), averaged per dispatch, with the derived
-    utilisation figures: MFMA busy and VALU active per SIMD (the SQ counters
-    sum over SIMDs and count quad-cycles where noted), GRBM_GUI_ACTIVE summed
-    over the 8 XCDs."""
-    rows = []
-    for d in args.sq_summary:
-        rows += _pmc_rows(d)
-    counters = sorted({r["Counter_Name"] for r in rows})
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    for kname in KERNEL_NAMES.values():
-        vals = {}
-        for c in counters:
-            v, n = _avg_counter(rows, kname, c)
-            if v is not None:
-                vals[c] = (v, n)
-        if not vals:
-            continue
-        path = os.path.join(ROOT, "profiles", f"{kname}_{args.workload}_sq.txt")
-        with open(path, "w") as out:
-            out.write(f"# SQ counters of {kname} on workload {args.workload} (per dispatch, mean over dispatches)\n")
-            out.write(f"# commands: {args.pmc_command}\n")
-            out.write(f"kernel_source_sha256_16: {kernel_source_sha()}\n")
-            for c, (v, n) in vals.items():
-                out.write(f"{c}: {v:.6g}  ({n} dispatches)\n")
-            simds, xcds = 1024, 8
-            if "GRBM_GUI_ACTIVE" in vals:
-                cyc = vals["GRBM_GUI_ACTIVE"][0] / xcds
-                out.write(f"elapsed_cycles_per_xcd: {cyc:.0f}\n")
-                if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
-                    out.write(f"mfma_busy_fraction: {vals['SQ_VALU_MFMA_BUSY_CYCLES'][0] / (cyc * simds):.3f}\n")
-                if "SQ_ACTIVE_INST_VALU" in vals:  # quad-cycles
-                    out.write(f"valu_active_fraction: {4 * vals['SQ_ACTIVE_INST_VALU'][0] / (cyc * simds):.3f}\n")
-                if "SQ_LDS_IDX_ACTIVE" in vals:
-                    out.write(f"lds_active_fraction_per_cu: {vals['SQ_LDS_IDX_ACTIVE'][0] / (cyc * 256):.3f}\n")
-            if "SQ_INSTS_MFMA" in vals:
-                out.write(f"mfma_flop_executed: {vals['SQ_INSTS_MFMA'][0] * 32768:.4g}  (32x32x16 bf16 = 32768 flop each)\n")
-        log(f"wrote {path}")
-
-
-def trace_summary(args):
-    """profiles/<kernel>_<workload>_trace.txt from a rocprofv3 --kernel-trace --stats run."""
-    import csv
-    from attn_workloads import DECODE_WORKLOADS, WORKLOADS, algorithmic_flops, workload_inputs
-    if args.workload in DECODE_WORKLOADS:
-        return decode_trace_summary(args)
-    w = WORKLOADS[args.workload]
-    seqlens = workload_inputs(w).seqlens if w.padded else None
-    fl = algorithmic_flops(w, seqlens)
-    share = {"fwd_kernel": fl["fwd"], "bwd_dkdv_kernel": fl["bwd_dkdv"], "bwd_dq_kernel": fl["bwd_dq"]}
-    B, S, Hq, d = w.B, w.S, w.Hq, w.d
-    pre_bytes = 2.0 * B * S * Hq * d * 2 + B * Hq * S * 4.0
-    files = glob.glob(os.path.join(args.trace_summary, "**", "*kernel_stats.csv"), recursive=True)
-    if not files:
-        sys.exit(f"no kernel_stats.csv under {args.trace_summary}")
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    for row in csv.DictReader(open(files[0])):
-        kname = next((k for k in KERNEL_NAMES.values() if k in row["Name"]), None)
-        if kname is None:
-            continue
-        avg_us = float(row["AverageNs"]) / 1e3
-        path = os.path.join(ROOT, "profiles", f"{kname}_{w.name}_trace.txt")
-        with open(path, "w") as out:
-            out.write(f"# rocprofv3 kernel-trace summary: {kname} on workload {w.name} {w.describe()}\n")
-            out.write(f"# command: {args.pmc_command}\n")
-            out.write(f"kernel: {row['Name']}\n")
-            out.write(f"kernel_source_sha256_16: {kernel_source_sha()}\n")
-            out.write(f"calls: {row['Calls']}\n")
-            out.write(f"average_us: {avg_us:.2f}\nmin_us: {float(row['MinNs']) / 1e3:.2f}\n"
-                      f"max_us: {float(row['MaxNs']) / 1e3:.2f}\n")
-            if kname in share:
-                out.write(f"algorithmic_gflop_per_launch: {share[kname] / 1e9:.3f}\n")
-                out.write(f"achieved_tflops_at_average: {share[kname] / (avg_us * 1e-6) / 1e12:.1f}\n")
-            else:
-                out.write(f"algorithmic_bytes_per_launch: {pre_bytes:.0f}\n")
-                out.write(f"achieved_gbs_at_average: {pre_bytes / (avg_us * 1e-6) / 1e9:.1f}\n")
-        log(f"wrote {path}: {avg_us:.1f} us")
-
-
-def decode_trace_summary(args):
-    import csv
-    from attn_workloads import DECODE_WORKLOADS, decode_bytes, decode_workload_inputs
-    w = DECODE_WORKLOADS[args.workload]
-    nb = decode_bytes(w.B, w.Sq, w.Smax, w.Hq, w.Hkv, w.d, decode_workload_inputs(w).cache_lens)
-    alg = {"decode_split_kernel": nb["cache"] + w.B * w.Sq * w.Hq * w.d * 2,
-           "decode_merge_kernel": w.B * w.Sq * w.Hq * (w.d * 2 + 4)}
-    files = glob.glob(os.path.join(args.trace_summary, "**", "*kernel_stats.csv"), recursive=True)
-    if not files:
-        sys.exit(f"no kernel_stats.csv under {args.trace_summary}")
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    for row in csv.DictReader(open(files[0])):
-        kname = next((k for k in alg if k in row["Name"]), None)
-        if kname is None:
-            continue
-        avg_us = float(row["AverageNs"]) / 1e3
-        path = os.path.join(ROOT, "profiles", f"{kname}_{w.name}_trace.txt")
-        with open(path, "w") as out:
-            out.write(f"# rocprofv3 kernel-trace summary: {kname} on workload {w.name} {w.describe()}\n")
-            out.write(f"# command: {args.pmc_command}\n")
-            out.write(f"kernel: {row['Name']}\n")
-            out.write(f"kernel_source_sha256_16: {kernel_source_sha()}\n")
-            out.write(f"calls: {row['Calls']}\n")
-            out.write(f"average_us: {avg_us:.2f}\nmin_us: {float(row['MinNs']) / 1e3:.2f}\n"
-                      f"max_us: {float(row['MaxNs']) / 1e3:.2f}\n")
-            out.write(f"algorithmic_bytes_per_launch: {alg[kname]:.0f}\n")
-            out.write(f"achieved_gbs_at_average: {alg[kname] / (avg_us * 1e-6) / 1e9:.1f}\n")
-        log(f"wrote {path}: {avg_us:.1f} us")
-
-
-# ----------------------------------------------------------------------------- copy calibration
-
-def copy_calibration(args):
-    import torch
-    n = int(args.copy_bytes)
-    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
-    dst = torch.empty_like(src)
-    for _ in range(5):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": n, "copies": 5}))
 
 
 # ----------------------------------------------------------------------------- the benchmark
@@ -710,13 +530,6 @@ def main():
     ap.add_argument("--rope", action="store_true",
                     help="rotary position embedding: attn_rope pre-pass, backward with the fused adjoint")
     ap.add_argument("--rope-base", type=float, default=10000.0)
-    ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--copy-bytes", type=float, default=1 << 30)
-    ap.add_argument("--copy-kernel", default="copy")
-    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
-    ap.add_argument("--sq-summary", nargs="+", metavar="DIR")
-    ap.add_argument("--pmc-command", default="", help="command line recorded in the written summaries")
-    ap.add_argument("--trace-summary", metavar="TRACE_DIR")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -725,15 +538,7 @@ def main():
         sys.exit(2)
     if args.workload is None:
         args.workload = "decode_llama1b" if args.decode else "llama1b"
-    if args.pmc_summary:
-        pmc_summary(args)
-    elif args.trace_summary:
-        trace_summary(args)
-    elif args.sq_summary:
-        sq_summary(args)
-    elif args.copy_calibration:
-        copy_calibration(args)
-    elif args.decode:
+    if args.decode:
         run_decode(args)
     else:
         run(args)
