@@ -125,6 +125,16 @@ struct BwdArgs {
 
 constexpr int kThreads = 256;  // four waves, one per SIMD
 
+// LDS fragment read-ahead of the backward tiles, in product steps: the
+// scheduling groups below put the reads of step i + PF beside the products of
+// step i (0 leaves the order to the compiler; the d=64 dQ pass, at three waves
+// per SIMD, has no registers to spare for it)
+constexpr int kDkdvReadAhead = 4;
+template <int D>
+constexpr int kDqReadAhead = D == 128 ? 2 : 0;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
 // Wave priority 1 while a wave issues its first run of MFMAs, so that the pipe
 // is refilled promptly while a sibling wave on the same SIMD runs VALU work;
 // back to 0 afterwards.
@@ -459,18 +469,31 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
       dp[m2][t] = nd;
     }
   }
+  // S and dP: step i = (kk, m2) = (i / 2, i % 2) takes one Q and one dO
+  // fragment. The reads run PF steps ahead of the products that use them, so
+  // that a product never waits for a read issued just before it.
+  constexpr int NS = 2 * KK;
+  bf16x8 aq[NS], ad[NS];
   prio_mfma();
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
+  for (int i = 0; i < NS; ++i) {
+    aq[i] = frag_row<D>(Qs, (i & 1) * 32, (i >> 1) * 16, lane);
+    ad[i] = frag_row<D>(dOs, (i & 1) * 32, (i >> 1) * 16, lane);
+  }
 #pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-      const bf16x8 aq = frag_row<D>(Qs, m2 * 32, kk * 16, lane);
-      const bf16x8 ad = frag_row<D>(dOs, m2 * 32, kk * 16, lane);
+  for (int i = 0; i < NS; ++i)
 #pragma unroll
-      for (int t = 0; t < NTJ; ++t) {
-        s[m2][t] = mfma32(aq, st.kf[t][kk], s[m2][t]);
-        dp[m2][t] = mfma32(ad, st.vf[t][kk], dp[m2][t]);
-      }
+    for (int t = 0; t < NTJ; ++t) {
+      s[i & 1][t] = mfma32(aq[i], st.kf[t][i >> 1], s[i & 1][t]);
+      dp[i & 1][t] = mfma32(ad[i], st.vf[t][i >> 1], dp[i & 1][t]);
+    }
+  if constexpr (kDkdvReadAhead > 0) {
+    constexpr int PF = kDkdvReadAhead;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PF, 0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * NTJ, 0);
+      if (i + PF < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
   }
   prio_base();
@@ -506,18 +529,31 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
       pb[u][t] = pack8(s[u >> 1][t], (u & 1) * 8);
       sb[u][t] = pack8(dp[u >> 1][t], (u & 1) * 8);
     }
+  // dV and dK: step i = (ct, u) = (i / 4, i % 4), two transposed fragments
+  // (two reads each), the same read-ahead
+  constexpr int NT2 = 4 * DT;
+  bf16x8 tdo[NT2], tq[NT2];
 #pragma unroll
-  for (int ct = 0; ct < DT; ++ct)
+  for (int i = 0; i < NT2; ++i) {
+    tdo[i] = frag_tr<D>(dOs, (i & 3) * 16, (i >> 2) * 32, lane);
+    tq[i] = frag_tr<D>(Qs, (i & 3) * 16, (i >> 2) * 32, lane);
+  }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bf16x8 ado = frag_tr<D>(dOs, u * 16, ct * 32, lane);
-      const bf16x8 aq = frag_tr<D>(Qs, u * 16, ct * 32, lane);
+  for (int i = 0; i < NT2; ++i)
 #pragma unroll
-      for (int t = 0; t < NTJ; ++t) {
-        st.dv[ct][t] = mfma32(ado, pb[u][t], st.dv[ct][t]);
-        st.dk[ct][t] = mfma32(aq, sb[u][t], st.dk[ct][t]);
-      }
+    for (int t = 0; t < NTJ; ++t) {
+      st.dv[i >> 2][t] = mfma32(tdo[i], pb[i & 3][t], st.dv[i >> 2][t]);
+      st.dk[i >> 2][t] = mfma32(tq[i], sb[i & 3][t], st.dk[i >> 2][t]);
     }
+  if constexpr (kDkdvReadAhead > 0) {
+    constexpr int PF = kDkdvReadAhead;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * PF, 1);
+#pragma unroll
+    for (int i = 0; i < NT2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * NTJ, 1);
+      if (i + PF < NT2) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
+    }
+  }
 }
 
 // GROUPS = 1: four waves. GROUPS = 2: eight waves in two groups of four that
@@ -806,18 +842,30 @@ __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, cons
       s[mt][t] = zero16();
       dp[mt][t] = mfma32(st.ones, st.nd[t], zero16());  // every row: -D of the lane's query
     }
+  // step i = (kk, mt) = (i / 2, i % 2): one K and one V fragment, read
+  // ahead of the products as in the dK/dV tile
+  constexpr int NS = 2 * KK;
+  bf16x8 ak[NS], av[NS];
   prio_mfma();
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
+  for (int i = 0; i < NS; ++i) {
+    ak[i] = frag_row<D>(Ks, (i & 1) * 32, (i >> 1) * 16, lane);
+    av[i] = frag_row<D>(Vs, (i & 1) * 32, (i >> 1) * 16, lane);
+  }
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const bf16x8 ak = frag_row<D>(Ks, mt * 32, kk * 16, lane);
-      const bf16x8 av = frag_row<D>(Vs, mt * 32, kk * 16, lane);
+  for (int i = 0; i < NS; ++i)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        s[mt][t] = mfma32(ak, st.qf[t][kk], s[mt][t]);
-        dp[mt][t] = mfma32(av, st.df[t][kk], dp[mt][t]);
-      }
+    for (int t = 0; t < NT; ++t) {
+      s[i & 1][t] = mfma32(ak[i], st.qf[t][i >> 1], s[i & 1][t]);
+      dp[i & 1][t] = mfma32(av[i], st.df[t][i >> 1], dp[i & 1][t]);
+    }
+  if constexpr (kDqReadAhead<D> > 0) {
+    constexpr int PF = kDqReadAhead<D>;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PF, 0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * NT, 0);
+      if (i + PF < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
   }
   prio_base();
@@ -836,14 +884,23 @@ __device__ __forceinline__ void dq_tile(DqState<D, NT>& st, const bf16* Ks, cons
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int t = 0; t < NT; ++t) sb[u][t] = pack8(dp[u >> 1][t], (u & 1) * 8);
+  constexpr int NT2 = 4 * DT;
+  bf16x8 tk[NT2];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int i = 0; i < NT2; ++i) tk[i] = frag_tr<D>(Ks, (i & 3) * 16, (i >> 2) * 32, lane);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bf16x8 ak = frag_tr<D>(Ks, u * 16, dt * 32, lane);
+  for (int i = 0; i < NT2; ++i)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) st.acc[dt][t] = mfma32(ak, sb[u][t], st.acc[dt][t]);
+    for (int t = 0; t < NT; ++t) st.acc[i >> 2][t] = mfma32(tk[i], sb[i & 3][t], st.acc[i >> 2][t]);
+  if constexpr (kDqReadAhead<D> > 0) {
+    constexpr int PF = kDqReadAhead<D>;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PF, 1);
+#pragma unroll
+    for (int i = 0; i < NT2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NT, 1);
+      if (i + PF < NT2) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
     }
+  }
 }
 
 // KS = 2 (small grids): as in the forward, two halves of the workgroup's
