@@ -474,6 +474,15 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
   // that a product never waits for a read issued just before it.
   constexpr int NS = 2 * KK;
   bf16x8 aq[NS], ad[NS];
+  // d=128 (one wave per SIMD, registers to spare): the tile's 64 LSE values
+  // are read here, so that the softmax below never waits on LDS for them
+  float4 l2all[2][4];
+  if constexpr (D == 128) {
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) l2all[m2][rr] = *reinterpret_cast<const float4*>(lse2 + m2 * 32 + rr * 8 + g * 4);
+  }
   prio_mfma();
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -504,7 +513,9 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int il0 = m2 * 32 + rr * 8 + g * 4;
-      const float4 l2 = *reinterpret_cast<const float4*>(lse2 + il0);
+      float4 l2;
+      if constexpr (D == 128) l2 = l2all[m2][rr];
+      else l2 = *reinterpret_cast<const float4*>(lse2 + il0);
       const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -573,7 +584,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
       sO1[GROUPS * TILE];
   __shared__ __attribute__((aligned(16))) float sstat[GROUPS][2][2][BMQ];  // [group][buf][LSE*log2e, -D]
 
-  const int grp = wave_id() >> 2;
+  // a compile-time 0 with one group: the stage buffers are then the arrays
+  // themselves, and the compiler can tell the tile being read from the one
+  // the next tile's copy is landing in (otherwise it waits for that copy in
+  // the middle of the tile)
+  const int grp = GROUPS == 1 ? 0 : wave_id() >> 2;
   const int swave = wave_id() & 3;  // wave within the group, in a scalar register
   const int gtid = threadIdx.x & (kThreads - 1);
   const int lane = threadIdx.x & 63;
