@@ -123,9 +123,12 @@ __device__ __forceinline__ bf16x8 frag_tr(const bf16* tile, int row0, int col0, 
   const int c = (col0 >> 3) + 2 * b4 + ((s & 3) >> 1);   // chunk
   const int h = (((col0 >> 4) + b4) & 1) << 2;            // h(c): c/2 = col0/16 + b4
   const int x = (((lane >> 5) << 2) + (s >> 2)) ^ h;      // row within the block, swizzled
-  const bf16* p = tile + (row0 >> 3) * BE + (c * 8 + x) * 8 + (s & 1) * 4;
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + BE));
+  // both addresses from the tile base: written as the first plus one block,
+  // the second read lost track of its LDS array in the compiler, which then
+  // waited for every in-flight tile copy before it
+  const int lo_off = (c * 8 + x) * 8 + (s & 1) * 4;
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + (row0 >> 3) * BE + lo_off));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + ((row0 >> 3) + 1) * BE + lo_off));
   s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
