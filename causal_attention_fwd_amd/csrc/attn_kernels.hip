@@ -125,13 +125,16 @@ struct BwdArgs {
 
 constexpr int kThreads = 256;  // four waves, one per SIMD
 
-// LDS fragment read-ahead of the backward tiles, in product steps: the
-// scheduling groups below put the reads of step i + PF beside the products of
-// step i (0 leaves the order to the compiler; the d=64 dQ pass, at three waves
-// per SIMD, has no registers to spare for it)
+// LDS fragment read-ahead, in product steps: scheduling groups put the reads
+// of step i + PF beside the products of step i, so that a product does not
+// wait for a read issued just before it. 0 leaves the order to the compiler:
+// the d=64 dQ pass (three waves per SIMD) has no registers to spare for it,
+// and the d=64 forward measured the same either way.
 constexpr int kDkdvReadAhead = 4;
 template <int D>
 constexpr int kDqReadAhead = D == 128 ? 2 : 0;
+template <int D>
+constexpr int kFwdReadAhead = D == 128 ? 2 : 0;
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
@@ -183,13 +186,21 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, NT>& st, const bf16* Ks, co
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int t = 0; t < NT; ++t) s[mt][t] = zero16();
+  constexpr int NS = 2 * KK;  // step i = (kk, mt) = (i / 2, i % 2)
+  bf16x8 kf[NS];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
+  for (int i = 0; i < NS; ++i) kf[i] = frag_row<D>(Ks, (i & 1) * 32, (i >> 1) * 16, lane);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const bf16x8 af = frag_row<D>(Ks, mt * 32, kk * 16, lane);
+  for (int i = 0; i < NS; ++i)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) s[mt][t] = mfma32(af, st.qf[t][kk], s[mt][t]);
+    for (int t = 0; t < NT; ++t) s[i & 1][t] = mfma32(kf[i], st.qf[t][i >> 1], s[i & 1][t]);
+  if constexpr (kFwdReadAhead<D> > 0) {
+    constexpr int PF = kFwdReadAhead<D>;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NT, 0);
+      if (i + PF < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
   }
   if (MASK) {
@@ -241,14 +252,23 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, NT>& st, const bf16* Ks, co
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int t = 0; t < NT; ++t) pb[u][t] = pack8(s[u >> 1][t], (u & 1) * 8);
+  constexpr int NT2 = 4 * DT;  // step i = (dt, u) = (i / 4, i % 4)
+  bf16x8 vf[NT2];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int i = 0; i < NT2; ++i) vf[i] = frag_tr<D>(Vs, (i & 3) * 16, (i >> 2) * 32, lane);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bf16x8 af = frag_tr<D>(Vs, u * 16, dt * 32, lane);
+  for (int i = 0; i < NT2; ++i)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) st.oacc[dt][t] = mfma32(af, pb[u][t], st.oacc[dt][t]);
+    for (int t = 0; t < NT; ++t) st.oacc[i >> 2][t] = mfma32(vf[i], pb[i & 3][t], st.oacc[i >> 2][t]);
+  if constexpr (kFwdReadAhead<D> > 0) {
+    constexpr int PF = kFwdReadAhead<D>;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PF, 1);
+#pragma unroll
+    for (int i = 0; i < NT2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NT, 1);
+      if (i + PF < NT2) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
     }
+  }
 }
 
 // KS = 2 (small grids): the workgroup's waves form two halves over the same
