@@ -101,3 +101,61 @@ def compare(gpu, ref, label=""):
     assert rel <= TOL_REL_FRO, f"{label} D: rel_fro={rel:.3e}"
     say(f"  {label}: " + "  ".join(f"{k} rel={v[0]:.2e} max={v[1]:.2e}" for k, v in report.items()))
     return report
+
+
+def whole_output_identities(inp, gpu, causal=True, label=""):
+    """Checks over every (sequence, kv head) unit at any size, on the GPU's
+    outputs (host arrays) in fp64:
+      * D_i = sum_c dO_ic O_ic from the GPU's own bf16 O (to fp32 summation);
+      * every O row lies in the range of the V rows it sees (prefix for
+        causal), widened by the bf16 roundings of P and O;
+      * sum_j dV_j = sum over the group's heads of sum_i dO_i, and
+        sum_j dK_j = 0 (every valid row of P sums to one and sum_j dS_ij = 0),
+        within a multiple of the bf16 rounding noise.
+    A skipped or repeated tile, a wrong mask, LSE or D breaks one of them."""
+    q, k, v, do, sl = host_inputs(inp)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    O, D, dK, dV = (np.asarray(gpu[n], dtype=np.float64) for n in ("O", "D", "dK", "dV"))
+    worst = {"D": 0.0, "O": 0.0, "dV": 0.0, "dK": 0.0}
+    for b in range(B):
+        L = int(sl[b]) if sl is not None else S
+        if L == 0:
+            continue
+        dob = do[b, :L].astype(np.float64)                     # [L, Hq, d]
+        ob = O[b, :L]
+        prod = dob * ob
+        dref = prod.sum(axis=-1).T                              # [Hq, L]
+        dtol = 1e-5 * np.abs(prod).sum(axis=-1).T + 1e-30
+        err = np.abs(D[b, :, :L] - dref)
+        assert np.all(err <= dtol), f"{label} D: b={b} max err {err.max():.3e}"
+        worst["D"] = max(worst["D"], float((err / dtol).max()))
+        for g in range(Hkv):
+            vb = v[b, :L, g].astype(np.float64)                 # [L, d]
+            if causal:
+                hi, lo = np.maximum.accumulate(vb, axis=0), np.minimum.accumulate(vb, axis=0)
+            else:
+                hi, lo = np.broadcast_to(vb.max(axis=0), vb.shape), np.broadcast_to(vb.min(axis=0), vb.shape)
+            tol = 2.0 ** -7 * float(np.abs(vb).max())
+            hs = slice(g * G, (g + 1) * G)
+            og = ob[:, hs]                                      # [L, G, d]
+            over = max(float((og - hi[:, None]).max()), float((lo[:, None] - og).max()))
+            assert over <= tol, f"{label} O outside the range of its visible V rows: b={b} g={g} by {over:.3e}"
+            worst["O"] = max(worst["O"], over / tol)
+            sdv = dV[b, :L, g].sum(axis=0)
+            sdo = dob[:, hs].sum(axis=(0, 1))
+            noise_v = (np.linalg.norm(dV[b, :L, g]) + np.linalg.norm(dob[:, hs])) * 2.0 ** -7
+            ev = float(np.linalg.norm(sdv - sdo))
+            assert ev <= noise_v, f"{label} sum dV != sum dO: b={b} g={g} {ev:.3e} > {noise_v:.3e}"
+            worst["dV"] = max(worst["dV"], ev / noise_v)
+            sdk = dK[b, :L, g].sum(axis=0)
+            dterm = np.abs(prod[:, hs]).sum(axis=-1) * 2.0 ** -9          # [L, G]
+            qn2 = (q[b, :L, hs].astype(np.float64) ** 2).sum(axis=-1)      # [L, G]
+            noise_k = np.linalg.norm(dK[b, :L, g]) * 2.0 ** -7 + 4 * inp.scale * np.sqrt((dterm ** 2 * qn2).sum())
+            ek = float(np.linalg.norm(sdk))
+            assert ek <= noise_k, f"{label} sum dK != 0: b={b} g={g} {ek:.3e} > {noise_k:.3e}"
+            worst["dK"] = max(worst["dK"], ek / noise_k)
+    say(f"  {label} identities over every unit (largest fraction of its bound): "
+        + "  ".join(f"{k} {v:.2f}" for k, v in worst.items()))
+

@@ -3,8 +3,9 @@
 Small shapes are compared element by element over every output; the five
 named workloads run at their full sizes, in the launch configuration the
 benchmark times, and are compared on whole (sequence, kv head) units sampled
-from the batch, plus properties that hold at any size (padding zeros, no
-NaN/Inf).
+from the batch (every kv head and sequence of llama1b), plus properties that
+hold at any size over every unit (padding zeros, no NaN/Inf, D from the GPU's
+O, O within the range of its visible V rows, the gradient sum identities).
 """
 import numpy as np
 import pytest
@@ -13,7 +14,7 @@ import torch
 import causal_attention_fwd_amd as attn
 from attn_workloads import WORKLOADS, make_inputs, workload_inputs
 
-from parity import compare, host_inputs, oracle_unit, run_gpu, say, slice_unit, to_gpu
+from parity import compare, host_inputs, oracle_unit, run_gpu, say, slice_unit, to_gpu, whole_output_identities
 
 import oracle
 
@@ -66,16 +67,18 @@ def test_zero_length_sequences():
 # ------------------------------------------------------------------ the five workloads at full size
 
 def _units(w, inp):
-    """(b, kv head) units compared against the oracle for a workload."""
+    """(b, kv head) units compared against the oracle for a workload (every
+    unit also meets the identities of whole_output_identities)."""
     if w.name in ("tiny", "gqa124m"):
         return None  # every unit
     if w.name == "llama1b":
-        return [(0, 0), (3, 7), (2, 5)]
+        # every kv head and every sequence at least once
+        return sorted({(g % w.B, g) for g in range(w.Hkv)} | {(0, 0), (3, 7), (2, 5)})
     if w.name == "padded":
         L = inp.seqlens.tolist()
-        return [(int(np.argmin(L)), 0), (int(np.argmax(L)), 15), (3, 9)]
+        return sorted({(int(np.argmin(L)), 0), (int(np.argmax(L)), 15)} | {(b, (5 * b + 3) % w.Hkv) for b in range(w.B)})
     if w.name == "longseq":
-        return [(0, 5)]
+        return [(0, 0), (0, 5)]
     raise KeyError(w.name)
 
 
@@ -101,6 +104,7 @@ def test_workload_parity(name):
     # properties over the whole output
     for key in ("O", "dQ", "dK", "dV", "D"):
         assert np.all(np.isfinite(gpu[key])), key
+    whole_output_identities(inp, gpu, label=name)
     if inp.seqlens is not None:
         for b, L in enumerate(inp.seqlens.tolist()):
             for key in ("O", "dQ", "dK", "dV"):
