@@ -6,6 +6,10 @@ attn_fwd -> attn_bwd_preprocess -> attn_bwd_dkdv -> attn_bwd_dq (the last two
 are exactly the two launches attn_bwd makes). The step is timed as replays of
 its captured HIP graph (no host-side launch cost; --eager times Python-issued
 launches instead); per-kernel times come from an eager pass with HIP events.
+Before anything is measured the step runs untimed for --clock-warmup-ms
+(default 250 ms; again as graph replays after the capture, which leaves the
+GPU idle; both reported as "clock_warmup"), then the --warmup steps: an idle
+GPU runs its first tens of milliseconds of MFMA work at a lower clock.
 Default workload: the 1B-class Llama attention, B=4, S=2048, Hq=32, Hkv=8,
 d=64, dO ~ N(0, 0.1).
 
@@ -146,6 +150,23 @@ def cpu_baseline(w, inp, budget_s: float, causal: bool = True, rope_base: float 
                       f"forward alone on the same units, {dtf:.1f} s"}
 
 
+def clock_warmup(torch, step, ms):
+    """Run the step, untimed, for about `ms` milliseconds before anything is
+    measured: a GPU that has been idle runs its first tens of milliseconds of
+    MFMA work at a lower clock (the llama1b step takes 0.399-0.405 ms after a
+    few warm-up steps and 0.366-0.369 ms after ~200 ms of work). Returns what
+    was run, for the JSON line."""
+    if ms <= 0:
+        return {"ms": 0.0, "steps": 0}
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for i in range(10):
+            step(n + i)
+        torch.cuda.synchronize()
+        n += 10
+    return {"ms": round((time.perf_counter() - t0) * 1e3, 1), "steps": n}
+
+
 def time_graph_replays(torch, makers, args):
     """Capture one HIP graph per maker, replay them in turn (warm-up, then the
     timed steps between synchronisations) and return ms per step; None when a
@@ -156,6 +177,8 @@ def time_graph_replays(torch, makers, args):
         log(f"graph capture failed ({type(e).__name__}: {e}); timing the eager launches instead")
         torch.cuda.synchronize()
         return None
+    # the capture left the GPU idle: warm its clock up again on the replays
+    args.graph_clock_warmup = clock_warmup(torch, lambda i: graphs[i % len(graphs)].replay(), args.clock_warmup_ms)
     for i in range(args.warmup):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
@@ -225,6 +248,7 @@ def run(args):
             if ev is not None:
                 ev[4].record()
 
+    warm = clock_warmup(torch, lambda i: step(), args.clock_warmup_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -300,6 +324,7 @@ def run(args):
                        algorithmic_gflop_per_step=round(fl["total"] / 1e9, 3),
                        rope_base=rb if args.rope else None),
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "clock_warmup": {"before_eager_pass": warm, "before_graph_timing": getattr(args, "graph_clock_warmup", None)},
         "step_event_ms": step_stats,
         "kernel_ms": dict({KERNEL_NAMES[n]: round(per[n], 4) for n in names} if not args.fused_bwd else
                           {"fwd_kernel": round(per["fwd"], 4),
@@ -458,6 +483,7 @@ def run_decode(args):
         if ev is not None:
             ev[1].record()
 
+    warm = clock_warmup(torch, step, args.clock_warmup_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -496,6 +522,7 @@ def run_decode(args):
                        cache_layout="[B,Hkv,Smax,d]" if args.decode_layout == "head" else "[B,Smax,Hkv,d]",
                        algorithmic_bytes_per_step=nb["total"]),
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "clock_warmup": {"before_eager_pass": warm, "before_graph_timing": getattr(args, "graph_clock_warmup", None)},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
@@ -519,6 +546,9 @@ def main():
     ap.add_argument("--no-hbm", action="store_true",
                     help="skip the rotated-input HBM measurement of the preprocess (and RoPE) kernels")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work in cpu_baseline")
+    ap.add_argument("--clock-warmup-ms", type=float, default=250.0,
+                    help="untimed runs of the step for this long before anything is measured, so that the GPU "
+                         "runs at its sustained clock (0: only the --warmup steps)")
     ap.add_argument("--eager", action="store_true",
                     help="time the step as eager launches from Python instead of replays of its captured HIP graph")
     ap.add_argument("--graph", action="store_true",
