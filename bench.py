@@ -252,6 +252,20 @@ def run(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    g_step = None
+    launch = "eager"
+    if not args.eager:
+        # the same launches captured in one HIP graph and replayed (the
+        # default: no host-side launch cost in the timed step)
+        def capture():
+            return attn.capture_step(q, k, v, do, o, lse, delta, dq, dk, dv, scale, sl, causal, ws,
+                                     fused=args.fused_bwd, rope_base=rb, q_rot=qa if args.rope else None,
+                                     k_rot=ka if args.rope else None)
+        g_step = time_graph_replays(torch, [capture], args)
+        launch = "hip graph" if g_step is not None else "eager (graph capture failed)"
+    # per-kernel times: an eager pass with HIP events on the library's stream,
+    # right after the timed replays so that the GPU is still at its sustained
+    # clock (with --eager it is the timed region itself)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -273,22 +287,9 @@ def run(args):
     step_stats = {"median": round(step_ev[len(step_ev) // 2], 4), "min": round(step_ev[0], 4),
                   "p90": round(step_ev[min(len(step_ev) - 1, (9 * len(step_ev)) // 10)], 4)}
     ms_step = wall * 1e3 / args.steps
-    launch = "eager"
-    if not args.eager:
-        # the same launches captured in one HIP graph and replayed (the
-        # default: no host-side launch cost in the timed step); the per-kernel
-        # times above stay those of the eager launches
-        def capture():
-            return attn.capture_step(q, k, v, do, o, lse, delta, dq, dk, dv, scale, sl, causal, ws,
-                                     fused=args.fused_bwd, rope_base=rb, q_rot=qa if args.rope else None,
-                                     k_rot=ka if args.rope else None)
-        g_step = time_graph_replays(torch, [capture], args)
-        if g_step is None:
-            launch = "eager (graph capture failed)"
-        else:
-            log(f"eager step {ms_step:.4f} ms, graph step {g_step:.4f} ms")
-            ms_step = g_step
-            launch = "hip graph"
+    if g_step is not None:
+        log(f"eager step {ms_step:.4f} ms, graph step {g_step:.4f} ms")
+        ms_step = g_step
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
 
     # roofline of the dominant kernel
