@@ -31,6 +31,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -40,7 +41,8 @@ sys.path.insert(0, ROOT)
 METRIC = "causal bf16 attention fwd+bwd TFLOP/s and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak (2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-KERNEL_SOURCES = ["causal_attention_fwd_amd/csrc/attn_kernels.hip", "causal_attention_fwd_amd/csrc/attn_common.h"]
+KERNEL_SOURCES = ["causal_attention_fwd_amd/csrc/attn_kernels.hip", "causal_attention_fwd_amd/csrc/attn_common.h",
+                  "causal_attention_fwd_amd/csrc/attn_launch.h", "causal_attention_fwd_amd/csrc/attn_plan.cpp"]
 KERNEL_NAMES = {"fwd": "fwd_kernel", "pre": "preprocess_kernel", "dkdv": "bwd_dkdv_kernel", "dq": "bwd_dq_kernel",
                 "dsplit": "decode_split_kernel", "dmerge": "decode_merge_kernel"}
 DECODE_METRIC = "decode attention over a bf16 key/value cache, HBM GB/s (algorithmic bytes) and % of 8 TB/s"
@@ -51,11 +53,22 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace runs collapsed: what
+    the compiler sees of it (string literals in these sources hold no comment
+    markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_sha() -> str:
+    """Hash of the kernel and launch-planning sources, comments and layout
+    excluded: profiler summaries taken on other code are not used."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1255,7 +1255,8 @@ __device__ __forceinline__ void decode_segment(const DecArgs& a, int b, int hkv,
     bf16x8 qv = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + kk * 16 + g * 8) : zero_bf16x8();
     if (a.rope) {
       // pairs kk*8 + 4g + e of the lane's 8 elements, rotated at the query's
-      // position and stored back in bf16 (the rotated query is a bf16 tensor)
+      // position in fp32 and rounded to bf16: the fragment is a bf16 MFMA
+      // operand (the training path stores its rotated queries in bf16 too)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float cs, sn;

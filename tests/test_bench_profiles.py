@@ -94,3 +94,14 @@ def test_trace_summary_prices_kernels(tmp_path):
     pre = 2.0 * w.B * w.S * w.Hq * w.d * 2 + w.B * w.Hq * w.S * 4.0
     assert float(p["algorithmic_bytes_per_launch"]) == pre
     assert os.path.exists(out / "dkdv_reduce_kernel_tiny_trace.txt")
+
+
+def test_kernel_hash_ignores_comments_and_layout(tmp_path):
+    sys.path.insert(0, ROOT)
+    import bench
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* plain\n product */ }\n"
+    b = "int f(int x) { return 2 * x; }"
+    c = "int f(int x) { return 3 * x; }"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(b) != bench._code_only(c)
+    assert len(bench.kernel_source_sha()) == 16
