@@ -271,6 +271,19 @@ __device__ __forceinline__ void fwd_tile(FwdState<D, NT>& st, const bf16* Ks, co
   }
 }
 
+// Merge slot for the state of key group k (1 .. KS-1) of row wave `wave` in a
+// key-split workgroup: NREG floats per lane, [register][lane], packed into the
+// four tile arrays, which are free after the pipeline's last barrier.
+template <int NREG, int KVT>
+__device__ __forceinline__ float* merge_slot(bf16* a0, bf16* a1, bf16* a2, bf16* a3, int k, int wave, int WR,
+                                             int lane) {
+  constexpr int PER = (KVT / 2) / (NREG * 64);  // slots per array (KVT bf16 = KVT / 2 floats)
+  static_assert(PER >= 1, "merge slot");
+  const int wi = (k - 1) * WR + wave;
+  bf16* arr = wi / PER == 0 ? a0 : wi / PER == 1 ? a1 : wi / PER == 2 ? a2 : a3;
+  return reinterpret_cast<float*>(arr) + (wi % PER) * NREG * 64 + lane;
+}
+
 // KS = 2 (small grids): the workgroup's waves form two halves over the same
 // query rows; each pipeline step brings two 64-key tiles, the first half of
 // the waves takes the even tiles, the second half the odd ones, and at the
@@ -286,7 +299,7 @@ void fwd_kernel(FwdArgs a) {
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
   constexpr int KVT = TileLayout<D>::template elems<KS * BN>();
-  static_assert(KS == 1 || KS == 2, "key split");
+  static_assert(KS == 1 || KS == 2 || KS == 4, "key split");
   __shared__ __attribute__((aligned(16))) bf16 sK0[KVT], sV0[KVT], sK1[KVT], sV1[KVT];
 
   const int lane = threadIdx.x & 63;
@@ -357,15 +370,14 @@ void fwd_kernel(FwdArgs a) {
   };
   tile_pipeline(ntiles, b0, b1, fetch, [](int, const KVBuf&) {}, compute);
 
-  if constexpr (KS == 2) {
-    // the odd-tile half hands its state to the even-tile half over the same
-    // rows (the tile buffers are free after the pipeline's last barrier):
-    // [register][lane] floats, oacc then mu and the partial row sums
+  if constexpr (KS > 1) {
+    // key groups 1 .. KS-1 hand their softmax state (oacc, then mu and the
+    // partial row sums) to group 0 over the same rows, which merges them one
+    // by one by log-sum-exp
     constexpr int NREG = DT * NT * 16 + 2 * NT;
-    static_assert(NREG * 64 * sizeof(float) <= sizeof(sK0), "merge buffer");
-    float* red = reinterpret_cast<float*>(wave == 0 ? sK0 : wave == 1 ? sV0 : wave == 2 ? sK1 : sV1) + lane;
-    static_assert(WR <= 4, "merge buffers");
-    if (kh == 1) {
+    static_assert((KS - 1) * WR <= 4 * ((KVT / 2) / (NREG * 64)), "merge buffers");
+    if (kh > 0) {
+      float* red = merge_slot<NREG, KVT>(sK0, sV0, sK1, sV1, kh, wave, WR, lane);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -377,22 +389,26 @@ void fwd_kernel(FwdArgs a) {
       }
     }
     __syncthreads();
-    if (kh == 1) return;
+    if (kh > 0) return;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float mu_b = red[(DT * NT * 16 + 2 * t) * 64];
-      const float ls_b = red[(DT * NT * 16 + 2 * t + 1) * 64];
-      const float mu = fmaxf(st.mu[t], mu_b);
-      // a half that saw no key has mu = -inf and nothing accumulated
-      const float fa = mu == kNegInf ? 1.f : fast_exp2((st.mu[t] - mu) * c);
-      const float fb = mu == kNegInf ? 0.f : fast_exp2((mu_b - mu) * c);
-      st.lsum[t] = st.lsum[t] * fa + ls_b * fb;
-      st.mu[t] = mu;
+    for (int k = 1; k < KS; ++k) {
+      const float* red = merge_slot<NREG, KVT>(sK0, sV0, sK1, sV1, k, wave, WR, lane);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int t = 0; t < NT; ++t) {
+        const float mu_b = red[(DT * NT * 16 + 2 * t) * 64];
+        const float ls_b = red[(DT * NT * 16 + 2 * t + 1) * 64];
+        const float mu = fmaxf(st.mu[t], mu_b);
+        // a group that saw no key has mu = -inf and nothing accumulated
+        const float fa = mu == kNegInf ? 1.f : fast_exp2((st.mu[t] - mu) * c);
+        const float fb = mu == kNegInf ? 0.f : fast_exp2((mu_b - mu) * c);
+        st.lsum[t] = st.lsum[t] * fa + ls_b * fb;
+        st.mu[t] = mu;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          st.oacc[dt][t][r] = st.oacc[dt][t][r] * fa + red[((t * DT + dt) * 16 + r) * 64] * fb;
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            st.oacc[dt][t][r] = st.oacc[dt][t][r] * fa + red[((t * DT + dt) * 16 + r) * 64] * fb;
+      }
     }
   }
 
@@ -950,7 +966,7 @@ void bwd_dq_kernel(BwdArgs a) {
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
   constexpr int KVT = TileLayout<D>::template elems<KS * BN>();
-  static_assert(KS == 1 || KS == 2, "key split");
+  static_assert(KS == 1 || KS == 2 || KS == 4, "key split");
   __shared__ __attribute__((aligned(16))) bf16 sK0[KVT], sV0[KVT], sK1[KVT], sV1[KVT];
 
   const int lane = threadIdx.x & 63;
@@ -1060,14 +1076,12 @@ void bwd_dq_kernel(BwdArgs a) {
   };
   tile_pipeline(ntiles, b0, b1, fetch, [](int, const KVBuf&) {}, compute);
 
-  if constexpr (KS == 2) {
-    // the odd-tile half adds its dQ sums to the even-tile half's through LDS
-    // (the tile buffers are free after the pipeline's last barrier)
+  if constexpr (KS > 1) {
+    // key groups 1 .. KS-1 add their dQ sums to group 0's through LDS
     constexpr int NREG = DT * NT * 16;
-    static_assert(NREG * 64 * sizeof(float) <= sizeof(sK0), "reduction buffer");
-    static_assert(WR <= 4, "reduction buffers");
-    float* red = reinterpret_cast<float*>(wave == 0 ? sK0 : wave == 1 ? sV0 : wave == 2 ? sK1 : sV1) + lane;
-    if (kh == 1) {
+    static_assert((KS - 1) * WR <= 4 * ((KVT / 2) / (NREG * 64)), "reduction buffers");
+    if (kh > 0) {
+      float* red = merge_slot<NREG, KVT>(sK0, sV0, sK1, sV1, kh, wave, WR, lane);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -1076,13 +1090,17 @@ void bwd_dq_kernel(BwdArgs a) {
           for (int r = 0; r < 16; ++r) red[((t * DT + dt) * 16 + r) * 64] = st.acc[dt][t][r];
     }
     __syncthreads();
-    if (kh == 1) return;
+    if (kh > 0) return;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int k = 1; k < KS; ++k) {
+      const float* red = merge_slot<NREG, KVT>(sK0, sV0, sK1, sV1, k, wave, WR, lane);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st.acc[dt][t][r] += red[((t * DT + dt) * 16 + r) * 64];
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st.acc[dt][t][r] += red[((t * DT + dt) * 16 + r) * 64];
+    }
   }
 
 #pragma unroll
@@ -1484,9 +1502,12 @@ template <> struct Tiles<128> {
   static constexpr int DQ_NT = 1, DQ_OCC = 2, DQ_W = 4;      // 128-row blocks
   static constexpr int DKDV_NTJ = 1, DKDV_OCC = 1, DKDV_GROUPS = 1;
 };
-// small-grid configurations: 64-row blocks of four waves, two per 64-key
-// tile of each 128-key pipeline step (the key range split in two halves)
-constexpr int kSmallNT = 1, kSmallW = 4, kSmallKS = 2;
+// Small-grid configurations (forward and dQ): 64-row blocks of four waves
+// whose two halves take alternate 64-key tiles of each 128-key pipeline step.
+// (Four key groups of two waves each at d=64 shorten the longest block's chain
+// but need 144 KB of LDS, one block per CU, and measured slower.)
+// Two waves per SIMD (two blocks per CU), so at most 256 registers per wave.
+struct Small { static constexpr int NT = 1, W = 4, KS = 2, OCC = 2; };
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -1521,9 +1542,9 @@ hipError_t fwd_d(const Problem& pr, const void* q, const void* k, const void* v,
   const int64_t wgs = (int64_t)a.nqb * pr.B * pr.Hq;
   if (wgs >= kCUs * (4 * OCC / W))
     return launch((const void*)&fwd_kernel<D, NT, OCC, W>, wgs, a, stream, 64 * W);
-  a.nqb = cdiv(pr.S, 32 * kSmallNT * (kSmallW / kSmallKS));
-  return launch((const void*)&fwd_kernel<D, kSmallNT, OCC, kSmallW, kSmallKS>, (int64_t)a.nqb * pr.B * pr.Hq, a,
-                stream, 64 * kSmallW);
+  a.nqb = cdiv(pr.S, 32 * Small::NT * (Small::W / Small::KS));
+  return launch((const void*)&fwd_kernel<D, Small::NT, Small::OCC, Small::W, Small::KS>, (int64_t)a.nqb * pr.B * pr.Hq, a,
+                stream, 64 * Small::W);
 }
 
 template <int D>
@@ -1566,9 +1587,9 @@ hipError_t dq_d(const Problem& pr, const void* q, const void* k, const void* v, 
   const int64_t wgs = (int64_t)a.nblk * pr.B * pr.Hq;
   if (wgs >= kCUs * (4 * OCC / W))
     return launch((const void*)&bwd_dq_kernel<D, NT, OCC, W>, wgs, a, stream, 64 * W);
-  a.nblk = cdiv(pr.S, 32 * kSmallNT * (kSmallW / kSmallKS));
-  return launch((const void*)&bwd_dq_kernel<D, kSmallNT, OCC, kSmallW, kSmallKS>, (int64_t)a.nblk * pr.B * pr.Hq,
-                a, stream, 64 * kSmallW);
+  a.nblk = cdiv(pr.S, 32 * Small::NT * (Small::W / Small::KS));
+  return launch((const void*)&bwd_dq_kernel<D, Small::NT, Small::OCC, Small::W, Small::KS>, (int64_t)a.nblk * pr.B * pr.Hq,
+                a, stream, 64 * Small::W);
 }
 
 template <int D>
