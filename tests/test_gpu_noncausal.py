@@ -27,6 +27,9 @@ FUZZ = [
     (3, 300, 4, 1, 64, (0, 300)),
     (3, 257, 2, 2, 128, (1, 257)),
     (2, 1000, 6, 3, 64, (500, 1000)),
+    # large-grid forward and dQ blocks, ragged lengths (as in the causal fuzz)
+    (2, 1000, 64, 16, 64, (500, 1000)),
+    (1, 1000, 64, 16, 128, (700, 1000)),
 ]
 
 

@@ -39,6 +39,13 @@ FUZZ = [
     (2, 1000, 6, 3, 64, (500, 1000)),
     (1, 520, 16, 2, 128, None),
     (2, 384, 5, 5, 64, (383, 384)),
+    # enough (block, head) pairs that the forward and dQ run their large-grid
+    # blocks (256 and 128 rows) and dK/dV needs no split, with sequence
+    # lengths that are no multiple of a block
+    (2, 1000, 64, 16, 64, None),
+    (2, 1000, 64, 16, 64, (500, 1000)),
+    (1, 1000, 64, 16, 128, (700, 1000)),
+    (1, 777, 128, 32, 64, None),
 ]
 
 
