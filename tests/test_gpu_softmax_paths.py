@@ -48,6 +48,14 @@ CASES = [
     (1, 260, 2, 2, 128, True, slice(130, 140), 129, 80.0),
     (1, 300, 2, 1, 64, True, slice(200, 232), 150, 10.0),    # 2^14: absorbed by the first path
     (2, 400, 4, 1, 64, True, slice(300, 301), 299, 13.0),
+    # large-grid forward blocks (256 rows; at d=64 each wave holds two 32-row
+    # query tiles): a late spike, one confined to the second tile of a wave
+    # (rows 608-639 of block rows 512-767 are wave 1's second tile), a
+    # bidirectional one and a d=128 one
+    (2, 1000, 64, 16, 64, True, slice(600, 632), 590, 60.0),
+    (2, 1000, 64, 16, 64, True, slice(610, 620), 600, 20.0),
+    (2, 1000, 64, 16, 64, False, slice(0, 16), 900, 60.0),
+    (1, 1000, 64, 16, 128, True, slice(700, 720), 650, 80.0),
 ]
 
 

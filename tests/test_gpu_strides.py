@@ -40,6 +40,7 @@ def same(a, b):
     (2, 300, 4, 2, 64, True, False),
     (1, 257, 8, 1, 128, True, True),
     (2, 200, 6, 3, 64, False, True),
+    (2, 1000, 64, 16, 64, True, True),   # large-grid forward and dQ blocks
 ])
 def test_fused_qkv_views(B, S, Hq, Hkv, d, causal, padded):
     say(f"fused qkv B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} causal={causal} padded={padded}")
