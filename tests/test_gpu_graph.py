@@ -45,16 +45,21 @@ def _eager(t, scale, sl, causal, fused=False, rope_base=0.0):
     return {"O": o, "LSE": lse, "D": delta, "dQ": dq, "dK": dk, "dV": dv}
 
 
-@pytest.mark.parametrize("causal,padded,fused,rope_base", [(True, False, False, 0.0), (True, True, False, 0.0),
-                                                           (False, True, False, 0.0), (True, True, True, 0.0),
-                                                           (True, False, False, 10000.0),
-                                                           (True, True, True, 10000.0)])
-def test_graph_replays_match_eager(causal, padded, fused, rope_base):
-    B, S, Hq, Hkv, d = 2, 384, 8, 2, 64
+@pytest.mark.parametrize("causal,padded,fused,rope_base,large", [(True, False, False, 0.0, False),
+                                                                 (True, True, False, 0.0, False),
+                                                                 (False, True, False, 0.0, False),
+                                                                 (True, True, True, 0.0, False),
+                                                                 (True, False, False, 10000.0, False),
+                                                                 (True, True, True, 10000.0, False),
+                                                                 (True, True, False, 0.0, True)])
+def test_graph_replays_match_eager(causal, padded, fused, rope_base, large):
+    # large: enough blocks for the large-grid forward and dQ kernels
+    B, S, Hq, Hkv, d = (2, 1000, 64, 16, 64) if large else (2, 384, 8, 2, 64)
     say(f"graph capture: B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} causal={causal} padded={padded} fused={fused} "
         f"rope={rope_base}")
     dev = torch.device("cuda")
-    inputs = [make_inputs(B, S, Hq, Hkv, d, 900 + i, padded=padded, seqlen_range=(200, 384)) for i in range(3)]
+    rng = (500, 1000) if large else (200, 384)
+    inputs = [make_inputs(B, S, Hq, Hkv, d, 900 + i, padded=padded, seqlen_range=rng) for i in range(3)]
     # buffers the graph is bound to
     buf = {n: getattr(inputs[0], n).to(dev).contiguous() for n in ("q", "k", "v", "do")}
     sl = inputs[0].seqlens.to(dev) if padded else None
