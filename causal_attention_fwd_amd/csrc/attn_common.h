@@ -180,10 +180,17 @@ __device__ __forceinline__ void tile_load_lds(const bf16* base, int64_t row_stri
 // once they have arrived (for data staged through registers), compute(t, buf)
 // reads the tile; the barrier after each compute publishes the next tile and
 // frees the one just read.
+// tile_pipeline_start issues the first tile's loads; a kernel calls it as
+// soon as the tile can be addressed, so that they travel while it finishes its
+// prologue, and then runs the rest with started = true.
+template <class Buf, class Fetch>
+__device__ __forceinline__ void tile_pipeline_start(int n, const Buf& b0, Fetch&& fetch) {
+  if (n > 0) fetch(0, b0);
+}
 template <class Buf, class Fetch, class Land, class Compute>
 __device__ __forceinline__ void tile_pipeline(int n, const Buf& b0, const Buf& b1, Fetch&& fetch, Land&& land,
-                                              Compute&& compute) {
-  if (n > 0) fetch(0, b0);
+                                              Compute&& compute, bool started = false) {
+  if (!started && n > 0) fetch(0, b0);
   wait_vmem();
   if (n > 0) land(0, b0);
   __syncthreads();

@@ -345,7 +345,8 @@ void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.oacc[dt][t] = zero16();
   }
-  wait_vmem();
+  // (no wait here: the pipeline's first wait covers these loads and the
+  // first K/V tile, which is issued before it, so the two latencies overlap)
 
   const KVBuf b0{sK0, sV0, 0}, b1{sK1, sV1, 1};
   auto fetch = [&](int kt, const KVBuf& buf) {
@@ -663,7 +664,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
       st.dv[ct][t] = zero16();
     }
   }
-  wait_vmem();
 
   const int qt0 = a.causal ? j0 / BMQ : 0;  // first query tile with rows at or below the block
   const int nq = (j0 < L) ? (L - 1) / BMQ - qt0 + 1 : 0;  // query tiles per head
@@ -727,7 +727,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
       dkdv_tile<D, NTJ, false>(st, buf.k, buf.v, ls, ds, lane, c, lo, hi);
     }
   };
-  tile_pipeline(trips, b0, b1, fetch, land, compute);
+  // the first Q/dO tile travels together with the K/V fragment loads above:
+  // one wait covers both
+  tile_pipeline_start(trips, b0, fetch);
+  wait_vmem();
+  tile_pipeline(trips, b0, b1, fetch, land, compute, /*started=*/true);
 
   if constexpr (GROUPS == 2) {
     // group 1 hands its partial sums to group 0 through LDS (the tile buffers
@@ -1000,6 +1004,16 @@ void bwd_dq_kernel(BwdArgs a) {
   const int key_last = a.causal ? wave_last : (wave_last < qw ? -1 : L - 1);
   const float c = a.scale * kLog2e;
 
+  // K/V tiles stream straight into LDS (no staging registers), double-buffered.
+  const KVBuf b0{sK0, sV0, 0}, b1{sK1, sV1, 1};
+  auto fetch = [&](int kt, const KVBuf& buf) {
+    tile_load_lds<KS * BN, D, W>(Kb, ks, kt * KS * BN, L, buf.k, wave_all, lane);
+    tile_load_lds<KS * BN, D, W>(Vb, ks, kt * KS * BN, L, buf.v, wave_all, lane);
+  };
+  // the first K/V tile is issued before the row loads below, so that its copy
+  // travels while they land and the prologue does its arithmetic on them
+  tile_pipeline_start(ntiles, b0, fetch);
+
   DqState<D, NT> st;
   st.ones = zero_bf16x8();
   if (g == 0) {
@@ -1050,12 +1064,6 @@ void bwd_dq_kernel(BwdArgs a) {
   }
   wait_vmem();
 
-  // K/V tiles stream straight into LDS (no staging registers), double-buffered.
-  const KVBuf b0{sK0, sV0, 0}, b1{sK1, sV1, 1};
-  auto fetch = [&](int kt, const KVBuf& buf) {
-    tile_load_lds<KS * BN, D, W>(Kb, ks, kt * KS * BN, L, buf.k, wave_all, lane);
-    tile_load_lds<KS * BN, D, W>(Vb, ks, kt * KS * BN, L, buf.v, wave_all, lane);
-  };
   auto compute = [&](int kt, const KVBuf& buf) {
     const int j0 = (kt * KS + kh) * BN;
     if (j0 > key_last) return;
@@ -1074,7 +1082,7 @@ void bwd_dq_kernel(BwdArgs a) {
       dq_tile<D, NT, false>(st, Ks, Vs, lane, c, lim);
     }
   };
-  tile_pipeline(ntiles, b0, b1, fetch, [](int, const KVBuf&) {}, compute);
+  tile_pipeline(ntiles, b0, b1, fetch, [](int, const KVBuf&) {}, compute, /*started=*/true);
 
   if constexpr (KS > 1) {
     // key groups 1 .. KS-1 add their dQ sums to group 0's through LDS
