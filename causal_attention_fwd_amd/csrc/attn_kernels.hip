@@ -1492,11 +1492,6 @@ namespace {
 // dQ passes; the dK/dV pass always gives each wave 32 key rows), waves per
 // SIMD (OCC: the register budget per wave is 512 / OCC) and waves per
 // workgroup of the forward and dQ passes (W: the waves of a workgroup share
-// each K/V tile loaded into LDS).
-// Per head dimension: 32-row tiles per wave (NT: query rows in the forward and
-// dQ passes; the dK/dV pass always gives each wave 32 key rows), waves per
-// SIMD (OCC: the register budget per wave is 512 / OCC) and waves per
-// workgroup of the forward and dQ passes (W: the waves of a workgroup share
 // each K/V tile loaded into LDS). The *_SMALL configurations (64-row query
 // blocks) are used when the default blocks would leave CUs without work.
 template <int D> struct Tiles;
