@@ -253,17 +253,13 @@ __device__ __forceinline__ void decode_qblock(int bid, int nqb, int B, int Hq, i
   }
 }
 
-// Key-block tiles (dK/dV): grid = nkb * parts * B * Hkv, a workgroup being one
-// part (of `parts`) of one key block. A key block's work grows with the number
-// of query rows below it, so blocks are dispatched longest first (key block 0
-// first, its parts together). With `pair_ends`, the second half of the
-// dispatch order walks the key blocks from the far end instead, so that when
-// two workgroups share a CU from the start, a long block tends to pair with a
-// short one. kv groups are pinned to XCDs as for query blocks.
-__device__ __forceinline__ void decode_kblock(int bid, int nkb, int parts, int B, int Hkv, bool pair_ends, int& kb,
-                                              int& part, int& b, int& hkv) {
+// Key-block tiles (dK/dV): grid = B * Hkv units of nkb * parts workgroups;
+// returns the workgroup's unit (b, hkv) and its slot within the unit (slots
+// are dispatched in order, so a unit's first key blocks, the longest under the
+// causal mask, go first). kv groups are pinned to XCDs as for query blocks.
+__device__ __forceinline__ void decode_kunit(int bid, int B, int Hkv, int& slot, int& b, int& hkv) {
   const int units = B * Hkv;
-  int unit, slot;
+  int unit;
   if ((units & 7) == 0) {
     const int xcd = bid & 7, xs = bid >> 3;
     const int upx = units >> 3;
@@ -273,10 +269,6 @@ __device__ __forceinline__ void decode_kblock(int bid, int nkb, int parts, int B
     slot = bid / units;
     unit = bid - slot * units;
   }
-  const int ks = slot / parts;
-  part = slot - ks * parts;
-  const int half = (nkb + 1) >> 1;
-  kb = (!pair_ends || ks < half) ? ks : nkb - 1 - (ks - half);
   b = unit / Hkv;
   hkv = unit - b * Hkv;
 }

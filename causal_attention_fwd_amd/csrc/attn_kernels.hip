@@ -604,6 +604,34 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
   }
 }
 
+// Key block, part and part count of a dK/dV workgroup from its slot in its
+// unit (dkdv_part_base gives the deal). Without a split and with pair_ends,
+// the second half of the slots walks the key blocks from the far end, so that
+// when two workgroups share a CU from the start a long block tends to pair
+// with a short one.
+__device__ __forceinline__ void dkdv_slot(int slot, int nkb, int parts, int S, int causal, bool pair_ends, int& kb,
+                                          int& part, int& nparts) {
+  if (parts == 1) {
+    const int half = (nkb + 1) >> 1;
+    kb = (!pair_ends || slot < half) ? slot : nkb - 1 - (slot - half);
+    part = 0;
+    nparts = 1;
+    return;
+  }
+  int lo = 0, hi = nkb - 1;  // the last key block whose first slot is <= slot
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (dkdv_part_base(mid, nkb, parts, S, causal) <= slot)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  kb = lo;
+  const int first = dkdv_part_base(kb, nkb, parts, S, causal);
+  part = slot - first;
+  nparts = dkdv_part_base(kb + 1, nkb, parts, S, causal) - first;
+}
+
 // GROUPS = 1: four waves. GROUPS = 2: eight waves in two groups of four that
 // own the same key rows and split the (head, query tile) sequence by parity;
 // their partial dK/dV are summed through LDS at the end. With two groups each
@@ -633,8 +661,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
-  int kb, b, hkv, part;
-  decode_kblock(blockIdx.x, a.nblk, a.parts, a.B, a.Hkv, GROUPS == 1 && a.parts == 1, kb, part, b, hkv);
+  int slot, b, hkv, kb, part, nparts;
+  decode_kunit(blockIdx.x, a.B, a.Hkv, slot, b, hkv);
+  dkdv_slot(slot, a.nblk, a.parts, a.S, a.causal, GROUPS == 1, kb, part, nparts);
   const int S = a.S;
   const int L = valid_len(a.seqlens, b, S);
   const int G = a.Hq / a.Hkv;
@@ -669,8 +698,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int nq = (j0 < L) ? (L - 1) / BMQ - qt0 + 1 : 0;  // query tiles per head
   const int iters = nq * G;                               // (head, query tile) pairs
   // this workgroup's share of them: [it_lo, it_hi)
-  const int it_lo = (int)((int64_t)part * iters / a.parts);
-  const int it_hi = (int)((int64_t)(part + 1) * iters / a.parts);
+  const int it_lo = (int)((int64_t)part * iters / nparts);
+  const int it_hi = (int)((int64_t)(part + 1) * iters / nparts);
   const int trips = (it_hi - it_lo + GROUPS - 1) / GROUPS;  // this group does it = it_lo + trip*GROUPS + grp
 
   float st_reg = 0.f;  // wave 0 of a group carries LSE, wave 1 D
@@ -844,7 +873,10 @@ __global__ __launch_bounds__(kThreads) void dkdv_reduce_kernel(BwdArgs a) {
   if (j < L) {
     const int64_t pstride = (int64_t)a.B * a.S * a.Hkv * D;
     const int64_t off = row * D + c4 * 4;
-    for (int p = 0; p < a.parts; ++p) {
+    const int kb = j / 128;  // the row's key block and the parts it was split into
+    const int nparts = dkdv_part_base(kb + 1, a.nblk, a.parts, a.S, a.causal) -
+                       dkdv_part_base(kb, a.nblk, a.parts, a.S, a.causal);
+    for (int p = 0; p < nparts; ++p) {
       const float4 k4 = *reinterpret_cast<const float4*>(a.part_dk + p * pstride + off);
       const float4 v4 = *reinterpret_cast<const float4*>(a.part_dv + p * pstride + off);
       kx[0] += k4.x; kx[1] += k4.y; kx[2] += k4.z; kx[3] += k4.w;
@@ -1563,7 +1595,8 @@ hipError_t dkdv_d(const Problem& pr, const void* q, const void* k, const void* v
                   const float* lse, const float* delta, void* dk, void* dv, void* workspace, hipStream_t stream) {
   constexpr int NTJ = Tiles<D>::DKDV_NTJ;
   const int parts = dkdv_parts(pr);
-  const size_t part_elems = (size_t)pr.B * pr.S * pr.Hkv * D * parts;
+  static_assert(128 * NTJ == 128, "the split's deal and the reduce pass assume 128-key blocks");
+  const size_t part_elems = (size_t)pr.B * pr.S * pr.Hkv * D * dkdv_max_parts(pr);
   float* part_dk = parts > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
   float* part_dv = parts > 1 ? part_dk + part_elems : nullptr;
   BwdArgs a{(const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)d_o, lse, delta,

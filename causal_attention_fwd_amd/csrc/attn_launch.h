@@ -49,8 +49,28 @@ int64_t max_grid(const Problem& pr);
 // partial sums are added by a reduce pass.
 int dkdv_parts(const Problem& pr);
 
+// With a split, each (sequence, kv head) unit's parts * nkb workgroups are
+// dealt to its nkb key blocks in proportion to the blocks' (head, query tile)
+// iterations, at least one each: under the causal mask block k meets
+// ceil(S/64) - 2k query tiles, so the first blocks get more workgroups and
+// every workgroup about the same number of iterations. Returns the index of
+// key block kb's first workgroup within the unit (kb = nkb gives the total);
+// bidirectional blocks all have the same work and the deal is even. Shared by
+// the planner (workspace size), the dK/dV pass and its reduce pass.
+__host__ __device__ inline int dkdv_part_base(int kb, int nkb, int parts, int S, int causal) {
+  const int64_t n64 = ((int64_t)S + 63) / 64;
+  const int64_t before = causal ? (int64_t)kb * n64 - (int64_t)kb * (kb - 1) : kb;
+  const int64_t all = causal ? (int64_t)nkb * n64 - (int64_t)nkb * (nkb - 1) : nkb;
+  return kb + (int)((int64_t)(parts - 1) * nkb * before / all);
+}
+
+// 128-key blocks of the dK/dV pass, and the largest number of parts a block
+// is split into: the number of partial-sum slices the split's workspace holds.
+int dkdv_blocks(const Problem& pr);
+int dkdv_max_parts(const Problem& pr);
+
 // Device workspace the backward needs: the split dK/dV pass's fp32 partial
-// sums (2 * parts * B * S * Hkv * d floats), 0 without a split.
+// sums (2 * dkdv_max_parts * B * S * Hkv * d floats), 0 without a split.
 size_t bwd_workspace_bytes(const Problem& pr);
 
 // Decode: Sq new queries per sequence against a [B, Smax, Hkv, d] key/value cache.

@@ -36,10 +36,24 @@ int dkdv_parts(const Problem& pr) {
   return (int)std::min(std::min(want, cap), kMaxParts);
 }
 
-size_t bwd_workspace_bytes(const Problem& pr) {
+int dkdv_blocks(const Problem& pr) { return (int)(((int64_t)pr.S + 127) / 128); }
+
+int dkdv_max_parts(const Problem& pr) {
   const int parts = dkdv_parts(pr);
-  if (parts <= 1) return 0;
-  return (size_t)2 * parts * pr.B * pr.S * pr.Hkv * pr.d * sizeof(float);
+  if (parts <= 1) return 1;
+  // the first block has the most work, but the rounding of the deal can give
+  // a later one a part more: take the largest count
+  const int nkb = dkdv_blocks(pr);
+  int most = 1;
+  for (int kb = 0; kb < nkb; ++kb)
+    most = std::max(most, dkdv_part_base(kb + 1, nkb, parts, pr.S, pr.causal) -
+                              dkdv_part_base(kb, nkb, parts, pr.S, pr.causal));
+  return most;
+}
+
+size_t bwd_workspace_bytes(const Problem& pr) {
+  if (dkdv_parts(pr) <= 1) return 0;
+  return (size_t)2 * dkdv_max_parts(pr) * pr.B * pr.S * pr.Hkv * pr.d * sizeof(float);
 }
 
 namespace {
