@@ -13,6 +13,7 @@ import subprocess
 import pytest
 
 import causal_attention_fwd_amd as attn
+from split_deal import dealt_parts
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
@@ -169,31 +170,11 @@ def test_workspace_bytes_is_linear_not_quadratic(lib):
     assert lib.attn_bwd_workspace_bytes(None) == 0
 
 
-def _dealt_parts(B, S, Hq, Hkv, causal):
-    """The split dK/dV pass's workgroups per 128-key block, from the rule the
-    planner documents: parts * nkb workgroups per (sequence, kv head), at least
-    one per block and the rest in proportion to the block's query tiles
-    (ceil(S/64) - 2*kb under the causal mask, all equal without it)."""
-    nkb = (S + 127) // 128
-    units = nkb * B * Hkv
-    if units >= 256:
-        return [1] * nkb
-    parts = min((256 + units - 1) // units, max(1, (S + 63) // 64 * (Hq // Hkv) // 4), 8)
-    n64 = (S + 63) // 64
-    w = [n64 - 2 * kb if causal else 1 for kb in range(nkb)]
-    extra = (parts - 1) * nkb
-    cum, first = 0, []
-    for kb in range(nkb + 1):
-        first.append(kb + extra * cum // sum(w))
-        if kb < nkb:
-            cum += w[kb]
-    return [first[kb + 1] - first[kb] for kb in range(nkb)]
-
-
 @pytest.mark.parametrize("B,S,Hq,Hkv,causal", [(2, 1024, 12, 4, 1), (2, 1024, 12, 4, 0), (1, 1000, 8, 1, 1),
-                                               (3, 333, 4, 2, 1), (1, 128, 2, 2, 1), (4, 2048, 32, 8, 1)])
+                                               (3, 333, 4, 2, 1), (1, 128, 2, 2, 1), (4, 2048, 32, 8, 1),
+                                               (2, 1281, 12, 4, 1)])
 def test_split_workspace_holds_the_most_parts_of_any_block(lib, B, S, Hq, Hkv, causal):
-    parts = _dealt_parts(B, S, Hq, Hkv, causal)
+    parts = dealt_parts(B, S, Hq, Hkv, causal)
     shape = _shape(B=B, S=S, Hq=Hq, Hkv=Hkv, d=64, causal=causal)
     split = sum(parts) > len(parts)
     want = 2 * max(parts) * B * S * Hkv * 64 * 4 if split else 0  # fp32 dK and dV partials

@@ -15,6 +15,7 @@ import causal_attention_fwd_amd as attn
 from attn_workloads import WORKLOADS, make_inputs, workload_inputs
 
 from parity import compare, host_inputs, oracle_unit, run_gpu, say, slice_unit, to_gpu, whole_output_identities
+from split_deal import dealt_parts
 
 import oracle
 
@@ -59,6 +60,29 @@ def test_fuzz_every_element(case):
     q, k, v, do, sl = host_inputs(inp)
     ref = oracle.backward(q, k, v, do, inp.scale, sl)
     compare(gpu, ref, f"fuzz{case}")
+
+
+# The split dK/dV pass deals each (sequence, kv head)'s workgroups to its key
+# blocks by their work; at S = 1281 the rounding gives the second block more
+# parts than the first (4, 5, 4, 4, ...) and the second-to-last fewer than the
+# last: the workspace must hold the largest count, the reduce pass each row's.
+UNEVEN = [(2, 1281, 12, 4, 64, None, True), (2, 1281, 12, 4, 64, (640, 1281), True),
+          (2, 1281, 12, 4, 128, None, True), (2, 1281, 12, 4, 64, None, False)]
+
+
+@pytest.mark.parametrize("case", UNEVEN, ids=["causal", "causal_padded", "causal_d128", "bidirectional"])
+def test_uneven_split_every_element(case):
+    B, S, Hq, Hkv, d, rng, causal = case
+    parts = dealt_parts(B, S, Hq, Hkv, causal)
+    if causal:
+        assert max(parts) > parts[0] and sum(parts) > len(parts), parts
+    seed = 4200 + S + d + 7 * int(causal)
+    say(f"uneven split B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} pad={rng} causal={causal} parts={parts} seed={seed}")
+    inp = make_inputs(B, S, Hq, Hkv, d, seed, padded=rng is not None, seqlen_range=rng)
+    gpu = run_gpu(inp, causal=causal)
+    q, k, v, do, sl = host_inputs(inp)
+    ref = oracle.backward(q, k, v, do, inp.scale, sl, causal=causal)
+    compare(gpu, ref, f"uneven{case}")
 
 
 def test_zero_length_sequences():
