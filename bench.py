@@ -280,12 +280,13 @@ def run(args):
     # per-kernel times: an eager pass with HIP events on the library's stream,
     # right after the timed replays so that the GPU is still at its sustained
     # clock (with --eager it is the timed region itself). After graph timing
-    # the pass is queued behind a few more replays of the step, which keep the
-    # GPU busy while the host enqueues it: the events then time the kernels
-    # back to back, not the host's launch gaps.
+    # the pass is queued behind at least 30 ms of replays of the step, which
+    # keep the GPU busy while the host enqueues it (a few ms for the default
+    # steps): the events then time the kernels back to back, not the host's
+    # launch gaps.
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     if g_step is not None:
-        for i in range(max(10, args.steps // 2)):
+        for i in range(max(10, math.ceil(30.0 / g_step))):
             args.graphs[i % len(args.graphs)].replay()
     t0 = time.perf_counter()
     for i in range(args.steps):
