@@ -1,8 +1,9 @@
 """Seeded synthetic workloads for causal attention (shared by tests and bench).
 
-This module only draws random inputs and names the workload shapes. It holds
-none of the attention arithmetic, so both the CPU oracle and the GPU path can
-take their inputs from here without sharing any of the method's code.
+This module only draws random inputs, names the workload shapes and counts
+(valid pairs, flops, bytes, the split dK/dV pass's workgroups per key block).
+It holds none of the attention arithmetic, so both the CPU oracle and the GPU
+path can take their inputs from here without sharing any of the method's code.
 
 Shapes follow the pages' workloads:
   * tiny        - a single tile, two heads (a sanity case the oracle runs in ms)
@@ -212,3 +213,27 @@ def decode_bytes(B: int, Sq: int, Smax: int, Hq: int, Hkv: int, d: int, cache_le
     cache = sum(lens) * Hkv * d * 2 * 2
     qo = B * Sq * Hq * d * 2 * 2 + B * Sq * Hq * 4
     return {"cache": cache, "q_o_lse": qo, "total": cache + qo}
+
+
+def dkdv_split_parts(B: int, S: int, Hq: int, Hkv: int, causal: bool = True) -> list:
+    """Workgroups per 128-key block of the split dK/dV pass, from the rule the
+    library documents (all ones when there is no split): each (sequence, kv
+    head) gets parts * nkb workgroups, parts = min(ceil(256 / blocks), a quarter
+    of the first block's (head, query tile) iterations, 8); every block gets
+    one and the rest go in proportion to the blocks' query tiles (ceil(S/64) -
+    2*kb under the causal mask, all equal without it). Pure counting, used to
+    check the library's workspace size and to price its reduce pass."""
+    nkb = (S + 127) // 128
+    units = nkb * B * Hkv
+    if units >= 256:
+        return [1] * nkb
+    parts = min((256 + units - 1) // units, max(1, (S + 63) // 64 * (Hq // Hkv) // 4), 8)
+    n64 = (S + 63) // 64
+    w = [n64 - 2 * kb if causal else 1 for kb in range(nkb)]
+    extra = (parts - 1) * nkb
+    cum, first = 0, []
+    for kb in range(nkb + 1):
+        first.append(kb + extra * cum // sum(w))
+        if kb < nkb:
+            cum += w[kb]
+    return [first[kb + 1] - first[kb] for kb in range(nkb)]

@@ -161,8 +161,7 @@ def _write_trace(kname, w, row, command, lines):
 def trace_summary(args):
     """Per-kernel average launch time from a rocprofv3 --kernel-trace --stats
     run, priced in algorithmic flops (the MFMA kernels) or bytes (the rest)."""
-    import causal_attention_fwd_amd as attn
-    from attn_workloads import DECODE_WORKLOADS, WORKLOADS, algorithmic_flops, workload_inputs
+    from attn_workloads import DECODE_WORKLOADS, WORKLOADS, algorithmic_flops, dkdv_split_parts, workload_inputs
     if args.workload in DECODE_WORKLOADS:
         return decode_trace_summary(args)
     w = WORKLOADS[args.workload]
@@ -171,11 +170,15 @@ def trace_summary(args):
     share = {"fwd_kernel": fl["fwd"], "bwd_dkdv_kernel": fl["bwd_dkdv"], "bwd_dq_kernel": fl["bwd_dq"]}
     B, S, Hq, Hkv, d = w.B, w.S, w.Hq, w.Hkv, w.d
     kv_bf16 = B * S * Hkv * d * 2.0
-    # dK/dV partials: the workspace holds parts x (dK, dV) in fp32
-    parts = attn.attn_bwd_workspace_bytes(B, S, Hq, Hkv, d) / (4 * kv_bf16)
+    # dK/dV partials: each key row's block was split into its own number of
+    # parts; the reduce pass reads that many fp32 (dK, dV) rows per key row
+    per_block = dkdv_split_parts(B, S, Hq, Hkv, not args.non_causal)
+    parts = sum(per_block) / len(per_block)
+    rows = [min(128, S - 128 * kb) for kb in range(len(per_block))]
+    partial_bytes = sum(p * r for p, r in zip(per_block, rows)) * B * Hkv * d * 4 * 2.0
     alg_bytes = {
         "preprocess_kernel": 2.0 * B * S * Hq * d * 2 + B * Hq * S * 4.0,
-        "dkdv_reduce_kernel": 2 * kv_bf16 * 2 * parts + 2 * kv_bf16,
+        "dkdv_reduce_kernel": partial_bytes + 2 * kv_bf16,
         "rope_kernel": 2.0 * B * S * (Hq + Hkv) * d * 2,
     }
     names = list(KERNEL_NAMES.values()) + list(TRACE_EXTRA.values())
@@ -188,7 +191,7 @@ def trace_summary(args):
                 out = [f"algorithmic_gflop_per_launch: {f / 1e9:.3f}",
                        f"achieved_tflops_at_average: {f / (avg_us * 1e-6) / 1e12:.1f}"]
                 if kname == "bwd_dkdv_kernel" and parts > 1:
-                    out.append(f"note: this shape splits each key block's query range over {parts:.0f} "
+                    out.append(f"note: this shape splits its key blocks' query ranges over {per_block} "
                                f"parts; the dK/dV call is this kernel plus dkdv_reduce_kernel")
                 return out
         else:
@@ -196,7 +199,8 @@ def trace_summary(args):
                 out = [f"algorithmic_bytes_per_launch: {b:.0f}",
                        f"achieved_gbs_at_average: {b / (avg_us * 1e-6) / 1e9:.1f}"]
                 if kname == "dkdv_reduce_kernel":
-                    out.append(f"parts: {parts:.0f} (fp32 dK and dV partials read, bf16 dK and dV written)")
+                    out.append(f"parts per key block: {per_block} (fp32 dK and dV partials read, "
+                               f"bf16 dK and dV written)")
                 return out
         _write_trace(kname, w, row, args.command, lines)
 

@@ -149,10 +149,12 @@ attn_status attn_bwd_preprocess(const attn_shape* shape, const void* o, const vo
  * for `shape`: O(B*S*Hkv*d) at most, never O(S^2) (the "Axis" Zyora Labs page,
  * feature list: memory stays flat as the sequence grows). It is 0 unless the
  * shape has too few 128-key blocks (B * ceil(S/128) * Hkv < 256) to give every
- * CU work; then each block's work is split into P <= 8 parts whose fp32
- * partial dK and dV sums (2 * P * B * S * Hkv * d floats) are added by a
- * reduce pass. Depends only on batch, seqlen, heads and head_dim. Returns 0
- * for a NULL or invalid shape.
+ * CU work; then each (sequence, kv head) gets parts * ceil(S/128) workgroups,
+ * parts <= 8, dealt to its key blocks by their work under the causal mask (at
+ * most 2 * parts - 1 to one block), and their fp32 partial dK and dV sums
+ * (2 * P * B * S * Hkv * d floats, P the largest count of any block) are added
+ * by a reduce pass. Depends only on batch, seqlen, heads, head_dim and the
+ * causal flag. Returns 0 for a NULL or invalid shape.
  */
 size_t attn_bwd_workspace_bytes(const attn_shape* shape);
 

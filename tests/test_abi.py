@@ -13,7 +13,7 @@ import subprocess
 import pytest
 
 import causal_attention_fwd_amd as attn
-from split_deal import dealt_parts
+from attn_workloads import dkdv_split_parts as dealt_parts
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")

@@ -15,7 +15,7 @@ import causal_attention_fwd_amd as attn
 from attn_workloads import WORKLOADS, make_inputs, workload_inputs
 
 from parity import compare, host_inputs, oracle_unit, run_gpu, say, slice_unit, to_gpu, whole_output_identities
-from split_deal import dealt_parts
+from attn_workloads import dkdv_split_parts as dealt_parts
 
 import oracle
 
