@@ -43,10 +43,10 @@ hipError_t launch_bwd_dq_with_delta(const Problem& pr, const void* q, const void
 // hardware's 2^31-1 workgroup limit by the API layer).
 int64_t max_grid(const Problem& pr);
 
-// Parts each 128-key block of the dK/dV pass is split into (1: no split).
+// Workgroups per 128-key block of the dK/dV pass, on average (1: no split).
 // When the key blocks alone would leave CUs idle, the (head, query tile)
-// iterations of every block are shared by several workgroups whose fp32
-// partial sums are added by a reduce pass.
+// iterations of the blocks are shared by several workgroups (dealt by
+// dkdv_part_base) whose fp32 partial sums are added by a reduce pass.
 int dkdv_parts(const Problem& pr);
 
 // With a split, each (sequence, kv head) unit's parts * nkb workgroups are

@@ -29,8 +29,9 @@ int dkdv_parts(const Problem& pr) {
   const int64_t units = ((int64_t)pr.S + 127) / 128 * pr.B * pr.Hkv;
   if (units >= kCUs) return 1;
   const int64_t want = (kCUs + units - 1) / units;
-  // every part of the longest block keeps at least four (head, query tile)
-  // iterations (two per wave group)
+  // at most a quarter of the longest block's (head, query tile) iterations:
+  // the uneven deal gives that block at most 2 * parts - 1 workgroups, so each
+  // still gets more than two (one per wave group)
   const int64_t iters0 = ((int64_t)pr.S + 63) / 64 * (pr.Hq / pr.Hkv);
   const int64_t cap = std::max<int64_t>(1, iters0 / 4);
   return (int)std::min(std::min(want, cap), kMaxParts);
