@@ -850,6 +850,332 @@ void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// Backward dK/dV with each key slice's work split over two waves of one SIMD
+// by role (d = 128, where one wave doing all of it needs 424 registers and so
+// runs alone on its SIMD). Eight waves per 128-key block: for key rows
+// [j0 + 32w, +32), wave w (the P wave) holds K and accumulates dV^T, wave
+// w + 4 (the dS wave, on the same SIMD) holds V and accumulates dK^T. Each
+// (head, query tile) takes two phases between barriers: first the P wave forms
+// S^T = K Q^T and P = exp2(S c - LSE log2e) and leaves P in LDS (fp32, the
+// lane's registers in order) while the dS wave forms dP^T = V dO^T - D; then
+// the P wave adds P^T dO to dV^T while the dS wave forms dS = P (dP - D) from
+// that P and adds dS^T Q to dK^T. The products and the softmax are those of
+// dkdv_tile, term for term; each wave runs half of them, and the two waves of
+// a SIMD interleave.
+// ----------------------------------------------------------------------------
+
+// The P wave's share of one 64-row query tile, first part: S and P (written
+// to pout, and packed to bf16 in pb for the dV product).
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_p_scores(const bf16x8 (&kf)[D / 16], const bf16* Qs, const float* lse2,
+                                              float* pout, int lane, float c, int lo, int hi, bf16x8 (&pb)[4]) {
+  constexpr int KK = D / 16;
+  const int g = lane >> 5;
+  f32x16 s[2] = {zero16(), zero16()};
+  constexpr int NS = 2 * KK;  // step i = (kk, m2) = (i / 2, i % 2)
+  bf16x8 aq[NS];
+  prio_mfma();
+#pragma unroll
+  for (int i = 0; i < NS; ++i) aq[i] = frag_row<D>(Qs, (i & 1) * 32, (i >> 1) * 16, lane);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) s[i & 1] = mfma32(aq[i], kf[i >> 1], s[i & 1]);
+  if constexpr (kDkdvReadAhead > 0) {
+    constexpr int PF = kDkdvReadAhead;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (i + PF < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+  }
+  prio_base();
+  // P = exp2(S*c - LSE*log2e); rows m2*32 + rr*8 + g*4 + e of registers rr*4 + e
+#pragma unroll
+  for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float4 l2 = *reinterpret_cast<const float4*>(lse2 + m2 * 32 + rr * 8 + g * 4);
+      const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float p = fast_exp2(__builtin_fmaf(s[m2][rr * 4 + e], c, -l2v[e]));
+        if (MASK) {
+          const int off = m2 * 32 + rr * 8 + e;
+          if (off < lo || off > hi) p = 0.f;
+        }
+        s[m2][rr * 4 + e] = p;
+        pv[e] = p;
+      }
+      *reinterpret_cast<float4*>(pout + ((m2 * 4 + rr) * 64 + lane) * 4) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+    }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) pb[u] = pack8(s[u >> 1], (u & 1) * 8);
+}
+
+// Second part, common to masked and interior tiles (so that dV^T stays in one
+// set of registers): dV^T += P^T dO.
+template <int D>
+__device__ __forceinline__ void dkdv_p_dv(f32x16 (&dv)[D / 32], const bf16* dOs, const bf16x8 (&pb)[4], int lane) {
+  constexpr int DT = D / 32;
+  constexpr int NT2 = 4 * DT;  // step i = (ct, u) = (i / 4, i % 4)
+  bf16x8 tdo[NT2];
+#pragma unroll
+  for (int i = 0; i < NT2; ++i) tdo[i] = frag_tr<D>(dOs, (i & 3) * 16, (i >> 2) * 32, lane);
+#pragma unroll
+  for (int i = 0; i < NT2; ++i) dv[i >> 2] = mfma32(tdo[i], pb[i & 3], dv[i >> 2]);
+  if constexpr (kDkdvReadAhead > 0) {
+    constexpr int PF = kDkdvReadAhead;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PF, 1);
+#pragma unroll
+    for (int i = 0; i < NT2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+      if (i + PF < NT2) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+    }
+  }
+}
+
+// The dS wave's first phase: dP^T - D (the accumulators start from -D).
+template <int D>
+__device__ __forceinline__ void dkdv_ds_dp(const bf16x8 (&vf)[D / 16], const bf16* dOs, const float* ndl, int lane,
+                                           f32x16 (&dp)[2]) {
+  constexpr int KK = D / 16;
+  const int g = lane >> 5;
+#pragma unroll
+  for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float4 d4 = *reinterpret_cast<const float4*>(ndl + m2 * 32 + rr * 8 + g * 4);
+      dp[m2][rr * 4 + 0] = d4.x;
+      dp[m2][rr * 4 + 1] = d4.y;
+      dp[m2][rr * 4 + 2] = d4.z;
+      dp[m2][rr * 4 + 3] = d4.w;
+    }
+  constexpr int NS = 2 * KK;
+  bf16x8 ad[NS];
+  prio_mfma();
+#pragma unroll
+  for (int i = 0; i < NS; ++i) ad[i] = frag_row<D>(dOs, (i & 1) * 32, (i >> 1) * 16, lane);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) dp[i & 1] = mfma32(ad[i], vf[i >> 1], dp[i & 1]);
+  if constexpr (kDkdvReadAhead > 0) {
+    constexpr int PF = kDkdvReadAhead;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (i + PF < NS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+  }
+  prio_base();
+}
+
+// The dS wave's second phase: dS = P (dP - D) with P from pin (zero where the
+// P wave masked it), then dK^T += dS^T Q.
+template <int D>
+__device__ __forceinline__ void dkdv_ds_dk(f32x16 (&dk)[D / 32], const bf16* Qs, const float* pin, int lane,
+                                           f32x16 (&dp)[2]) {
+  constexpr int DT = D / 32;
+#pragma unroll
+  for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float4 p4 = *reinterpret_cast<const float4*>(pin + ((m2 * 4 + rr) * 64 + lane) * 4);
+      dp[m2][rr * 4 + 0] *= p4.x;
+      dp[m2][rr * 4 + 1] *= p4.y;
+      dp[m2][rr * 4 + 2] *= p4.z;
+      dp[m2][rr * 4 + 3] *= p4.w;
+    }
+  bf16x8 sb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) sb[u] = pack8(dp[u >> 1], (u & 1) * 8);
+  constexpr int NT2 = 4 * DT;
+  bf16x8 tq[NT2];
+#pragma unroll
+  for (int i = 0; i < NT2; ++i) tq[i] = frag_tr<D>(Qs, (i & 3) * 16, (i >> 2) * 32, lane);
+#pragma unroll
+  for (int i = 0; i < NT2; ++i) dk[i >> 2] = mfma32(tq[i], sb[i & 3], dk[i >> 2]);
+  if constexpr (kDkdvReadAhead > 0) {
+    constexpr int PF = kDkdvReadAhead;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * PF, 1);
+#pragma unroll
+    for (int i = 0; i < NT2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+      if (i + PF < NT2) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(8 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_roles_kernel(BwdArgs a) {
+  constexpr int BMQ = 64;
+  constexpr int BN = 128;
+  constexpr int KK = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int TILE = TileLayout<D>::template elems<BMQ>();
+  // two stages of the Q and dO tiles, each its own array
+  __shared__ __attribute__((aligned(16))) bf16 sQ0[TILE], sO0[TILE], sQ1[TILE], sO1[TILE];
+  // P of the four P waves: [key slice][(m2, rr)][lane][4]
+  __shared__ __attribute__((aligned(16))) float sP[4][8 * 64 * 4];
+  __shared__ __attribute__((aligned(16))) float sstat[2][2][BMQ];  // [stage][LSE*log2e, -D]
+
+  const int wid = wave_id();      // scalar
+  const bool ds_role = wid >= 4;  // waves 4..7: dS waves
+  const int kw = wid & 3;         // key slice
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  int slot, b, hkv, kb, part, nparts;
+  decode_kunit(blockIdx.x, a.B, a.Hkv, slot, b, hkv);
+  dkdv_slot(slot, a.nblk, a.parts, a.S, a.causal, false, kb, part, nparts);
+  const int S = a.S;
+  const int L = valid_len(a.seqlens, b, S);
+  const int G = a.Hq / a.Hkv;
+  const int64_t qs = a.sq.s;
+  const int64_t os = a.so.s;
+  const int64_t ks = a.skv.s;
+
+  const int j0 = kb * BN;
+  const int jw = j0 + kw * 32;
+  const int j = jw + l32;  // the lane's key row
+  const float c = a.scale * kLog2e;
+
+  // the P wave keeps K rows, the dS wave V rows (B operands of S^T and dP^T)
+  const bf16* KVb = (ds_role ? a.v : a.k) + b * a.skv.b + hkv * a.skv.h;
+  bf16x8 kv[KK];
+  f32x16 acc[DT];  // dV^T (P wave) or dK^T (dS wave)
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    kv[kk] = j < L ? *reinterpret_cast<const bf16x8*>(KVb + (int64_t)j * ks + kk * 16 + g * 8) : zero_bf16x8();
+#pragma unroll
+  for (int ct = 0; ct < DT; ++ct) acc[ct] = zero16();
+
+  const int qt0 = a.causal ? j0 / BMQ : 0;  // first query tile with rows at or below the block
+  const int nq = (j0 < L) ? (L - 1) / BMQ - qt0 + 1 : 0;  // query tiles per head
+  const int iters = nq * G;                               // (head, query tile) pairs
+  const int it_lo = (int)((int64_t)part * iters / nparts);
+  const int it_hi = (int)((int64_t)(part + 1) * iters / nparts);
+  const int trips = it_hi - it_lo;
+
+  float st_reg = 0.f;  // wave 0 carries LSE, wave 1 D
+  auto fetch = [&](int t, const KVBuf& buf) {
+    const int it = it_lo + t;
+    const int hh = it / nq;
+    const int qt = qt0 + (it - hh * nq);
+    const int h = hkv * G + hh;
+    if (wid < 2) {
+      // raw value only (arithmetic here would make the compiler wait for the
+      // load before the step's compute); the pointer is chosen on the scalar
+      // wave index
+      const int i = qt * BMQ + lane;
+      const float* src = wid == 0 ? a.lse : a.delta;
+      st_reg = 0.f;
+      if (i < L) st_reg = src[((int64_t)b * a.Hq + h) * S + i];
+    }
+    const bf16* Qb = a.q + b * a.sq.b + h * a.sq.h;
+    const bf16* dOb = a.d_o + b * a.so.b + h * a.so.h;
+    tile_load_lds<BMQ, D, 8>(Qb, qs, qt * BMQ, L, buf.k, wid, lane);
+    tile_load_lds<BMQ, D, 8>(dOb, os, qt * BMQ, L, buf.v, wid, lane);
+  };
+  auto land = [&](int t, const KVBuf& buf) {
+    if (t < trips && wid < 2) sstat[buf.idx][wid][lane] = wid == 0 ? st_reg * kLog2e : -st_reg;
+  };
+  // 0: the tile has no (key, query) pair of this slice; 1: masked; 2: interior
+  auto kind = [&](int t, int& i0) {
+    const int it = it_lo + t;
+    const int hh = it / nq;
+    i0 = (qt0 + (it - hh * nq)) * BMQ;
+    if ((a.causal && i0 + BMQ - 1 < jw) || jw >= L) return 0;
+    return ((a.causal && i0 < jw + 31) || (i0 + BMQ > L) || (jw + 32 > L)) ? 1 : 2;
+  };
+  float* const pslot = &sP[kw][0];
+  // the barrier between the phases publishes P only: it waits for the wave's
+  // own LDS accesses (lgkmcnt) and leaves the next tile's copy in flight, which
+  // __syncthreads() (a workgroup fence) would drain; the compiler fences keep
+  // memory operations on their side of it
+  auto phase_barrier = []() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto compute_p = [&](int t, const KVBuf& buf) {
+    int i0;
+    const int kd = kind(t, i0);
+    bf16x8 pb[4];
+    if (kd == 1) {
+      const int lo = a.causal ? j - i0 - g * 4 : -(1 << 30);  // causal: i >= j
+      const int hi = (j < L) ? L - 1 - i0 - g * 4 : -1;       // i < L, and no rows when j >= L
+      dkdv_p_scores<D, true>(kv, buf.k, sstat[buf.idx][0], pslot, lane, c, lo, hi, pb);
+    } else if (kd == 2) {
+      dkdv_p_scores<D, false>(kv, buf.k, sstat[buf.idx][0], pslot, lane, c, 0, 0, pb);
+    }
+    phase_barrier();  // P is in LDS for the partner
+    if (kd != 0) dkdv_p_dv<D>(acc, buf.v, pb, lane);
+  };
+  auto compute_ds = [&](int t, const KVBuf& buf) {
+    int i0;
+    const int kd = kind(t, i0);
+    f32x16 dp[2];
+    if (kd != 0) dkdv_ds_dp<D>(kv, buf.v, sstat[buf.idx][1], lane, dp);
+    phase_barrier();  // the partner's P is in LDS
+    if (kd != 0) dkdv_ds_dk<D>(acc, buf.k, pslot, lane, dp);
+  };
+  // each role runs its own copy of the pipeline loop (same steps, same
+  // barriers), so that its accumulators stay in one set of registers
+  KVBuf b0{sQ0, sO0, 0}, b1{sQ1, sO1, 1};
+  // the first tile travels together with the K or V rows above: one wait
+  tile_pipeline_start(trips, b0, fetch);
+  wait_vmem();
+  if (ds_role)
+    tile_pipeline(trips, b0, b1, fetch, land, compute_ds, /*started=*/true);
+  else
+    tile_pipeline(trips, b0, b1, fetch, land, compute_p, /*started=*/true);
+
+  if (a.parts > 1) {
+    // this part's unscaled fp32 sums for the valid key rows (dV from the P
+    // waves, dK from the dS waves); the reduce pass adds the parts
+    if (j < L) {
+      const int64_t prow = ((int64_t)part * a.B + b) * S;
+      float* dst = (ds_role ? a.part_dk : a.part_dv) + ((prow + j) * a.Hkv + hkv) * D;
+#pragma unroll
+      for (int ct = 0; ct < DT; ++ct)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          *reinterpret_cast<float4*>(dst + ct * 32 + rr * 8 + g * 4) =
+              make_float4(acc[ct][rr * 4 + 0], acc[ct][rr * 4 + 1], acc[ct][rr * 4 + 2], acc[ct][rr * 4 + 3]);
+    }
+    return;
+  }
+
+  // Epilogue: dK = scale * dK^T (and the rotation's adjoint), dV = dV^T,
+  // transposed back; the lane owns key row j; padded rows get zeros
+  if (j < S) {
+    const bool valid = j < L;
+    bf16* dst = (ds_role ? a.dk : a.dv) + b * a.skv.b + hkv * a.skv.h;
+#pragma unroll
+    for (int ct = 0; ct < DT; ++ct)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[ct][rr * 4 + e];
+        if (ds_role) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] *= a.scale;
+          if (a.rope) rope_adjoint4(a.rf, ct * 32 + rr * 8, g, j, x);
+        }
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (bf16)(valid ? x[e] : 0.f);
+        *reinterpret_cast<bf16x4*>(dst + (int64_t)j * ks + ct * 32 + rr * 8 + g * 4) = o4;
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // dK/dV reduce (split dK/dV pass only): dK = scale * sum_p part_dk[p], dV =
 // sum_p part_dv[p] over the parts in a fixed order (deterministic), the
 // rotation's adjoint applied to dK, rounded to bf16 and written through the
@@ -1604,8 +1930,12 @@ hipError_t dkdv_d(const Problem& pr, const void* q, const void* k, const void* v
             cdiv(pr.S, 128 * NTJ), pr.scale, pr.causal, pr.rope_base > 0.f, rope_freq(pr), pr.sq, pr.skv, pr.so,
             nullptr, nullptr, parts, part_dk, part_dv};
   constexpr int GR = Tiles<D>::DKDV_GROUPS;
-  hipError_t e = launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR>,
-                        (int64_t)a.nblk * parts * pr.B * pr.Hkv, a, stream, kThreads * GR);
+  hipError_t e;
+  if constexpr (D == 128)
+    e = launch((const void*)&bwd_dkdv_roles_kernel<D>, (int64_t)a.nblk * parts * pr.B * pr.Hkv, a, stream, 8 * 64);
+  else
+    e = launch((const void*)&bwd_dkdv_kernel<D, NTJ, Tiles<D>::DKDV_OCC, GR>, (int64_t)a.nblk * parts * pr.B * pr.Hkv,
+               a, stream, kThreads * GR);
   if (e != hipSuccess || parts == 1) return e;
   const int64_t threads = (int64_t)pr.B * pr.S * pr.Hkv * (D / 4);
   return launch((const void*)&dkdv_reduce_kernel<D>, (threads + kThreads - 1) / kThreads, a, stream);
