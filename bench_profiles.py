@@ -37,12 +37,21 @@ def _pmc_rows(d):
     return rows
 
 
+# The dK/dV pass's kernel under either of its implementations (at d=128 the
+# role split has its own name); both are filed under the pass's name.
+KERNEL_ALIASES = {"bwd_dkdv_kernel": ("bwd_dkdv_kernel", "bwd_dkdv_roles_kernel")}
+
+
+def _is_kernel(name, kname):
+    return any(alias in name for alias in KERNEL_ALIASES.get(kname, (kname,)))
+
+
 def _avg_counter(rows, match, counter):
-    """Mean over dispatches of one counter for the kernels whose name contains
-    `match` (a counter reported per XCD or per instance is summed per dispatch)."""
+    """Mean over dispatches of one counter for the kernels `match` names
+    (a counter reported per XCD or per instance is summed per dispatch)."""
     vals = {}
     for r in rows:
-        if match in r.get("Kernel_Name", "") and r.get("Counter_Name") == counter:
+        if _is_kernel(r.get("Kernel_Name", ""), match) and r.get("Counter_Name") == counter:
             key = r.get("Dispatch_Id") or r.get("Correlation_Id") or str(len(vals))
             vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
     return (sum(vals.values()) / len(vals), len(vals)) if vals else (None, 0)
@@ -183,7 +192,7 @@ def trace_summary(args):
     }
     names = list(KERNEL_NAMES.values()) + list(TRACE_EXTRA.values())
     for row in _kernel_stats(args.trace):
-        kname = next((k for k in names if k in row["Name"]), None)
+        kname = next((k for k in names if _is_kernel(row["Name"], k)), None)
         if kname is None:
             continue
         if kname in share:

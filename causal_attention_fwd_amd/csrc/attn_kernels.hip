@@ -604,6 +604,27 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
   }
 }
 
+// (head, query tile) of a dK/dV block's iteration it (0 .. nq*G - 1).
+// down: the query tiles from the last one down to the block's first, each for
+// every head of the group in turn. The blocks of a kv group that run at the
+// same time (on one XCD) then read the same Q and dO tiles at the same step
+// and its L2 serves them; walking up from each block's own diagonal they read
+// different tiles (longseq's d=128 dK/dV fetched 9.9 GB from HBM per launch,
+// 2.1 GB walking down, 2 % faster). The d=64 pass keeps the upward walk,
+// each head's tiles from the diagonal up: walking down cut llama1b's fetch
+// from 159 to 138 MB but not its time (0.4 % slower), and with a split it
+// would put every head's masked diagonal tile in a block's last part.
+__device__ __forceinline__ void dkdv_trip(int it, int nq, int G, int qt0, bool down, int& hh, int& qt) {
+  if (down) {
+    const int r = it / G;
+    hh = it - r * G;
+    qt = qt0 + nq - 1 - r;
+  } else {
+    hh = it / nq;
+    qt = qt0 + (it - hh * nq);
+  }
+}
+
 // Key block, part and part count of a dK/dV workgroup from its slot in its
 // unit (dkdv_part_base gives the deal). Without a split and with pair_ends,
 // the second half of the slots walks the key blocks from the far end, so that
@@ -708,8 +729,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   auto fetch = [&](int trip, const KVBuf& buf) {
     const int it = it_lo + trip * GROUPS + grp;
     if (it >= it_hi) return;
-    const int hh = it / nq;
-    const int qt = qt0 + (it - hh * nq);
+    int hh, qt;
+    dkdv_trip(it, nq, G, qt0, false, hh, qt);
     const int h = hkv * G + hh;
     if (swave < 2) {
       // raw value only: any arithmetic on it here would make the compiler wait
@@ -734,8 +755,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   auto compute = [&](int trip, const KVBuf& buf) {
     const int it = it_lo + trip * GROUPS + grp;
     if (it >= it_hi) return;
-    const int hh = it / nq;
-    const int qt = qt0 + (it - hh * nq);
+    int hh, qt;
+    dkdv_trip(it, nq, G, qt0, false, hh, qt);
     const int i0 = qt * BMQ;
     // skip when every query row of the tile is above this wave's key rows, or
     // the wave's keys are all padding
@@ -1066,8 +1087,8 @@ void bwd_dkdv_roles_kernel(BwdArgs a) {
   float st_reg = 0.f;  // wave 0 carries LSE, wave 1 D
   auto fetch = [&](int t, const KVBuf& buf) {
     const int it = it_lo + t;
-    const int hh = it / nq;
-    const int qt = qt0 + (it - hh * nq);
+    int hh, qt;
+    dkdv_trip(it, nq, G, qt0, a.parts == 1, hh, qt);
     const int h = hkv * G + hh;
     if (wid < 2) {
       // raw value only (arithmetic here would make the compiler wait for the
@@ -1089,8 +1110,9 @@ void bwd_dkdv_roles_kernel(BwdArgs a) {
   // 0: the tile has no (key, query) pair of this slice; 1: masked; 2: interior
   auto kind = [&](int t, int& i0) {
     const int it = it_lo + t;
-    const int hh = it / nq;
-    i0 = (qt0 + (it - hh * nq)) * BMQ;
+    int hh, qt;
+    dkdv_trip(it, nq, G, qt0, a.parts == 1, hh, qt);
+    i0 = qt * BMQ;
     if ((a.causal && i0 + BMQ - 1 < jw) || jw >= L) return 0;
     return ((a.causal && i0 < jw + 31) || (i0 + BMQ > L) || (jw + 32 > L)) ? 1 : 2;
   };
