@@ -2,8 +2,11 @@
 """Benchmark: causal bf16 attention fwd + bwd on one MI355X.
 
 One step = the whole path over one batch of resident synthetic inputs:
-attn_fwd -> attn_bwd_preprocess -> attn_bwd_dkdv -> attn_bwd_dq (the last two
-are exactly the two launches attn_bwd makes). The step is timed as replays of
+attn_fwd -> attn_bwd_dq_delta (the dQ pass, which also computes the
+preprocess's D = rowsum(dO * O)) -> attn_bwd_dkdv (which reads that D); the
+last two are exactly the launches attn_bwd_fused makes.
+--separate-preprocess runs attn_fwd -> attn_bwd_preprocess -> attn_bwd_dkdv ->
+attn_bwd_dq instead (the last two being attn_bwd). The step is timed as replays of
 its captured HIP graph (no host-side launch cost; --eager times Python-issued
 launches instead); per-kernel times come from an eager pass with HIP events.
 Before anything is measured the step runs untimed for --clock-warmup-ms
@@ -233,34 +236,36 @@ def run(args):
         qa, ka = torch.empty_like(q), torch.empty_like(k)
     ws = attn.bwd_workspace(q, k)  # the backward's workspace (None when the shape needs none)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        if args.rope:
+    # the step's launches in order. Default: the backward with the preprocess
+    # folded into the dQ pass (attn_bwd_dq_delta computes D, then
+    # attn_bwd_dkdv reads it: the launches of attn_bwd_fused, issued as two
+    # calls so that each kernel has its own events); --separate-preprocess:
+    # attn_bwd_preprocess, then the two passes of attn_bwd.
+    order = (["rope"] if args.rope else []) + (["fwd", "pre", "dkdv", "dq"] if args.separate_preprocess
+                                                else ["fwd", "dq", "dkdv"])
+
+    def launch_one(name):
+        if name == "rope":
             attn.attn_rope(q, k, qa, ka, rb)
-        if ev is not None:
-            ev[5].record()
-        attn.attn_fwd(qa, ka, v, o, lse, scale, sl, cz)
-        if ev is not None:
-            ev[1].record()
-        if args.fused_bwd:
-            # preprocess folded into dQ, which runs first; events 2 and 3 bracket dQ + D
-            if ev is not None:
-                ev[2].record()
-            attn.attn_bwd_fused(qa, ka, v, o, do, lse, delta, dq, dk, dv, scale, sl, ws, cz, rb)
-            if ev is not None:
-                ev[3].record()
-                ev[4].record()
-        else:
+        elif name == "fwd":
+            attn.attn_fwd(qa, ka, v, o, lse, scale, sl, cz)
+        elif name == "pre":
             attn.attn_bwd_preprocess(o, do, delta, sl)
-            if ev is not None:
-                ev[2].record()
+        elif name == "dkdv":
             attn.attn_bwd_dkdv(qa, ka, v, do, lse, delta, dk, dv, scale, sl, cz, rb, ws)
-            if ev is not None:
-                ev[3].record()
+        elif args.separate_preprocess:
             attn.attn_bwd_dq(qa, ka, v, do, lse, delta, dq, scale, sl, cz, rb)
+        else:
+            attn.attn_bwd_dq_delta(qa, ka, v, o, do, lse, delta, dq, scale, sl, cz, rb)
+
+    def step(ev=None):
+        # ev[i] is recorded before launch i, ev[len(order)] after the last
+        for i, name in enumerate(order):
             if ev is not None:
-                ev[4].record()
+                ev[i].record()
+            launch_one(name)
+        if ev is not None:
+            ev[len(order)].record()
 
     warm = clock_warmup(torch, lambda i: step(), args.clock_warmup_ms)
     for _ in range(args.warmup):
@@ -273,7 +278,7 @@ def run(args):
         # default: no host-side launch cost in the timed step)
         def capture():
             return attn.capture_step(q, k, v, do, o, lse, delta, dq, dk, dv, scale, sl, causal, ws,
-                                     fused=args.fused_bwd, rope_base=rb, q_rot=qa if args.rope else None,
+                                     fused=not args.separate_preprocess, rope_base=rb, q_rot=qa if args.rope else None,
                                      k_rot=ka if args.rope else None)
         g_step = time_graph_replays(torch, [capture], args)
         launch = "hip graph" if g_step is not None else "eager (graph capture failed)"
@@ -284,7 +289,7 @@ def run(args):
     # keep the GPU busy while the host enqueues it (a few ms for the default
     # steps): the events then time the kernels back to back, not the host's
     # launch gaps.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)] for _ in range(args.steps)]
     if g_step is not None:
         for i in range(max(10, math.ceil(30.0 / g_step))):
             args.graphs[i % len(args.graphs)].replay()
@@ -293,18 +298,10 @@ def run(args):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = ["fwd", "pre", "dkdv", "dq"]
-    per = {n: 0.0 for n in names}
-    rope_ms = 0.0
-    for ev in events:
-        per["fwd"] += ev[5].elapsed_time(ev[1])
-        for j, n in enumerate(names[1:], start=1):
-            per[n] += ev[j].elapsed_time(ev[j + 1])
-        rope_ms += ev[0].elapsed_time(ev[5])
-    per = {n: per[n] / args.steps for n in names}           # ms per launch
-    rope_ms /= args.steps
+    per = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps  # ms per launch
+           for i, n in enumerate(order)}
     # per-step event times (first to last launch of the step): median, min, p90
-    step_ev = sorted(ev[0].elapsed_time(ev[4]) for ev in events)
+    step_ev = sorted(ev[0].elapsed_time(ev[-1]) for ev in events)
     step_stats = {"median": round(step_ev[len(step_ev) // 2], 4), "min": round(step_ev[0], 4),
                   "p90": round(step_ev[min(len(step_ev) - 1, (9 * len(step_ev)) // 10)], 4)}
     ms_step = wall * 1e3 / args.steps
@@ -313,16 +310,9 @@ def run(args):
         ms_step = g_step
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
 
-    # roofline of the dominant kernel
-    dom = max(per, key=per.get)
-    if args.fused_bwd:
-        # one call launches dQ (+D) and dK/dV back to back: priced together
-        # against the backward's algorithmic flops
-        achieved = fl["bwd"] / (per["dkdv"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "kernel": "bwd_dq_kernel+bwd_dkdv_kernel (attn_bwd_fused)",
-                "ms_per_launch": per["dkdv"], "traffic": None}
-    elif dom == "pre":
+    # roofline of the dominant kernel (the RoPE pre-pass is priced in hbm_rotated)
+    dom = max((n for n in order if n != "rope"), key=per.get)
+    if dom == "pre":
         alg_bytes = 2.0 * B * S * Hq * d * 2 + B * Hq * S * 4.0
         achieved = alg_bytes / (per[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -332,31 +322,27 @@ def run(args):
         achieved = share / (per[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS}
-    if not args.fused_bwd:
-        roof["kernel"] = KERNEL_NAMES[dom]
-        roof["ms_per_launch"] = per[dom]
-        roof["traffic"] = read_traffic(dom, w.name) if (causal and not args.rope) else None
+    roof["kernel"] = KERNEL_NAMES[dom]
+    roof["ms_per_launch"] = per[dom]
+    roof["traffic"] = read_traffic(dom, w.name) if (causal and not args.rope) else None
+    label = {n: KERNEL_NAMES.get(n, "rope_kernel") for n in order}
+    if not args.separate_preprocess:
+        label["dq"] = "bwd_dq_kernel (computes D)"
 
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": dict(w.describe(), causal=causal, launch=launch, fused_bwd=bool(args.fused_bwd),
+        "config": dict(w.describe(), causal=causal, launch=launch, step_launches=[label[n] for n in order],
                        valid_pairs_per_head=fl["pairs_per_head"],
                        algorithmic_gflop_per_step=round(fl["total"] / 1e9, 3),
                        rope_base=rb if args.rope else None),
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "clock_warmup": {"before_eager_pass": warm, "before_graph_timing": getattr(args, "graph_clock_warmup", None)},
         "step_event_ms": step_stats,
-        "kernel_ms": dict({KERNEL_NAMES[n]: round(per[n], 4) for n in names} if not args.fused_bwd else
-                          {"fwd_kernel": round(per["fwd"], 4),
-                           "attn_bwd_fused (bwd_dq_kernel + bwd_dkdv_kernel)": round(per["dkdv"], 4)},
-                          **({"rope_kernel": round(rope_ms, 4)} if args.rope else {})),
-        "kernel_tflops": ({KERNEL_NAMES[n]: round(s / (per[n] * 1e-3) / 1e12, 1)
-                           for n, s in (("fwd", fl["fwd"]), ("dkdv", fl["bwd_dkdv"]), ("dq", fl["bwd_dq"]))}
-                          if not args.fused_bwd else
-                          {"fwd_kernel": round(fl["fwd"] / (per["fwd"] * 1e-3) / 1e12, 1),
-                           "attn_bwd_fused": round(fl["bwd"] / (per["dkdv"] * 1e-3) / 1e12, 1)}),
+        "kernel_ms": {label[n]: round(per[n], 4) for n in order},
+        "kernel_tflops": {label[n]: round(s / (per[n] * 1e-3) / 1e12, 1)
+                          for n, s in (("fwd", fl["fwd"]), ("dkdv", fl["bwd_dkdv"]), ("dq", fl["bwd_dq"]))},
         "roofline": roof,
     }
     if not args.no_hbm:
@@ -577,8 +563,9 @@ def main():
                     help="(the default) time replays of the step captured in one HIP graph")
     ap.add_argument("--non-causal", action="store_true",
                     help="bidirectional attention (causal = 0): every key of the valid prefix, all pairs priced")
-    ap.add_argument("--fused-bwd", action="store_true",
-                    help="attn_bwd_fused: the preprocess folded into the dQ pass (3 launches per step)")
+    ap.add_argument("--separate-preprocess", action="store_true",
+                    help="the backward as attn_bwd_preprocess + attn_bwd (4 launches per step) instead of the "
+                         "default attn_bwd_dq_delta + attn_bwd_dkdv (the launches of attn_bwd_fused)")
     ap.add_argument("--rope", action="store_true",
                     help="rotary position embedding: attn_rope pre-pass, backward with the fused adjoint")
     ap.add_argument("--rope-base", type=float, default=10000.0)

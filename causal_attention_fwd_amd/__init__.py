@@ -14,6 +14,7 @@ Entry points (same names as the C ABI):
     attn_bwd_dkdv(q, k, v, d_o, lse, delta, dk, dv, scale, seqlens=None, workspace=None)
     attn_bwd_dq(q, k, v, d_o, lse, delta, dq, scale, seqlens=None)
     attn_bwd_fused(q, k, v, o, d_o, lse, delta, dq, dk, dv, scale, seqlens=None, workspace=None)
+    attn_bwd_dq_delta(q, k, v, o, d_o, lse, delta, dq, scale, seqlens=None)
     attn_decode_workspace_bytes(B, Sq, Smax, Hq, Hkv, d)
     attn_decode(q, k_cache, v_cache, o, lse, scale, cache_lens=None, workspace=None)
     attn_decode_noalloc(q, k_cache, v_cache, o, lse, scale, cache_lens=None)
@@ -27,7 +28,7 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["attn_rope", "rope", "attn_bwd_fused", "capture_decode", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
+__all__ = ["attn_rope", "rope", "attn_bwd_fused", "attn_bwd_dq_delta", "capture_decode", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
            "attn_bwd_dkdv", "attn_bwd_dq", "bwd_workspace", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_noalloc", "attn_status_string",
            "forward", "backward", "decode", "capture_step", "AttnError", "library_path", "load_library",
            "STATUS"]
@@ -40,7 +41,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3:
 
 # The symbols include/attn.h declares.
 EXPORTED = ("attn_rope", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_dkdv",
-            "attn_bwd_dq", "attn_bwd_fused", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_noalloc",
+            "attn_bwd_dq", "attn_bwd_fused", "attn_bwd_dq_delta", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_noalloc",
             "attn_status_string")
 
 
@@ -103,6 +104,8 @@ def load_library():
     lib.attn_decode_noalloc.restype = i32
     lib.attn_bwd_fused.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_bwd_fused.restype = i32
+    lib.attn_bwd_dq_delta.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_bwd_dq_delta.restype = i32
     lib.attn_rope.argtypes = [shp, vp, vp, vp, vp, vp]
     lib.attn_rope.restype = i32
     lib.attn_status_string.argtypes = [i32]
@@ -357,6 +360,26 @@ def attn_bwd_fused(q, k, v, o, d_o, lse, delta, dq, dk, dv, scale: float, seqlen
     ws_ptr, ws_bytes = _workspace_arg(workspace, q, k)
     _call(load_library().attn_bwd_fused, "attn_bwd_fused", ctypes.byref(shape), *[ctypes.c_void_p(p) for p in ptrs],
           ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), _stream())
+
+
+def attn_bwd_dq_delta(q, k, v, o, d_o, lse, delta, dq, scale: float, seqlens=None, causal: int = 1,
+                      rope_base: float = 0.0):
+    """D, dQ <- the dQ pass with the preprocess folded in (writes `delta` and
+    `dq`); followed by attn_bwd_dkdv it is attn_bwd_fused."""
+    torch = _torch()
+    shape, (B, S, Hq, Hkv, d) = _shape_from(q, k, scale, seqlens, causal, rope_base, qg=[("q", q)],
+                                            kvg=[("k", k), ("v", v)],
+                                            og=[("o", o), ("d_o", d_o), ("dq", dq)])
+    ptrs = [_check_gpu("q", q, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("k", k, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("v", v, torch.bfloat16, (B, S, Hkv, d), True),
+            _check_gpu("o", o, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("d_o", d_o, torch.bfloat16, (B, S, Hq, d), True),
+            _check_gpu("lse", lse, torch.float32, (B, Hq, S)),
+            _check_gpu("delta", delta, torch.float32, (B, Hq, S)),
+            _check_gpu("dq", dq, torch.bfloat16, (B, S, Hq, d), True)]
+    _call(load_library().attn_bwd_dq_delta, "attn_bwd_dq_delta", ctypes.byref(shape),
+          *[ctypes.c_void_p(p) for p in ptrs], _stream())
 
 
 # ------------------------------------------------------------------ decode

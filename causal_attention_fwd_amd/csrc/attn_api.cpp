@@ -216,6 +216,16 @@ attn_status attn_bwd_fused(const attn_shape* shape, const void* q, const void* k
   return from_hip(attn::launch_bwd_dkdv(pr, q, k, v, d_o, lse, delta, dk, dv, workspace, stream));
 }
 
+attn_status attn_bwd_dq_delta(const attn_shape* shape, const void* q, const void* k, const void* v, const void* o,
+                              const void* d_o, const float* lse, float* delta, void* dq, hipStream_t stream) {
+  attn::Problem pr;
+  attn_status st = check_shape(shape, &pr);
+  if (st != ATTN_OK) return st;
+  st = check_ptrs({q, k, v, o, d_o, lse, delta, dq});
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd_dq_with_delta(pr, q, k, v, o, d_o, lse, delta, dq, stream));
+}
+
 size_t attn_decode_workspace_bytes(const attn_decode_shape* shape) {
   attn::DecodeProblem pr;
   if (check_decode_shape(shape, &pr) != ATTN_OK) return 0;

@@ -209,6 +209,21 @@ attn_status attn_bwd_fused(const attn_shape* shape, const void* q, const void* k
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The first launch of attn_bwd_fused on its own (same operation and citation:
+ * the dQ pass of the backward with the preprocess folded in). It computes
+ * D = rowsum(dO * O) from the O and dO rows it loads (fp32 from the bf16
+ * inputs, 0 on padded rows), writes it to `delta` [B,Hq,S] fp32 (an output
+ * here) and forms dQ [B,S,Hq,d] bf16 with it. attn_bwd_dq_delta followed on
+ * the same stream by attn_bwd_dkdv, which then reads that D, enqueues exactly
+ * the launches of attn_bwd_fused; a caller splits the two to time them or to
+ * place other work between them. O shares the o_stride triple with dO and dQ.
+ * Same validation and error codes as attn_bwd_dq; no workspace.
+ * Deterministic.
+ */
+attn_status attn_bwd_dq_delta(const attn_shape* shape, const void* q, const void* k, const void* v, const void* o,
+                              const void* d_o, const float* lse, float* delta, void* dq, hipStream_t stream);
+
+/*
  * Decode: attention of Sq new queries per sequence against a key/value cache
  * (inference). "AxiomLM" (PyPI page), "Key Features" and "Zero-Overhead
  * Inference & Streaming Generation": a state-cached key/value decode engine,

@@ -97,6 +97,12 @@ int main(void) {
   n = g_stub_launches;
   expect("fused", attn_bwd_fused(&s, P(1), P(2), P(3), P(4), P(6), (float*)P(5), (float*)P(7), P(8), P(9), P(10),
                                  P(15), attn_bwd_workspace_bytes(&s), 0), ATTN_OK, n, 2);
+  n = g_stub_launches;
+  expect("dq delta", attn_bwd_dq_delta(&s, P(1), P(2), P(3), P(4), P(6), (float*)P(5), (float*)P(7), P(8), 0),
+         ATTN_OK, n, 1);
+  n = g_stub_launches;
+  expect("dq delta null o", attn_bwd_dq_delta(&s, P(1), P(2), P(3), NULL, P(6), (float*)P(5), (float*)P(7), P(8), 0),
+         ATTN_ERR_INVALID_ARG, n, 0);
   s.rope_base = 10000.f;
   n = g_stub_launches; expect("rope", attn_rope(&s, P(1), P(2), P(11), P(12), 0), ATTN_OK, n, 1);
   s.rope_base = 0.f;

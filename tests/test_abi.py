@@ -92,6 +92,10 @@ def _fused(lib, shape, ptrs=(GOOD,) * 10, ws=None, ws_bytes=0):
                               P(ws), ctypes.c_size_t(ws_bytes), P(0))
 
 
+def _dq_delta(lib, shape, ptrs=(GOOD,) * 8):
+    return lib.attn_bwd_dq_delta(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], P(0))
+
+
 def _pre(lib, shape, ptrs=(GOOD,) * 3):
     return lib.attn_bwd_preprocess(ctypes.byref(shape) if shape is not None else None, *[P(p) for p in ptrs], P(0))
 
@@ -298,6 +302,18 @@ def test_fused_backward_pointers(lib):
         assert _fused(lib, _shape(), ptrs) == 1
         ptrs[i] = ODD
         assert _fused(lib, _shape(), ptrs) == 3
+
+
+def test_dq_delta_pointers_and_shapes(lib):
+    assert _dq_delta(lib, None) == 1
+    for i in range(8):
+        ptrs = [GOOD] * 8
+        ptrs[i] = 0
+        assert _dq_delta(lib, _shape(), ptrs) == 1
+        ptrs[i] = ODD
+        assert _dq_delta(lib, _shape(), ptrs) == 3
+    assert _dq_delta(lib, _shape(d=96)) == 2
+    assert _dq_delta(lib, _shape(Hq=6, Hkv=4)) == 1
 
 
 def test_plain_c_client_and_struct_layouts(lib, tmp_path):

@@ -98,3 +98,51 @@ def test_fused_backward_llama1b_units():
                 "dK": got["dK"][b:b + 1, :, g:g + 1], "dV": got["dV"][b:b + 1, :, g:g + 1],
                 "LSE": got["LSE"][b:b + 1, hs], "D": got["D"][b:b + 1, hs]}
         compare(unit, ref, f"fused-llama1b[b={b},g={g}]")
+
+
+SPLIT_CASES = [
+    # B, S, Hq, Hkv, d, causal, padded range, rope base
+    (2, 130, 4, 2, 64, True, None, 0.0),
+    (3, 257, 6, 3, 128, True, (0, 257), 0.0),
+    (2, 300, 8, 2, 64, False, (100, 300), 10000.0),
+    (2, 1000, 64, 16, 64, True, (500, 1000), 0.0),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "B{}_S{}_H{}-{}_d{}_{}{}".format(
+    *c[:5], "causal" if c[5] else "bidir", "_rope" if c[7] else ""))
+def test_dq_delta_then_dkdv_is_the_fused_backward(case):
+    """attn_bwd_dq_delta then attn_bwd_dkdv on one stream: the launches of
+    attn_bwd_fused, so the same bits, and the oracle's gradients and D."""
+    B, S, Hq, Hkv, d, causal, rng, rb = case
+    say(f"dq_delta + dkdv B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} causal={causal} pad={rng} rope={rb}")
+    inp = make_inputs(B, S, Hq, Hkv, d, 5300 + S + d, padded=rng is not None, seqlen_range=rng)
+    q, k, v, do = (getattr(inp, n).to(DEV).contiguous() for n in ("q", "k", "v", "do"))
+    sl = inp.seqlens.to(DEV) if inp.seqlens is not None else None
+    if rb:
+        q, k = attn.rope(q, k, rb)
+    o, lse = attn.forward(q, k, v, inp.scale, sl, causal=causal)
+    outs = []
+    for split in (True, False):
+        delta = torch.full_like(lse, float("nan"))
+        dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+        if split:
+            attn.attn_bwd_dq_delta(q, k, v, o, do, lse, delta, dq, inp.scale, sl, int(causal), rb)
+            attn.attn_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, inp.scale, sl, int(causal), rb)
+        else:
+            attn.attn_bwd_fused(q, k, v, o, do, lse, delta, dq, dk, dv, inp.scale, sl, None, int(causal), rb)
+        outs.append((delta, dq, dk, dv))
+    torch.cuda.synchronize()
+    for name, a, b in zip(("D", "dQ", "dK", "dV"), *outs):
+        # bitwise: the bf16 / fp32 bit patterns (NaN-safe)
+        bits = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(a.view(bits).cpu(), b.view(bits).cpu()), name
+    host = lambda x: x.float().cpu().numpy()  # noqa: E731
+    delta, dq, dk, dv = outs[0]
+    got = {"O": host(o), "LSE": host(lse), "D": host(delta), "dQ": host(dq), "dK": host(dk), "dV": host(dv)}
+    qh, kh, vh, doh, slh = host_inputs(inp)
+    if rb:
+        ref = oracle_rope.backward(qh, kh, vh, doh, inp.scale, slh, rb, causal=causal, bf16_storage=True)
+    else:
+        ref = oracle.backward(qh, kh, vh, doh, inp.scale, slh, causal=causal)
+    compare(got, ref, f"dq_delta{case}")
