@@ -199,6 +199,9 @@ def trace_summary(args):
             def lines(avg_us, f=share[kname], kname=kname):
                 out = [f"algorithmic_gflop_per_launch: {f / 1e9:.3f}",
                        f"achieved_tflops_at_average: {f / (avg_us * 1e-6) / 1e12:.1f}"]
+                if kname == "bwd_dq_kernel":
+                    out.append("note: in the benchmark's default step this pass also computes D = rowsum(dO*O) "
+                               "(attn_bwd_dq_delta); with --separate-preprocess it reads D")
                 if kname == "bwd_dkdv_kernel" and parts > 1:
                     out.append(f"note: this shape splits its key blocks' query ranges over {per_block} "
                                f"parts; the dK/dV call is this kernel plus dkdv_reduce_kernel")
