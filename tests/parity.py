@@ -34,12 +34,23 @@ def to_gpu(inp):
     return t
 
 
-def run_gpu(inp, t=None, causal=True):
-    """fwd -> preprocess -> bwd on the GPU; returns host fp32 numpy arrays."""
+def run_gpu(inp, t=None, causal=True, bench_order=False):
+    """fwd -> preprocess -> bwd on the GPU; returns host fp32 numpy arrays.
+    bench_order: the benchmark's launch sequence instead, fwd ->
+    attn_bwd_dq_delta (dQ, forming D) -> attn_bwd_dkdv (reading that D)."""
     t = t or to_gpu(inp)
     o, lse = attn.forward(t["q"], t["k"], t["v"], inp.scale, t["seqlens"], causal=causal)
-    dq, dk, dv, delta = attn.backward(t["q"], t["k"], t["v"], o, t["do"], lse, inp.scale, t["seqlens"],
-                                      causal=causal)
+    if bench_order:
+        delta = torch.full_like(lse, float("nan"))
+        dq = torch.full_like(t["q"], float("nan"))
+        dk, dv = torch.full_like(t["k"], float("nan")), torch.full_like(t["v"], float("nan"))
+        attn.attn_bwd_dq_delta(t["q"], t["k"], t["v"], o, t["do"], lse, delta, dq, inp.scale, t["seqlens"],
+                               int(causal))
+        attn.attn_bwd_dkdv(t["q"], t["k"], t["v"], t["do"], lse, delta, dk, dv, inp.scale, t["seqlens"],
+                           int(causal))
+    else:
+        dq, dk, dv, delta = attn.backward(t["q"], t["k"], t["v"], o, t["do"], lse, inp.scale, t["seqlens"],
+                                          causal=causal)
     torch.cuda.synchronize()
     host = lambda x: x.float().cpu().numpy()  # noqa: E731
     return {"O": host(o), "LSE": host(lse), "D": host(delta), "dQ": host(dq), "dK": host(dk), "dV": host(dv)}

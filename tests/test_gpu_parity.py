@@ -2,7 +2,8 @@
 
 Small shapes are compared element by element over every output; the five
 named workloads run at their full sizes, in the launch configuration the
-benchmark times, and are compared on whole (sequence, kv head) units sampled
+benchmark times (and with the backward's other launch order, preprocess then
+attn_bwd), and are compared on whole (sequence, kv head) units sampled
 from the batch (every kv head and sequence of llama1b), plus properties that
 hold at any size over every unit (padding zeros, no NaN/Inf, D from the GPU's
 O, O within the range of its visible V rows, the gradient sum identities).
@@ -119,31 +120,47 @@ def test_workload_parity(name):
     w = WORKLOADS[name]
     say(f"workload {name}: {w.describe()} seed={w.seed}")
     inp = workload_inputs(w)
-    gpu = run_gpu(inp)
+    # the backward both ways: preprocess + attn_bwd, and the benchmark's
+    # launch sequence (attn_bwd_dq_delta forming D, then attn_bwd_dkdv)
+    runs = {"separate": run_gpu(inp)}
+    say(f"workload {name}: separate preprocess done; benchmark launch order")
+    runs["bench"] = run_gpu(inp, bench_order=True)
     say(f"workload {name}: GPU done, oracle running")
     units = _units(w, inp)
     if units is None:
         q, k, v, do, sl = host_inputs(inp)
-        compare(gpu, oracle.backward(q, k, v, do, inp.scale, sl), name)
+        ref = oracle.backward(q, k, v, do, inp.scale, sl)
+        for how, gpu in runs.items():
+            compare(gpu, ref, f"{name} ({how})")
     else:
         dtype = np.float32 if name == "longseq" else np.float64
         G = w.Hq // w.Hkv
         for b, hkv in units:
             say(f"workload {name}: unit b={b} kv_head={hkv}")
             ref = oracle_unit(inp, b, hkv, dtype)
-            compare(slice_unit(gpu, b, hkv, G), ref, f"{name}[b={b},g={hkv}]")
+            for how, gpu in runs.items():
+                compare(slice_unit(gpu, b, hkv, G), ref, f"{name}[b={b},g={hkv}] ({how})")
     # properties over the whole output
-    for key in ("O", "dQ", "dK", "dV", "D"):
-        assert np.all(np.isfinite(gpu[key])), key
-    whole_output_identities(inp, gpu, label=name)
-    if inp.seqlens is not None:
-        for b, L in enumerate(inp.seqlens.tolist()):
-            for key in ("O", "dQ", "dK", "dV"):
-                assert np.all(gpu[key][b, L:] == 0.0), (key, b)
-            assert np.all(np.isneginf(gpu["LSE"][b, :, L:]))
-            assert np.all(np.isfinite(gpu["LSE"][b, :, :L]))
-    else:
-        assert np.all(np.isfinite(gpu["LSE"]))
+    for how, gpu in runs.items():
+        for key in ("O", "dQ", "dK", "dV", "D"):
+            assert np.all(np.isfinite(gpu[key])), (how, key)
+        whole_output_identities(inp, gpu, label=f"{name} ({how})")
+        if inp.seqlens is not None:
+            for b, L in enumerate(inp.seqlens.tolist()):
+                for key in ("O", "dQ", "dK", "dV"):
+                    assert np.all(gpu[key][b, L:] == 0.0), (how, key, b)
+                assert np.all(np.isneginf(gpu["LSE"][b, :, L:]))
+                assert np.all(np.isfinite(gpu["LSE"][b, :, :L]))
+        else:
+            assert np.all(np.isfinite(gpu["LSE"]))
+    # D from the dQ pass and from the preprocess: fp32 sums of the same d
+    # products of bf16 values in two orders, so they differ by at most
+    # 2 * d * 2^-24 * sum |dO * O| (the same forward ran twice: O is identical)
+    np.testing.assert_array_equal(runs["bench"]["O"], runs["separate"]["O"])
+    _, _, _, do, _ = host_inputs(inp)
+    abs_sum = np.einsum("bshc->bhs", np.abs(do.astype(np.float64) * runs["bench"]["O"].astype(np.float64)))
+    bound = 2 * w.d * 2.0 ** -24 * abs_sum + 1e-30
+    assert np.all(np.abs(runs["bench"]["D"].astype(np.float64) - runs["separate"]["D"]) <= bound)
 
 
 # ------------------------------------------------------------------ contracts
