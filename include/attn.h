@@ -209,8 +209,10 @@ attn_status attn_bwd_fused(const attn_shape* shape, const void* q, const void* k
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * The first launch of attn_bwd_fused on its own (same operation and citation:
- * the dQ pass of the backward with the preprocess folded in). It computes
+ * The first launch of attn_bwd_fused on its own: the dQ pass of the fused
+ * flash-attention backward ("Axis", Zyora Labs page, feature list; D is the
+ * standard row term of the exact softmax gradient, as in attn_bwd_preprocess)
+ * with the preprocess folded in. It computes
  * D = rowsum(dO * O) from the O and dO rows it loads (fp32 from the bf16
  * inputs, 0 on padded rows), writes it to `delta` [B,Hq,S] fp32 (an output
  * here) and forms dQ [B,S,Hq,d] bf16 with it. attn_bwd_dq_delta followed on
