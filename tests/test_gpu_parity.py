@@ -61,6 +61,9 @@ def test_fuzz_every_element(case):
     q, k, v, do, sl = host_inputs(inp)
     ref = oracle.backward(q, k, v, do, inp.scale, sl)
     compare(gpu, ref, f"fuzz{case}")
+    # the benchmark's launch order: attn_bwd_dq_delta (D formed in the dQ pass), then attn_bwd_dkdv
+    say(f"fuzz case B={B} S={S} Hq={Hq} Hkv={Hkv} d={d} pad={rng} seed={seed}: attn_bwd_dq_delta/attn_bwd_dkdv")
+    compare(run_gpu(inp, bench_order=True), ref, f"fuzz{case} (dq_delta, dkdv)")
 
 
 # The split dK/dV pass deals each (sequence, kv head)'s workgroups to its key
