@@ -719,45 +719,85 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int nq = (j0 < L) ? (L - 1) / BMQ - qt0 + 1 : 0;  // query tiles per head
   const int iters = nq * G;                               // (head, query tile) pairs
   // this workgroup's share of them: [it_lo, it_hi)
-  const int it_lo = (int)((int64_t)part * iters / nparts);
-  const int it_hi = (int)((int64_t)(part + 1) * iters / nparts);
+  // (an unsplit block, the usual case, takes all of them without the 64-bit
+  // divisions, which cost a few hundred scalar instructions per workgroup)
+  const int it_lo = nparts == 1 ? 0 : (int)((int64_t)part * iters / nparts);
+  const int it_hi = nparts == 1 ? iters : (int)((int64_t)(part + 1) * iters / nparts);
   const int trips = (it_hi - it_lo + GROUPS - 1) / GROUPS;  // this group does it = it_lo + trip*GROUPS + grp
 
   float st_reg = 0.f;  // wave 0 of a group carries LSE, wave 1 D
   const KVBuf b0{sQ0 + grp * TILE, sO0 + grp * TILE, 0}, b1{sQ1 + grp * TILE, sO1 + grp * TILE, 1};
-  // this group handles (head, query tile) pair it = it_lo + trip * GROUPS + grp
+  // This group handles (head, query tile) pair it = it_lo + trip * GROUPS +
+  // grp: head hh = it / nq, query tile qt0 + it % nq. The pipeline fetches
+  // trip t + 1 and computes trip t, each in increasing order, so each keeps a
+  // cursor that steps GROUPS pairs per call instead of dividing per tile, and
+  // carries the offsets of the tile's first row in Q, dO and the LSE / D rows
+  // (no per-tile 64-bit products).
+  struct Cursor {
+    int r;                // query tile - qt0
+    int64_t qoff, ooff;   // elements to row (qt0 + r) * BMQ of head hkv*G + hh in Q, in dO
+    int64_t soff;         // index of that row in LSE / D
+  };
+  const int it_first = it_lo + grp;
+  const int nq1 = nq > 0 ? nq : 1;  // nq = 0 only when there are no trips
+  const int hh_first = it_first / nq1;
+  Cursor cur_f;
+  cur_f.r = it_first - hh_first * nq1;
+  {
+    const int h = hkv * G + hh_first;
+    const int64_t row = (int64_t)(qt0 + cur_f.r) * BMQ;
+    cur_f.qoff = b * a.sq.b + h * a.sq.h + row * qs;
+    cur_f.ooff = b * a.so.b + h * a.so.h + row * os;
+    cur_f.soff = ((int64_t)b * a.Hq + h) * S + row;
+  }
+  Cursor cur_c = cur_f;
+  // trips of this group that hold a pair (it < it_hi), computed once: behind
+  // the empty asm the compiler keeps the value instead of recomputing the
+  // 64-bit divisions of it_lo and it_hi at every use inside the loop
+  int my_trips = max(0, (it_hi - it_first + GROUPS - 1) / GROUPS);
+  asm volatile("" : "+s"(my_trips));
+  // per step GROUPS tiles down the same head; past its last tile, back nq
+  // tiles and on to the next head
+  const int64_t q_step = (int64_t)GROUPS * BMQ * qs, o_step = (int64_t)GROUPS * BMQ * os;
+  const int64_t q_wrap = a.sq.h - (int64_t)nq1 * BMQ * qs, o_wrap = a.so.h - (int64_t)nq1 * BMQ * os;
+  const int64_t s_wrap = (int64_t)S - (int64_t)nq1 * BMQ;
+  auto step = [&](Cursor& cu) {
+    cu.r += GROUPS;
+    cu.qoff += q_step;
+    cu.ooff += o_step;
+    cu.soff += GROUPS * BMQ;
+    while (cu.r >= nq1) {
+      cu.r -= nq1;
+      cu.qoff += q_wrap;
+      cu.ooff += o_wrap;
+      cu.soff += s_wrap;
+    }
+  };
   auto fetch = [&](int trip, const KVBuf& buf) {
-    const int it = it_lo + trip * GROUPS + grp;
-    if (it >= it_hi) return;
-    int hh, qt;
-    dkdv_trip(it, nq, G, qt0, false, hh, qt);
-    const int h = hkv * G + hh;
+    if (trip >= my_trips) return;
+    const int i0 = (qt0 + cur_f.r) * BMQ;
     if (swave < 2) {
       // raw value only: any arithmetic on it here would make the compiler wait
       // for this load before the tile's compute. Wave 0 of the group loads
       // LSE, wave 1 D; the choice is made on the scalar wave index (a
       // per-lane choice between the two pointers is compiled into a vector
       // load of the pointer from the argument block, waited for at once)
-      const int i = qt * BMQ + lane;
       const float* src = swave == 0 ? a.lse : a.delta;
       st_reg = 0.f;
-      if (i < L) st_reg = src[((int64_t)b * a.Hq + h) * S + i];
+      if (i0 + lane < L) st_reg = src[cur_f.soff + lane];
     }
-    const bf16* Qb = a.q + b * a.sq.b + h * a.sq.h;
-    const bf16* dOb = a.d_o + b * a.so.b + h * a.so.h;
-    tile_load_lds<BMQ, D, 4>(Qb, qs, qt * BMQ, L, buf.k, wave, lane);
-    tile_load_lds<BMQ, D, 4>(dOb, os, qt * BMQ, L, buf.v, wave, lane);
+    // the copies start at the tile's first row: rows at or past L - i0 are zeros
+    tile_load_lds<BMQ, D, 4>(a.q + cur_f.qoff, qs, 0, L - i0, buf.k, wave, lane);
+    tile_load_lds<BMQ, D, 4>(a.d_o + cur_f.ooff, os, 0, L - i0, buf.v, wave, lane);
+    step(cur_f);
   };
   auto land = [&](int trip, const KVBuf& buf) {
-    if (it_lo + trip * GROUPS + grp < it_hi && swave < 2)
-      sstat[grp][buf.idx][swave][lane] = swave == 0 ? st_reg * kLog2e : -st_reg;
+    if (trip < my_trips && swave < 2) sstat[grp][buf.idx][swave][lane] = swave == 0 ? st_reg * kLog2e : -st_reg;
   };
   auto compute = [&](int trip, const KVBuf& buf) {
-    const int it = it_lo + trip * GROUPS + grp;
-    if (it >= it_hi) return;
-    int hh, qt;
-    dkdv_trip(it, nq, G, qt0, false, hh, qt);
-    const int i0 = qt * BMQ;
+    if (trip >= my_trips) return;
+    const int i0 = (qt0 + cur_c.r) * BMQ;
+    step(cur_c);
     // skip when every query row of the tile is above this wave's key rows, or
     // the wave's keys are all padding
     if ((a.causal && i0 + BMQ - 1 < jw) || jw >= L) return;
@@ -1080,8 +1120,8 @@ void bwd_dkdv_roles_kernel(BwdArgs a) {
   const int qt0 = a.causal ? j0 / BMQ : 0;  // first query tile with rows at or below the block
   const int nq = (j0 < L) ? (L - 1) / BMQ - qt0 + 1 : 0;  // query tiles per head
   const int iters = nq * G;                               // (head, query tile) pairs
-  const int it_lo = (int)((int64_t)part * iters / nparts);
-  const int it_hi = (int)((int64_t)(part + 1) * iters / nparts);
+  const int it_lo = nparts == 1 ? 0 : (int)((int64_t)part * iters / nparts);
+  const int it_hi = nparts == 1 ? iters : (int)((int64_t)(part + 1) * iters / nparts);
   const int trips = it_hi - it_lo;
 
   float st_reg = 0.f;  // wave 0 carries LSE, wave 1 D
