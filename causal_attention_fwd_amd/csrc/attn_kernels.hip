@@ -506,9 +506,11 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
       dp[m2][t] = nd;
     }
   }
-  // S and dP: step i = (kk, m2) = (i / 2, i % 2) takes one Q and one dO
-  // fragment. The reads run PF steps ahead of the products that use them, so
-  // that a product never waits for a read issued just before it.
+  // S and dP: step i = (m2, kk) = (i / KK, i % KK) takes one Q and one dO
+  // fragment: the first half of the query rows (m2 = 0) is done after KK
+  // steps, so its softmax can start while the second half's products run.
+  // The reads run PF steps ahead of the products that use them, so that a
+  // product never waits for a read issued just before it.
   constexpr int NS = 2 * KK;
   bf16x8 aq[NS], ad[NS];
   // d=128 (one wave per SIMD, registers to spare): the tile's 64 LSE values
@@ -523,15 +525,15 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
   prio_mfma();
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    aq[i] = frag_row<D>(Qs, (i & 1) * 32, (i >> 1) * 16, lane);
-    ad[i] = frag_row<D>(dOs, (i & 1) * 32, (i >> 1) * 16, lane);
+    aq[i] = frag_row<D>(Qs, (i / KK) * 32, (i % KK) * 16, lane);
+    ad[i] = frag_row<D>(dOs, (i / KK) * 32, (i % KK) * 16, lane);
   }
 #pragma unroll
   for (int i = 0; i < NS; ++i)
 #pragma unroll
     for (int t = 0; t < NTJ; ++t) {
-      s[i & 1][t] = mfma32(aq[i], st.kf[t][i >> 1], s[i & 1][t]);
-      dp[i & 1][t] = mfma32(ad[i], st.vf[t][i >> 1], dp[i & 1][t]);
+      s[i / KK][t] = mfma32(aq[i], st.kf[t][i % KK], s[i / KK][t]);
+      dp[i / KK][t] = mfma32(ad[i], st.vf[t][i % KK], dp[i / KK][t]);
     }
   if constexpr (kDkdvReadAhead > 0) {
     constexpr int PF = kDkdvReadAhead;
@@ -577,21 +579,23 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<D, NTJ>& st, const bf16* Qs,
       pb[u][t] = pack8(s[u >> 1][t], (u & 1) * 8);
       sb[u][t] = pack8(dp[u >> 1][t], (u & 1) * 8);
     }
-  // dV and dK: step i = (ct, u) = (i / 4, i % 4), two transposed fragments
-  // (two reads each), the same read-ahead
+  // dV and dK: step i = (u, ct) = (i / DT, i % DT), two transposed fragments
+  // (two reads each), the same read-ahead; the first half's query rows (u =
+  // 0, 1) come first, so these products can start while the second half's
+  // softmax still runs
   constexpr int NT2 = 4 * DT;
   bf16x8 tdo[NT2], tq[NT2];
 #pragma unroll
   for (int i = 0; i < NT2; ++i) {
-    tdo[i] = frag_tr<D>(dOs, (i & 3) * 16, (i >> 2) * 32, lane);
-    tq[i] = frag_tr<D>(Qs, (i & 3) * 16, (i >> 2) * 32, lane);
+    tdo[i] = frag_tr<D>(dOs, (i / DT) * 16, (i % DT) * 32, lane);
+    tq[i] = frag_tr<D>(Qs, (i / DT) * 16, (i % DT) * 32, lane);
   }
 #pragma unroll
   for (int i = 0; i < NT2; ++i)
 #pragma unroll
     for (int t = 0; t < NTJ; ++t) {
-      st.dv[i >> 2][t] = mfma32(tdo[i], pb[i & 3][t], st.dv[i >> 2][t]);
-      st.dk[i >> 2][t] = mfma32(tq[i], sb[i & 3][t], st.dk[i >> 2][t]);
+      st.dv[i % DT][t] = mfma32(tdo[i], pb[i / DT][t], st.dv[i % DT][t]);
+      st.dk[i % DT][t] = mfma32(tq[i], sb[i / DT][t], st.dk[i % DT][t]);
     }
   if constexpr (kDkdvReadAhead > 0) {
     constexpr int PF = kDkdvReadAhead;
