@@ -4,7 +4,7 @@ Small shapes are compared element by element over every output; the five
 named workloads run at their full sizes, in the launch configuration the
 benchmark times (and with the backward's other launch order, preprocess then
 attn_bwd), and are compared on whole (sequence, kv head) units sampled
-from the batch (every kv head and sequence of llama1b), plus properties that
+from the batch (all of llama1b's and longseq's), plus properties that
 hold at any size over every unit (padding zeros, no NaN/Inf, D from the GPU's
 O, O within the range of its visible V rows, the gradient sum identities).
 """
@@ -107,13 +107,14 @@ def _units(w, inp):
     if w.name in ("tiny", "gqa124m"):
         return None  # every unit
     if w.name == "llama1b":
-        # every kv head and every sequence at least once
-        return sorted({(g % w.B, g) for g in range(w.Hkv)} | {(0, 0), (3, 7), (2, 5)})
+        # every (sequence, kv head) unit
+        return [(b, g) for b in range(w.B) for g in range(w.Hkv)]
     if w.name == "padded":
         L = inp.seqlens.tolist()
         return sorted({(int(np.argmin(L)), 0), (int(np.argmax(L)), 15)} | {(b, (5 * b + 3) % w.Hkv) for b in range(w.B)})
     if w.name == "longseq":
-        return [(0, 0), (0, 5)]
+        # every one of its eight kv groups
+        return [(0, g) for g in range(w.Hkv)]
     raise KeyError(w.name)
 
 
